@@ -1,0 +1,10 @@
+"""fp64 CPU oracle for attention and its JVP -- test infrastructure only.
+
+Only the test suite, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may import this package.  The GPU product path never
+imports it and shares no code with it.
+"""
+
+from .attention_jvp import attention, attention_jvp, attention_jvp_rows, ROW_CHUNK
+
+__all__ = ["attention", "attention_jvp", "attention_jvp_rows", "ROW_CHUNK"]
