@@ -1,0 +1,162 @@
+"""Python binding of libattn_jvp.so: fused attention forward + JVP on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/attn_jvp.h``; torch supplies
+device memory and the current stream.  The names mirror the C entry points:
+
+    attn_jvp_fwd(q, k, v, tq, tk, tv, scale=None, lse=True) -> (o, to, lse)
+        bf16 inputs [B, H, Nq|Nk, d] on the GPU; fp32 outputs
+    attn_jvp_fwd_f32(...)  the same with fp32 inputs
+    attn_jvp_workspace_bytes(B, H, Nk, d)
+    attn_jvp_strerror(status)
+
+The operation (rCM record LIT-783, Anthology of the SOTA, "Key takeaways",
+"JVP at production scale", paper §3.2 / App. C): O = softmax(s Q K^T) V, its
+tangent dO along (dQ, dK, dV), and lse = ln sum_j exp(s q_i . k_j).
+
+If the shared library has not been built, the first call raises ImportError:
+there is no fallback implementation.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["attn_jvp_fwd", "attn_jvp_fwd_f32", "attn_jvp_workspace_bytes",
+           "attn_jvp_strerror", "AttnJvpError", "LIB_PATH", "lib"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_jvp.so")
+
+_lib = None
+
+
+def lib():
+    """The loaded shared library (loaded on first use).
+
+    Raises ImportError if it has not been built: there is no fallback.
+    """
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -m attention_forward_mode_amd.build "
+            "or __graft_entry__.build()); there is no non-HIP fallback")
+    L = ctypes.CDLL(LIB_PATH)
+    _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_jvp_fwd.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _vp]
+    L.attn_jvp_fwd.restype = _i
+    L.attn_jvp_fwd_ws.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _vp, _sz, _vp]
+    L.attn_jvp_fwd_ws.restype = _i
+    L.attn_jvp_fwd_f32.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _vp]
+    L.attn_jvp_fwd_f32.restype = _i
+    L.attn_jvp_workspace_bytes.argtypes = [_i, _i, _i, _i]
+    L.attn_jvp_workspace_bytes.restype = _sz
+    L.attn_jvp_strerror.argtypes = [_i]
+    L.attn_jvp_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+OK, EINVAL, EUNSUPPORTED, EALIGN, ELAUNCH = 0, -1, -2, -3, -4
+
+
+class AttnJvpError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(f"attn_jvp: {attn_jvp_strerror(status)} (status {status})")
+
+
+def attn_jvp_strerror(status):
+    return lib().attn_jvp_strerror(int(status)).decode()
+
+
+def attn_jvp_workspace_bytes(B, H, Nk, d):
+    return int(lib().attn_jvp_workspace_bytes(B, H, Nk, d))
+
+
+def _check(q, k, v, tq, tk, tv, dtype):
+    for name, t in (("q", q), ("k", k), ("v", v), ("tq", tq), ("tk", tk), ("tv", tv)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch.Tensor")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d], got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tq.shape != q.shape:
+        raise ValueError("tq must have q's shape")
+    for name, t in (("k", k), ("v", v), ("tk", tk), ("tv", tv)):
+        if t.shape != (B, H, Nk, d):
+            raise ValueError(f"{name} must be {(B, H, Nk, d)}, got {tuple(t.shape)}")
+    dev = q.device
+    if any(t.device != dev for t in (k, v, tq, tk, tv)):
+        raise ValueError("all inputs must be on one device")
+    return B, H, Nq, Nk, d
+
+
+def _outputs(q, B, H, Nq, d, want_lse, out):
+    if out is not None:
+        o, to, lse = out
+        for name, t, shape in (("o", o, (B, H, Nq, d)), ("to", to, (B, H, Nq, d)),
+                               ("lse", lse, (B, H, Nq))):
+            if t is None and name == "lse":
+                continue
+            if (t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous()
+                    or t.device != q.device):
+                raise ValueError(f"out {name} must be a contiguous fp32 {shape} tensor on {q.device}")
+    else:
+        o = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+        to = torch.empty_like(o)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if want_lse else None
+    return o, to, lse
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def attn_jvp_fwd(q, k, v, tq, tk, tv, scale=None, lse=True, out=None, workspace=None):
+    """bf16 attention + JVP.  Returns (o, to, lse) fp32 (lse None if lse=False).
+
+    ``out`` may pass preallocated (o, to, lse) fp32 tensors; ``workspace`` a
+    uint8 device tensor of at least ``attn_jvp_workspace_bytes`` bytes (by
+    default one is taken from torch's caching allocator).  Launches on the
+    current stream; does not synchronise.
+    """
+    B, H, Nq, Nk, d = _check(q, k, v, tq, tk, tv, torch.bfloat16)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o, to, lse_t = _outputs(q, B, H, Nq, d, lse, out)
+    nbytes = attn_jvp_workspace_bytes(B, H, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_jvp_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                                 _ptr(o), _ptr(to), _ptr(lse_t), B, H, Nq, Nk, d, s,
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 stream)
+    if rc != OK:
+        raise AttnJvpError(rc)
+    return o, to, lse_t
+
+
+def attn_jvp_fwd_f32(q, k, v, tq, tk, tv, scale=None, lse=True, out=None):
+    """fp32 attention + JVP.  Returns (o, to, lse) fp32 (lse None if lse=False)."""
+    B, H, Nq, Nk, d = _check(q, k, v, tq, tk, tv, torch.float32)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o, to, lse_t = _outputs(q, B, H, Nq, d, lse, out)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_jvp_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                                  _ptr(o), _ptr(to), _ptr(lse_t), B, H, Nq, Nk, d, s, stream)
+    if rc != OK:
+        raise AttnJvpError(rc)
+    return o, to, lse_t

@@ -1,0 +1,135 @@
+// attn_jvp_api.cpp -- the C ABI declared in include/attn_jvp.h: argument
+// validation, workspace management and dispatch to the gfx950 launchers.
+// Every check runs before anything is launched, so a rejected call leaves the
+// outputs untouched.
+#include "attn_jvp.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxSliceBytes = int64_t(1) << 31;  // one (b, h) slice, 32-bit buffer offsets
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+// Shared checks of sizes, scale and pointers; esize is the input element size.
+int validate(const void* const* in, float* o, float* to, float* lse, int B, int H, int Nq, int Nk,
+             int d, float scale, int esize) {
+  for (int i = 0; i < 6; ++i)
+    if (in[i] == nullptr) return ATTN_JVP_EINVAL;
+  if (o == nullptr || to == nullptr) return ATTN_JVP_EINVAL;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_JVP_EINVAL;
+  if (!(scale >= 0.0f) || std::isinf(scale)) return ATTN_JVP_EINVAL;
+  if (d != 64 && d != 128) return ATTN_JVP_EUNSUPPORTED;
+  // Grid and offsets: B*H*ceil(Nq/128) workgroups and B*H*ceil(Nk/64) pack
+  // workgroups must fit an int; per-slice byte counts must fit 2^31 (padded).
+  const int64_t bh = int64_t(B) * H;
+  const int64_t qpad = (int64_t(Nq) + 127) / 128 * 128, kpad = (int64_t(Nk) + 63) / 64 * 64;
+  if (bh * (qpad / 128) > INT32_MAX || bh * (kpad / 64) > INT32_MAX) return ATTN_JVP_EINVAL;
+  if (qpad * d * esize >= kMaxSliceBytes || kpad * d * esize >= kMaxSliceBytes)
+    return ATTN_JVP_EUNSUPPORTED;
+  for (int i = 0; i < 6; ++i)
+    if (misaligned(in[i], 16)) return ATTN_JVP_EALIGN;
+  if (misaligned(o, 16) || misaligned(to, 16) || (lse != nullptr && misaligned(lse, 4)))
+    return ATTN_JVP_EALIGN;
+  return ATTN_JVP_OK;
+}
+
+// One stream-ordered pool per device; memory stays cached between calls.
+std::mutex g_pool_mu;
+hipMemPool_t g_pool[64] = {};
+
+hipError_t device_pool(hipMemPool_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if (g_pool[dev] == nullptr) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) return e;
+    g_pool[dev] = pool;
+  }
+  *out = g_pool[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_jvp_strerror(int status) {
+  switch (status) {
+    case ATTN_JVP_OK: return "ok";
+    case ATTN_JVP_EINVAL: return "invalid argument (null pointer, size < 1, bad scale or workspace, or size overflow)";
+    case ATTN_JVP_EUNSUPPORTED: return "unsupported (head dim must be 64 or 128; a (b, h) slice must stay under 2^31 bytes)";
+    case ATTN_JVP_EALIGN: return "misaligned pointer (tensors need 16-byte, workspace 256-byte alignment)";
+    case ATTN_JVP_ELAUNCH: return "HIP launch or allocation failed";
+    default: return "unknown status";
+  }
+}
+
+size_t attn_jvp_workspace_bytes(int B, int H, int Nk, int d) {
+  if (B < 1 || H < 1 || Nk < 1 || (d != 64 && d != 128)) return 0;
+  return ajvp::bf16_workspace_bytes(B, H, Nk, d);
+}
+
+int attn_jvp_fwd_ws(const void* q, const void* k, const void* v, const void* tq, const void* tk,
+                    const void* tv, float* o, float* to, float* lse, int B, int H, int Nq, int Nk,
+                    int d, float scale, void* workspace, size_t workspace_bytes,
+                    attn_jvp_stream_t stream) {
+  const void* in[6] = {q, k, v, tq, tk, tv};
+  int rc = validate(in, o, to, lse, B, H, Nq, Nk, d, scale, 2);
+  if (rc != ATTN_JVP_OK) return rc;
+  if (workspace == nullptr || workspace_bytes < ajvp::bf16_workspace_bytes(B, H, Nk, d))
+    return ATTN_JVP_EINVAL;
+  if (misaligned(workspace, 256)) return ATTN_JVP_EALIGN;
+  hipError_t e = ajvp::launch_bf16(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, d, scale,
+                                   workspace, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+}
+
+int attn_jvp_fwd(const void* q, const void* k, const void* v, const void* tq, const void* tk,
+                 const void* tv, float* o, float* to, float* lse, int B, int H, int Nq, int Nk,
+                 int d, float scale, attn_jvp_stream_t stream) {
+  const void* in[6] = {q, k, v, tq, tk, tv};
+  int rc = validate(in, o, to, lse, B, H, Nq, Nk, d, scale, 2);
+  if (rc != ATTN_JVP_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipMemPool_t pool = nullptr;
+  if (device_pool(&pool) != hipSuccess) return ATTN_JVP_ELAUNCH;
+  const size_t bytes = ajvp::bf16_workspace_bytes(B, H, Nk, d);
+  void* ws = nullptr;
+  if (hipMallocFromPoolAsync(&ws, bytes, pool, st) != hipSuccess) return ATTN_JVP_ELAUNCH;
+  hipError_t e = ajvp::launch_bf16(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, d, scale, ws, st);
+  hipError_t f = hipFreeAsync(ws, st);
+  return (e == hipSuccess && f == hipSuccess) ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+}
+
+int attn_jvp_fwd_f32(const float* q, const float* k, const float* v, const float* tq,
+                     const float* tk, const float* tv, float* o, float* to, float* lse, int B,
+                     int H, int Nq, int Nk, int d, float scale, attn_jvp_stream_t stream) {
+  const void* in[6] = {q, k, v, tq, tk, tv};
+  int rc = validate(in, o, to, lse, B, H, Nq, Nk, d, scale, 4);
+  if (rc != ATTN_JVP_OK) return rc;
+  hipError_t e = ajvp::launch_f32(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, d, scale,
+                                  reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+}
+
+}  // extern "C"

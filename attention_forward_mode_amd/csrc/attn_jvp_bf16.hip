@@ -1,0 +1,391 @@
+// attn_jvp_bf16.hip -- fused attention forward + JVP for gfx950, bf16 inputs.
+//
+// The operation (rCM record LIT-783 in the Anthology of the SOTA, "Key
+// takeaways", "JVP at production scale", paper §3.2 / App. C: FlashAttention-2
+// and its Jacobian-vector product in one tiled pass):
+//   O = softmax(s Q K^T) V,  dO = (P * (dS - mu)) V + P dV,
+//   dS = s (dQ K^T + Q dK^T),  mu = rowsum(P * dS),  lse = ln rowsum exp(s Q K^T).
+//
+// Two kernels per call:
+//  1. pack_v: V and dV -> fp16, transposed to [d][64 keys] tiles in matrix-core
+//     operand order (XOR-swizzled 16-byte chunks), zero-padded past Nk.  HBM
+//     bound, ~1% of the fused kernel's time at N = 32760.  fp16 instead of bf16
+//     for the second contraction keeps P and P*dS at 11 significant bits.
+//  2. attn_jvp_bf16: one workgroup = 4 waves x 32 query rows of one (b, h).
+//     Per 64-key tile: stage K, dK (bf16) and the packed V^T, dV^T (fp16) in
+//     LDS by direct global->LDS loads (double buffered, one tile ahead), then
+//     per wave and 32-key block
+//        S^T  = K Q^T            (bf16 MFMA 32x32x16, Q held in registers)
+//        dS^T = dK Q^T + K dQ^T  (same K fragments reused)
+//     online softmax in the accumulator layout (each lane owns one query row,
+//     so row state is per lane), and
+//        A^T += V^T P^T,  G^T += V^T (s P dS)^T + dV^T P^T  (fp16 MFMA)
+//     with P, s*P*dS rounded to fp16.  The epilogue forms O = A / l,
+//     mu = s u / l (u = rowsum P dS), dO = G / l - mu O and lse.
+//  The running max is only raised when a tile's max exceeds it by more than
+//  kTau (log2 units): results are exact either way, p stays <= 2^kTau, and the
+//  accumulator rescale is skipped on most tiles.
+#include "cdna4.hpp"
+#include "launch.hpp"
+
+namespace ajvp {
+namespace bf16_path {
+
+constexpr int kBC = 64;             // keys per tile
+constexpr int kThreads = 256;       // 4 waves
+constexpr int kRowsPerWave = 32;
+constexpr int kBR = 128;            // query rows per workgroup
+constexpr float kTau = 4.0f;        // lazy-rescale headroom, log2 units
+
+template <int D>
+struct Geo {
+  static constexpr int kTileBytes = kBC * D * 2;          // one tile of K (bf16) or V^T (fp16)
+  static constexpr int kStageBytes = 4 * kTileBytes;      // K | dK | V^T | dV^T
+  static constexpr int kPackTileBytes = 2 * kTileBytes;   // V^T | dV^T in the workspace
+  static constexpr int kKS = D / 16;                      // contraction steps over d
+  static constexpr int kCB = D / 32;                      // 32-column output blocks
+};
+
+// Key held at position `pos` (0..63) of a packed V^T row.  Positions
+// 16G + 8g + e hold the keys that the S^T accumulator of lane half g puts in
+// slots 8t + e of block G/2, t = G%2: keys 16G + 4g + e (e < 4) and
+// 16G + 8 + 4g + (e - 4) (e >= 4).
+__device__ inline int packed_key(int pos) {
+  const int G = pos >> 4, g = (pos >> 3) & 1, e = pos & 7;
+  return 16 * G + (e < 4 ? 4 * g + e : 8 + 4 * g + (e - 4));
+}
+
+template <int D>
+__device__ __attribute__((always_inline)) inline void pack_v_body(const uint16_t* __restrict__ v,
+                                                                  const uint16_t* __restrict__ dv,
+                                                                  char* __restrict__ ws, int Nk,
+                                                                  int ntiles) {
+  using G = Geo<D>;
+  __shared__ _Float16 sv[2][kBC][D + 2];
+  const int tile = blockIdx.x % ntiles;
+  const size_t bh = blockIdx.x / ntiles;
+  const uint16_t* src[2] = {v + bh * (size_t)Nk * D, dv + bh * (size_t)Nk * D};
+  const int key0 = tile * kBC;
+  constexpr int kIn = kBC * D / 8;  // 16-byte input chunks per tensor
+  for (int c = threadIdx.x; c < 2 * kIn; c += kThreads) {
+    const int t = c / kIn, rem = c % kIn, r = rem / (D / 8), col = (rem % (D / 8)) * 8;
+    const int key = key0 + r;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (key < Nk) x = *reinterpret_cast<const u32x4*>(src[t] + (size_t)key * D + col);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t bits = (x[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      sv[t][r][col + e] = (_Float16)__builtin_bit_cast(float, bits << 16);
+    }
+  }
+  __syncthreads();
+  char* out = ws + ((size_t)bh * ntiles + tile) * G::kPackTileBytes;
+  for (int c = threadIdx.x; c < 2 * D * 8; c += kThreads) {
+    const int t = c / (D * 8), rem = c % (D * 8), col = rem / 8, p = rem % 8;
+    f16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = sv[t][packed_key(8 * p + e)][col];
+    const int phys = p ^ (col & 7);
+    *reinterpret_cast<u32x4*>(out + t * G::kTileBytes + col * 128 + phys * 16) =
+        __builtin_bit_cast(u32x4, h);
+  }
+}
+
+template <int D>
+struct RowState {
+  f32x16 accA[Geo<D>::kCB];  // A^T = sum p v      (rows: output column, cols: query)
+  f32x16 accG[Geo<D>::kCB];  // G^T = sum p (s dS v + dv)
+  float m;                   // running max of s*log2e*S (log2 units), per query row
+  float l;                   // this lane's half of sum p
+  float u;                   // this lane's half of sum p * dS_raw
+};
+
+// One 32-key block of a staged tile for one wave: S^T, dS^T, the online
+// softmax update and the second contraction.  `blk` points at the block's first
+// key row of K inside the LDS stage; `key0` is the block's first key.
+template <int D, bool kMask>
+__device__ __attribute__((always_inline)) inline void jvp_block(RowState<D>& st, const char* stage,
+                                                                int kb, const u32x4* qf,
+                                                                const u32x4* dqf, int l32, int g,
+                                                                int key0, int Nk, float c_log2,
+                                                                float scale) {
+  using G = Geo<D>;
+  const char* sK = stage;
+  const char* sdK = stage + G::kTileBytes;
+  const char* sV = stage + 2 * G::kTileBytes;
+  const char* sdV = stage + 3 * G::kTileBytes;
+  const int sw = l32 & 7;
+
+  // ---- S^T = K Q^T and dS^T = dK Q^T + K dQ^T for 32 keys x 32 queries ----
+  f32x16 s = f32x16{}, ds = f32x16{};
+  const int rowoff = (32 * kb + l32) * D * 2;
+#pragma unroll
+  for (int ks = 0; ks < G::kKS; ++ks) {
+    const int off = rowoff + (((2 * ks + g) ^ sw) << 4);
+    const u32x4 a = lds_load16(sK + off);
+    const u32x4 da = lds_load16(sdK + off);
+    s = mma_bf16(a, qf[ks], s);
+    ds = mma_bf16(a, dqf[ks], ds);
+    ds = mma_bf16(da, qf[ks], ds);
+  }
+
+  // Keys past Nk (last tile only) are zero rows of K and dK; they are left out
+  // of the max and get p = 0.
+  auto masked = [&](int r) {
+    return kMask && key0 + 8 * (r >> 2) + 4 * g + (r & 3) >= Nk;
+  };
+  if constexpr (kMask) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (masked(r)) s[r] = -INFINITY;
+  }
+
+  // ---- online softmax; each lane owns query row l32, lane halves split keys ----
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  mx = fmaxf(mx, swap_halves(mx));
+  const float mt = mx * c_log2;
+  const float m_new = (mt > st.m + kTau) ? mt : st.m;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  st.m = m_new;
+
+  float p[16], pd[16], lsum = 0.f, usum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -m_new));
+    if (masked(r)) p[r] = 0.f;
+    lsum += p[r];
+    const float t = p[r] * ds[r];
+    usum += t;
+    pd[r] = t * scale;
+  }
+  u32x4 pb[2], pdb[2];
+  pb[0] = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+  pb[1] = pack_f16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+  pdb[0] = pack_f16x8(pd[0], pd[1], pd[2], pd[3], pd[4], pd[5], pd[6], pd[7]);
+  pdb[1] = pack_f16x8(pd[8], pd[9], pd[10], pd[11], pd[12], pd[13], pd[14], pd[15]);
+  st.l = st.l * alpha + lsum;
+  st.u = st.u * alpha + usum;
+  if (wave_any(alpha != 1.0f)) {
+#pragma unroll
+    for (int cb = 0; cb < G::kCB; ++cb) {
+      st.accA[cb] *= alpha;
+      st.accG[cb] *= alpha;
+    }
+  }
+
+  // ---- A^T += V^T P^T ; G^T += V^T (s P dS)^T + dV^T P^T ----
+#pragma unroll
+  for (int cb = 0; cb < G::kCB; ++cb) {
+    const int vrow = (32 * cb + l32) * 128;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int off = vrow + (((4 * kb + 2 * t + g) ^ sw) << 4);
+      const u32x4 a = lds_load16(sV + off);
+      const u32x4 da = lds_load16(sdV + off);
+      st.accA[cb] = mma_f16(a, pb[t], st.accA[cb]);
+      st.accG[cb] = mma_f16(a, pdb[t], st.accG[cb]);
+      st.accG[cb] = mma_f16(da, pb[t], st.accG[cb]);
+    }
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+__device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ tq, const uint16_t* __restrict__ tk,
+    const char* __restrict__ vpack, float* __restrict__ o, float* __restrict__ to,
+    float* __restrict__ lse, int Nq, int Nk, int nqt, int ntiles, int total_wg, float scale,
+    float c_log2) {
+  using G = Geo<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::kStageBytes];
+
+  // Work item.  Hardware deals workgroups round-robin over the 8 XCDs; remap so
+  // that each XCD walks a contiguous range of (b, h, row-tile) ids and its
+  // concurrently resident workgroups share one head's K/V in that XCD's L2.
+  int id = blockIdx.x;
+  if ((total_wg & 7) == 0) id = (id & 7) * (total_wg >> 3) + (id >> 3);
+  const int qt = to_sgpr(id % nqt);
+  const size_t bh = (size_t)to_sgpr(id / nqt);
+
+  const int tid = threadIdx.x, wave = to_sgpr(tid >> 6), lane = tid & 63;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int row = qt * kBR + wave * kRowsPerWave + l32;
+
+  // Q and dQ fragments: the B operand of S^T = K Q^T (lane: row l32, d-slice g).
+  const uint32_t qbytes = (uint32_t)Nq * D * 2;
+  const auto rq = make_rsrc(q + bh * (size_t)Nq * D, qbytes);
+  const auto rtq = make_rsrc(tq + bh * (size_t)Nq * D, qbytes);
+  u32x4 qf[G::kKS], dqf[G::kKS];
+#pragma unroll
+  for (int ks = 0; ks < G::kKS; ++ks) {
+    const uint32_t off = (uint32_t)row * D * 2 + (16 * ks + 8 * g) * 2;
+    qf[ks] = buf_load16(rq, off);
+    dqf[ks] = buf_load16(rtq, off);
+  }
+
+  // Staging by direct global->LDS loads (no registers): each wave moves
+  // kDmaPerWave KiB per tile, 16 bytes per lane, into a contiguous KiB of LDS.
+  // K and dK come from the caller's tensors (zero past Nk through the buffer
+  // range check) with each lane fetching the chunk that belongs at its LDS slot
+  // under the XOR swizzle; V^T and dV^T are copied linearly from the packed tiles.
+  constexpr int kKiBPerTensor = G::kTileBytes / 1024;
+  const uint32_t kbytes = (uint32_t)Nk * D * 2;
+  const auto rk = make_rsrc(k + bh * (size_t)Nk * D, kbytes);
+  const auto rtk = make_rsrc(tk + bh * (size_t)Nk * D, kbytes);
+  const auto rv = make_rsrc(vpack + bh * (size_t)ntiles * G::kPackTileBytes,
+                            (uint32_t)ntiles * G::kPackTileBytes);
+  constexpr int kPerTensor = kKiBPerTensor / 4;        // KiB of each tensor per wave
+  auto issue_stage = [&](int kt, int buf) {
+    char* sbase = smem + buf * G::kStageBytes;
+#pragma unroll
+    for (int tensor = 0; tensor < 4; ++tensor)
+#pragma unroll
+      for (int j = 0; j < kPerTensor; ++j) {
+        const int kib = wave * kPerTensor + j;         // KiB index within this tensor's tile
+        const int P = kib * 64 + lane;                 // 16-byte slot within the tile
+        lds_void* dst = (lds_void*)(sbase + tensor * G::kTileBytes + kib * 1024);
+        if (tensor < 2) {
+          const int krow = P / (D / 8), phys = P % (D / 8);
+          const uint32_t off =
+              (uint32_t)kt * kBC * D * 2 + krow * D * 2 + ((phys ^ (krow & 7)) << 4);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(tensor == 0 ? rk : rtk, dst, 16, off, 0, 0, 0);
+        } else {
+          const uint32_t off =
+              (uint32_t)kt * G::kPackTileBytes + (tensor - 2) * G::kTileBytes + P * 16;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, off, 0, 0, 0);
+        }
+      }
+  };
+
+  RowState<D> st;
+#pragma unroll
+  for (int cb = 0; cb < G::kCB; ++cb) {
+    st.accA[cb] = f32x16{};
+    st.accG[cb] = f32x16{};
+  }
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.u = 0.f;
+
+  issue_stage(0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles - 1; ++kt) {
+    // The other buffer was last read in iteration kt-1, which every wave has
+    // finished (barrier below), so the next tile can stream into it now.
+    issue_stage(kt + 1, (kt + 1) & 1);
+    const char* stage = smem + (kt & 1) * G::kStageBytes;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      jvp_block<D, false>(st, stage, kb, qf, dqf, l32, g, kt * kBC + 32 * kb, Nk, c_log2, scale);
+    // Own direct loads complete (vmcnt), then everyone's (barrier).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+  {
+    // Last tile, peeled so the loop has one code path: keys past Nk are masked.
+    const int kt = ntiles - 1;
+    const char* stage = smem + (kt & 1) * G::kStageBytes;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      jvp_block<D, true>(st, stage, kb, qf, dqf, l32, g, kt * kBC + 32 * kb, Nk, c_log2, scale);
+  }
+
+  // ---- epilogue: O = A / l, mu = s u / l, dO = G / l - mu O, lse ----
+  const float l = st.l + swap_halves(st.l);
+  const float u = st.u + swap_halves(st.u);
+  const float inv_l = 1.0f / l;
+  const float mu = u * scale * inv_l;
+  if (row < Nq) {
+    float* orow = o + (bh * (size_t)Nq + row) * D;
+    float* trow = to + (bh * (size_t)Nq + row) * D;
+#pragma unroll
+    for (int cb = 0; cb < G::kCB; ++cb)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int c0 = 32 * cb + 8 * qq + 4 * g;
+        f32x4 ov, tv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = st.accA[cb][4 * qq + e] * inv_l;
+          ov[e] = a;
+          tv[e] = st.accG[cb][4 * qq + e] * inv_l - mu * a;
+        }
+        *reinterpret_cast<f32x4*>(orow + c0) = ov;
+        *reinterpret_cast<f32x4*>(trow + c0) = tv;
+      }
+    if (lse != nullptr && g == 0) lse[bh * (size_t)Nq + row] = (st.m + __log2f(l)) * kLn2;
+  }
+}
+
+#define AJVP_BF16_KERNEL(D)                                                                  \
+  __global__ __launch_bounds__(kThreads, 1) void attn_jvp_bf16_d##D(                          \
+      const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,                         \
+      const uint16_t* __restrict__ tq, const uint16_t* __restrict__ tk,                       \
+      const char* __restrict__ vpack, float* __restrict__ o, float* __restrict__ to,          \
+      float* __restrict__ lse, int Nq, int Nk, int nqt, int ntiles, int total_wg, float scale,  \
+      float c_log2) {                                                                          \
+    attn_jvp_bf16_body<D>(q, k, tq, tk, vpack, o, to, lse, Nq, Nk, nqt, ntiles, total_wg, scale, \
+                          c_log2);                                                             \
+  }                                                                                            \
+  __global__ __launch_bounds__(kThreads) void pack_v_d##D(const uint16_t* __restrict__ v,     \
+                                                          const uint16_t* __restrict__ dv,    \
+                                                          char* __restrict__ ws, int Nk,      \
+                                                          int ntiles) {                       \
+    pack_v_body<D>(v, dv, ws, Nk, ntiles);                                                     \
+  }
+AJVP_BF16_KERNEL(64)
+AJVP_BF16_KERNEL(128)
+#undef AJVP_BF16_KERNEL
+
+template <int D> struct Kernels;
+template <> struct Kernels<64> {
+  static constexpr auto main = attn_jvp_bf16_d64;
+  static constexpr auto pack = pack_v_d64;
+};
+template <> struct Kernels<128> {
+  static constexpr auto main = attn_jvp_bf16_d128;
+  static constexpr auto pack = pack_v_d128;
+};
+
+template <int D>
+hipError_t launch_bf16_d(const void* q, const void* k, const void* v, const void* tq,
+                         const void* tk, const void* tv, float* o, float* to, float* lse, int B,
+                         int H, int Nq, int Nk, float scale, void* ws, hipStream_t stream) {
+  const int ntiles = (Nk + kBC - 1) / kBC;
+  const int nqt = (Nq + kBR - 1) / kBR;
+  const int bh = B * H;
+  hipLaunchKernelGGL(Kernels<D>::pack, dim3(ntiles * bh), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(tv),
+                     static_cast<char*>(ws), Nk, ntiles);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int total = bh * nqt;
+  hipLaunchKernelGGL(Kernels<D>::main, dim3(total), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(tq), static_cast<const uint16_t*>(tk),
+                     static_cast<const char*>(ws), o, to, lse, Nq, Nk, nqt, ntiles, total, scale,
+                     scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace bf16_path
+using namespace bf16_path;
+
+size_t bf16_workspace_bytes(int B, int H, int Nk, int d) {
+  const size_t ntiles = ((size_t)Nk + kBC - 1) / kBC;
+  return (size_t)B * H * ntiles * 2 * kBC * (size_t)d * 2;
+}
+
+hipError_t launch_bf16(const void* q, const void* k, const void* v, const void* tq,
+                       const void* tk, const void* tv, float* o, float* to, float* lse, int B,
+                       int H, int Nq, int Nk, int d, float scale, void* ws, hipStream_t stream) {
+  if (d == 128)
+    return launch_bf16_d<128>(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, scale, ws, stream);
+  return launch_bf16_d<64>(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, scale, ws, stream);
+}
+
+}  // namespace ajvp

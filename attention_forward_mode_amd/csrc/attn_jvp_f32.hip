@@ -1,0 +1,269 @@
+// attn_jvp_f32.hip -- fused attention forward + JVP for gfx950, fp32 throughout.
+//
+// Same operation as the bf16 path (rCM record LIT-783 in the Anthology of the
+// SOTA, "Key takeaways", "JVP at production scale", paper §3.2 / App. C), kept
+// in fp32 end to end: it is the precision reference the pages motivate (the
+// record's second takeaway: BF16 JVP error is much larger than BF16 output
+// error, Fig. 11).  Structure: one workgroup = 4 waves x 32 query rows; 32-key
+// tiles of K, dK, V, dV staged in LDS by direct global->LDS loads (double
+// buffered, one tile ahead); fp32 MFMA 32x32x2 for S^T = K Q^T, dS^T = dK Q^T + K dQ^T,
+// A^T += V^T P^T and G^T += V^T (s P dS)^T + dV^T P^T; online softmax per lane.
+#include "cdna4.hpp"
+#include "launch.hpp"
+
+namespace ajvp {
+namespace f32_path {
+
+constexpr int kBC = 32;        // keys per tile
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kRowsPerWave = 32;
+constexpr int kBR = 128;
+constexpr float kTau = 4.0f;   // lazy-rescale headroom, log2 units
+
+template <int D>
+struct GeoF {
+  static constexpr int kTileBytes = kBC * D * 4;       // one fp32 tile
+  static constexpr int kStageBytes = 4 * kTileBytes;   // K | dK | V | dV
+  static constexpr int kQ4 = D / 8;                    // float4 operand chunks per lane
+  static constexpr int kCB = D / 32;
+  static constexpr int kRowChunks = D / 4;             // 16-byte chunks per row
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline f32x16 mma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+struct RowStateF {
+  f32x16 accA[GeoF<D>::kCB];
+  f32x16 accG[GeoF<D>::kCB];
+  float m, l, u;
+};
+
+// Tiles are stored row-major [32 keys][D] with 16-byte chunk c of row r at
+// chunk position c ^ (r & 7): conflict-free for both read patterns below.
+template <int D>
+__device__ inline int swz(int r, int chunk) {
+  return r * D * 4 + ((chunk ^ (r & 7)) << 4);
+}
+
+template <int D, bool kMask>
+__device__ __attribute__((always_inline)) inline void jvp_tile_f32(
+    RowStateF<D>& st, const char* stage, const f32x4* qf, const f32x4* dqf, int l32, int g,
+    int key0, int Nk, float c_log2, float scale) {
+  using G = GeoF<D>;
+  const char* sK = stage;
+  const char* sdK = stage + G::kTileBytes;
+  const char* sV = stage + 2 * G::kTileBytes;
+  const char* sdV = stage + 3 * G::kTileBytes;
+
+  // S^T, dS^T: contraction slot (j, e, half g) <-> d = 8j + 4g + e.
+  f32x16 s = f32x16{}, ds = f32x16{};
+#pragma unroll
+  for (int j = 0; j < G::kQ4; ++j) {
+    const int off = swz<D>(l32, 2 * j + g);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(sK + off);
+    const f32x4 da = *reinterpret_cast<const f32x4*>(sdK + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s = mma_f32(a[e], qf[j][e], s);
+      ds = mma_f32(a[e], dqf[j][e], ds);
+      ds = mma_f32(da[e], qf[j][e], ds);
+    }
+  }
+  auto masked = [&](int r) { return kMask && key0 + 8 * (r >> 2) + 4 * g + (r & 3) >= Nk; };
+  if constexpr (kMask) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (masked(r)) s[r] = -INFINITY;
+  }
+
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  mx = fmaxf(mx, swap_halves(mx));
+  const float mt = mx * c_log2;
+  const float m_new = (mt > st.m + kTau) ? mt : st.m;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  st.m = m_new;
+
+  float p[16], pd[16], lsum = 0.f, usum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -m_new));
+    if (masked(r)) p[r] = 0.f;
+    lsum += p[r];
+    const float t = p[r] * ds[r];
+    usum += t;
+    pd[r] = t * scale;
+  }
+  st.l = st.l * alpha + lsum;
+  st.u = st.u * alpha + usum;
+  if (wave_any(alpha != 1.0f)) {
+#pragma unroll
+    for (int cb = 0; cb < G::kCB; ++cb) {
+      st.accA[cb] *= alpha;
+      st.accG[cb] *= alpha;
+    }
+  }
+
+  // Second contraction over keys: step r uses key 8(r/4) + 4g + r%4, which is
+  // the key this lane's accumulator slot r holds.
+#pragma unroll
+  for (int cb = 0; cb < G::kCB; ++cb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+      const int c = 32 * cb + l32;
+      const int off = swz<D>(key, c >> 2) + ((c & 3) << 2);
+      const float a = *reinterpret_cast<const float*>(sV + off);
+      const float da = *reinterpret_cast<const float*>(sdV + off);
+      st.accA[cb] = mma_f32(a, p[r], st.accA[cb]);
+      st.accG[cb] = mma_f32(a, pd[r], st.accG[cb]);
+      st.accG[cb] = mma_f32(da, p[r], st.accG[cb]);
+    }
+  }
+}
+
+template <int D>
+__device__ __attribute__((always_inline)) inline void attn_jvp_f32_body(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ tq, const float* __restrict__ tk, const float* __restrict__ tv,
+    float* __restrict__ o, float* __restrict__ to, float* __restrict__ lse, int Nq, int Nk,
+    int nqt, int ntiles, int total_wg, float scale, float c_log2) {
+  using G = GeoF<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::kStageBytes];
+
+  int id = blockIdx.x;
+  if ((total_wg & 7) == 0) id = (id & 7) * (total_wg >> 3) + (id >> 3);
+  const int qt = to_sgpr(id % nqt);
+  const size_t bh = (size_t)to_sgpr(id / nqt);
+  const int tid = threadIdx.x, wave = to_sgpr(tid >> 6), lane = tid & 63;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int row = qt * kBR + wave * kRowsPerWave + l32;
+
+  const uint32_t qbytes = (uint32_t)Nq * D * 4;
+  const auto rq = make_rsrc(q + bh * (size_t)Nq * D, qbytes);
+  const auto rtq = make_rsrc(tq + bh * (size_t)Nq * D, qbytes);
+  f32x4 qf[G::kQ4], dqf[G::kQ4];
+#pragma unroll
+  for (int j = 0; j < G::kQ4; ++j) {
+    const uint32_t off = (uint32_t)row * D * 4 + (8 * j + 4 * g) * 4;
+    qf[j] = __builtin_bit_cast(f32x4, buf_load16(rq, off));
+    dqf[j] = __builtin_bit_cast(f32x4, buf_load16(rtq, off));
+  }
+
+  // Staging by direct global->LDS loads: each wave moves a quarter of each
+  // tensor's tile, 16 bytes per lane into a contiguous KiB of LDS; each lane
+  // fetches the chunk that belongs at its LDS slot under the XOR swizzle.  Rows
+  // past Nk read as zero through the buffer range check.
+  const uint32_t kbytes = (uint32_t)Nk * D * 4;
+  const __amdgpu_buffer_rsrc_t rsrc[4] = {make_rsrc(k + bh * (size_t)Nk * D, kbytes),
+                                          make_rsrc(tk + bh * (size_t)Nk * D, kbytes),
+                                          make_rsrc(v + bh * (size_t)Nk * D, kbytes),
+                                          make_rsrc(tv + bh * (size_t)Nk * D, kbytes)};
+  constexpr int kPerTensor = G::kTileBytes / 1024 / 4;  // KiB of each tensor per wave
+  auto issue_stage = [&](int kt, int buf) {
+    char* sbase = smem + buf * G::kStageBytes;
+#pragma unroll
+    for (int tensor = 0; tensor < 4; ++tensor)
+#pragma unroll
+      for (int j = 0; j < kPerTensor; ++j) {
+        const int kib = wave * kPerTensor + j;
+        const int P = kib * 64 + lane;
+        const int r = P / G::kRowChunks, phys = P % G::kRowChunks;
+        const uint32_t off = (uint32_t)kt * kBC * D * 4 + r * D * 4 + ((phys ^ (r & 7)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc[tensor], (lds_void*)(sbase + tensor * G::kTileBytes + kib * 1024), 16, off, 0, 0, 0);
+      }
+  };
+
+  RowStateF<D> st;
+#pragma unroll
+  for (int cb = 0; cb < G::kCB; ++cb) {
+    st.accA[cb] = f32x16{};
+    st.accG[cb] = f32x16{};
+  }
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.u = 0.f;
+
+  issue_stage(0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles - 1; ++kt) {
+    issue_stage(kt + 1, (kt + 1) & 1);
+    jvp_tile_f32<D, false>(st, smem + (kt & 1) * G::kStageBytes, qf, dqf, l32, g, kt * kBC, Nk,
+                           c_log2, scale);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+  {
+    const int kt = ntiles - 1;  // peeled: keys past Nk are masked
+    jvp_tile_f32<D, true>(st, smem + (kt & 1) * G::kStageBytes, qf, dqf, l32, g, kt * kBC, Nk,
+                          c_log2, scale);
+  }
+
+  const float l = st.l + swap_halves(st.l);
+  const float u = st.u + swap_halves(st.u);
+  const float inv_l = 1.0f / l;
+  const float mu = u * scale * inv_l;
+  if (row < Nq) {
+    float* orow = o + (bh * (size_t)Nq + row) * D;
+    float* trow = to + (bh * (size_t)Nq + row) * D;
+#pragma unroll
+    for (int cb = 0; cb < G::kCB; ++cb)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int c0 = 32 * cb + 8 * qq + 4 * g;
+        f32x4 ov, tv4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = st.accA[cb][4 * qq + e] * inv_l;
+          ov[e] = a;
+          tv4[e] = st.accG[cb][4 * qq + e] * inv_l - mu * a;
+        }
+        *reinterpret_cast<f32x4*>(orow + c0) = ov;
+        *reinterpret_cast<f32x4*>(trow + c0) = tv4;
+      }
+    if (lse != nullptr && g == 0) lse[bh * (size_t)Nq + row] = (st.m + __log2f(l)) * kLn2;
+  }
+}
+
+#define AJVP_F32_KERNEL(D)                                                                      \
+  __global__ __launch_bounds__(kThreads, 1) void attn_jvp_f32_d##D(                              \
+      const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,     \
+      const float* __restrict__ tq, const float* __restrict__ tk, const float* __restrict__ tv,  \
+      float* __restrict__ o, float* __restrict__ to, float* __restrict__ lse, int Nq, int Nk,    \
+      int nqt, int ntiles, int total_wg, float scale, float c_log2) {                            \
+    attn_jvp_f32_body<D>(q, k, v, tq, tk, tv, o, to, lse, Nq, Nk, nqt, ntiles, total_wg, scale,  \
+                         c_log2);                                                                 \
+  }
+AJVP_F32_KERNEL(64)
+AJVP_F32_KERNEL(128)
+#undef AJVP_F32_KERNEL
+
+template <int D>
+hipError_t launch_f32_d(const float* q, const float* k, const float* v, const float* tq,
+                        const float* tk, const float* tv, float* o, float* to, float* lse, int B,
+                        int H, int Nq, int Nk, float scale, hipStream_t stream) {
+  const int ntiles = (Nk + kBC - 1) / kBC;
+  const int nqt = (Nq + kBR - 1) / kBR;
+  const int total = B * H * nqt;
+  hipLaunchKernelGGL((D == 128 ? attn_jvp_f32_d128 : attn_jvp_f32_d64), dim3(total), dim3(kThreads), 0, stream, q, k, v, tq,
+                     tk, tv, o, to, lse, Nq, Nk, nqt, ntiles, total, scale, scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace f32_path
+using namespace f32_path;
+
+hipError_t launch_f32(const float* q, const float* k, const float* v, const float* tq,
+                      const float* tk, const float* tv, float* o, float* to, float* lse, int B,
+                      int H, int Nq, int Nk, int d, float scale, hipStream_t stream) {
+  if (d == 128) return launch_f32_d<128>(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, scale, stream);
+  return launch_f32_d<64>(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, scale, stream);
+}
+
+}  // namespace ajvp

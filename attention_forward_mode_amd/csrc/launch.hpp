@@ -1,0 +1,23 @@
+// launch.hpp -- host-side launchers of the gfx950 attention-JVP kernels.
+// Called only by the C ABI (attn_jvp_api.cpp) after it has validated every
+// argument; each returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+namespace ajvp {
+
+// Workspace bytes of the bf16 path: fp16 V^T and dV^T tiles, 64 keys each.
+size_t bf16_workspace_bytes(int B, int H, int Nk, int d);
+
+hipError_t launch_bf16(const void* q, const void* k, const void* v, const void* tq,
+                       const void* tk, const void* tv, float* o, float* to, float* lse,
+                       int B, int H, int Nq, int Nk, int d, float scale, void* workspace,
+                       hipStream_t stream);
+
+hipError_t launch_f32(const float* q, const float* k, const float* v, const float* tq,
+                      const float* tk, const float* tv, float* o, float* to, float* lse,
+                      int B, int H, int Nq, int Nk, int d, float scale, hipStream_t stream);
+
+}  // namespace ajvp

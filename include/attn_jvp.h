@@ -1,0 +1,140 @@
+/*
+ * attn_jvp.h -- fused softmax-attention forward pass and its Jacobian-vector
+ * product (JVP) on AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation.  The rCM record in the Anthology of the SOTA (LIT-783, "Key
+ * takeaways", bullet "JVP at production scale", paper §3.2 and App. C)
+ * describes one tiled pass that computes FlashAttention-2 together with its
+ * Jacobian-vector product, for self- and cross-attention, with the tangents
+ * of Q, K and V laid out exactly like Q, K and V.  Per (batch b, head h), for
+ * queries i < Nq, keys j < Nk, head dim d and the scalar `scale` s:
+ *
+ *   S   = s Q K^T,  P = row-softmax(S),  O = P V,
+ *   lse = ln sum_j exp(S_ij)                                (natural log)
+ *   dS  = s (dQ K^T + Q dK^T),  mu_i = sum_j P_ij dS_ij,
+ *   dO  = (P * (dS - mu)) V + P dV                          (the tangent of O)
+ *
+ * `scale` is a constant: it has no tangent.  There is no mask, no causal
+ * mode, no dropout and no grouped heads (K and V have H heads, like Q).
+ *
+ * Layout.  Every tensor is dense, row-major and contiguous:
+ *   q, tq, o, to : [B, H, Nq, d]      k, v, tk, tv : [B, H, Nk, d]
+ *   lse          : [B, H, Nq]
+ * A tangent has exactly its primal's shape, dtype and layout.  Offsets are
+ * computed in 64-bit.
+ *
+ * Precision.  attn_jvp_fwd takes bf16 inputs (uint16 storage holding IEEE
+ * bfloat16 bit patterns); all products are formed on bf16/fp16 matrix cores
+ * with fp32 accumulation, and O, dO and lse are written in fp32.  The second
+ * contraction (P and P*dS against V and dV) runs on fp16 operands: V and dV
+ * are converted exactly (bf16 -> fp16 is exact for 2^-14 <= |x| < 65504; smaller
+ * magnitudes round to fp16 subnormals), P and P*dS are rounded to nearest.
+ * An input outside fp16 range, or |scale * dS| beyond about 4000, overflows to
+ * a non-finite output rather than a wrong finite one.  attn_jvp_fwd_f32 takes
+ * fp32 inputs and computes in fp32 throughout.  NaN/Inf inputs propagate.
+ *
+ * Ownership and streams.  All tensor pointers are DEVICE pointers owned by the
+ * caller, on the current HIP device.  Outputs must not alias inputs or each
+ * other.  Every call is asynchronous on `stream` (NULL = the null stream) and
+ * never synchronises the host.  The calls hold no state across calls apart
+ * from a per-device memory pool used by attn_jvp_fwd for its workspace
+ * (stream-ordered hipMallocFromPoolAsync / hipFreeAsync); attn_jvp_fwd_ws uses
+ * a caller-provided workspace instead.
+ *
+ * Errors.  Argument errors are detected before anything is launched and leave
+ * every output untouched:
+ *   ATTN_JVP_EINVAL       a required pointer is NULL; B, H, Nq or Nk < 1;
+ *                         `scale` is negative, NaN or infinite; a size product
+ *                         overflows; the workspace is NULL or too small
+ *   ATTN_JVP_EUNSUPPORTED d is not 64 or 128, or one (b, h) slice of K/V
+ *                         exceeds 2^31 bytes
+ *   ATTN_JVP_EALIGN       a tensor pointer is not 16-byte aligned (workspace:
+ *                         256-byte aligned)
+ *   ATTN_JVP_ELAUNCH      the HIP runtime rejected a launch or an allocation
+ *                         (hipGetLastError); outputs are then unspecified
+ * Device-side faults surface at the caller's next synchronisation.
+ */
+#ifndef ATTN_JVP_H
+#define ATTN_JVP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define ATTN_JVP_API __attribute__((visibility("default")))
+#else
+#define ATTN_JVP_API
+#endif
+
+#define ATTN_JVP_OK 0
+#define ATTN_JVP_EINVAL (-1)
+#define ATTN_JVP_EUNSUPPORTED (-2)
+#define ATTN_JVP_EALIGN (-3)
+#define ATTN_JVP_ELAUNCH (-4)
+
+/* Opaque HIP stream handle (hipStream_t). */
+typedef struct ihipStream_t *attn_jvp_stream_t;
+
+/*
+ * Attention and its JVP, bf16 inputs, fp32 outputs (the operation above).
+ *   q, k, v     primal inputs (bf16 bit patterns), layouts above
+ *   tq, tk, tv  their tangents dQ, dK, dV (bf16), same layouts
+ *   o, to       outputs O and dO, fp32 [B, H, Nq, d]
+ *   lse         output row log-sum-exp, fp32 [B, H, Nq]; may be NULL (not written)
+ *   B, H        batch and head counts; Nq, Nk query and key lengths (any >= 1;
+ *               Nq != Nk is cross-attention); d = 64 or 128
+ *   scale       softmax scale s >= 0 (typically 1/sqrt(d))
+ *   stream      HIP stream for every launch
+ * Allocates a workspace of attn_jvp_workspace_bytes(B, H, Nk, d) bytes from a
+ * library-owned stream-ordered pool and frees it stream-ordered.
+ * Returns ATTN_JVP_OK or an error code above.
+ */
+ATTN_JVP_API int attn_jvp_fwd(const void *q, const void *k, const void *v,
+                 const void *tq, const void *tk, const void *tv,
+                 float *o, float *to, float *lse,
+                 int B, int H, int Nq, int Nk, int d, float scale,
+                 attn_jvp_stream_t stream);
+
+/*
+ * Bytes of workspace the bf16 path needs for these sizes (fp16 transposed
+ * copies of V and dV in matrix-core tile order, padded to 64 keys); 0 if a size
+ * is invalid.  Same operation as attn_jvp_fwd.
+ */
+ATTN_JVP_API size_t attn_jvp_workspace_bytes(int B, int H, int Nk, int d);
+
+/*
+ * attn_jvp_fwd with a caller-provided device workspace (256-byte aligned,
+ * at least attn_jvp_workspace_bytes(B, H, Nk, d) bytes, not shared with a call
+ * that may run concurrently).  Allocates nothing.  Same arguments, semantics and
+ * errors as attn_jvp_fwd otherwise.
+ */
+ATTN_JVP_API int attn_jvp_fwd_ws(const void *q, const void *k, const void *v,
+                    const void *tq, const void *tk, const void *tv,
+                    float *o, float *to, float *lse,
+                    int B, int H, int Nq, int Nk, int d, float scale,
+                    void *workspace, size_t workspace_bytes,
+                    attn_jvp_stream_t stream);
+
+/*
+ * The same operation with fp32 inputs and fp32 arithmetic throughout (the
+ * precision reference path).  Same layouts, arguments and errors; needs no
+ * workspace and allocates nothing.
+ */
+ATTN_JVP_API int attn_jvp_fwd_f32(const float *q, const float *k, const float *v,
+                     const float *tq, const float *tk, const float *tv,
+                     float *o, float *to, float *lse,
+                     int B, int H, int Nq, int Nk, int d, float scale,
+                     attn_jvp_stream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+ATTN_JVP_API const char *attn_jvp_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_JVP_H */

@@ -1,0 +1,132 @@
+"""The C ABI boundary, checked without a GPU: the library loads, exports every
+entry point declared in include/*.h, and rejects bad arguments before it
+launches anything (so no device is touched)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import attention_forward_mode_amd as ajvp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, EINVAL, EUNSUPPORTED, EALIGN, ELAUNCH = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        # declarations start a line: "ATTN_JVP_API <type> name(" (skip the macro's definition)
+        names += re.findall(r"^ATTN_JVP_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = ajvp.lib()
+    names = declared_functions()
+    assert set(names) >= {"attn_jvp_fwd", "attn_jvp_fwd_ws", "attn_jvp_fwd_f32",
+                          "attn_jvp_workspace_bytes", "attn_jvp_strerror"}
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/ but not exported"
+
+
+def test_error_codes_match_header():
+    text = open(os.path.join(ROOT, "include", "attn_jvp.h")).read()
+    codes = dict(re.findall(r"#define (ATTN_JVP_\w+) \(?(-?\d+)\)?", text))
+    assert {k: int(v) for k, v in codes.items()} == {
+        "ATTN_JVP_OK": OK, "ATTN_JVP_EINVAL": EINVAL, "ATTN_JVP_EUNSUPPORTED": EUNSUPPORTED,
+        "ATTN_JVP_EALIGN": EALIGN, "ATTN_JVP_ELAUNCH": ELAUNCH}
+
+
+def test_strerror():
+    for code in (OK, EINVAL, EUNSUPPORTED, EALIGN, ELAUNCH, 12345):
+        msg = ajvp.attn_jvp_strerror(code)
+        assert isinstance(msg, str) and msg
+    assert ajvp.attn_jvp_strerror(OK) == "ok"
+    assert ajvp.attn_jvp_strerror(12345) == "unknown status"
+
+
+def test_workspace_bytes():
+    # fp16 V^T and dV^T, padded to 64 keys: 2 * 64 * d * 2 bytes per key tile
+    assert ajvp.attn_jvp_workspace_bytes(1, 1, 1, 128) == 2 * 64 * 128 * 2
+    assert ajvp.attn_jvp_workspace_bytes(1, 12, 32760, 128) == 12 * 512 * 2 * 64 * 128 * 2
+    assert ajvp.attn_jvp_workspace_bytes(2, 3, 65, 64) == 6 * 2 * 2 * 64 * 64 * 2
+    assert ajvp.attn_jvp_workspace_bytes(0, 1, 1, 128) == 0
+    assert ajvp.attn_jvp_workspace_bytes(1, 1, 1, 96) == 0
+
+
+# Fake, never-dereferenced device addresses: every call below must be rejected
+# by validation before any launch.
+A = 0x7F0000000000  # 256-byte aligned
+
+
+def _call(fn, ptrs=None, B=1, H=1, Nq=4, Nk=4, d=128, scale=0.1, ws=None, ws_bytes=None):
+    L = ajvp.lib()
+    p = [A + i * 0x100000 for i in range(9)] if ptrs is None else ptrs
+    args = [ctypes.c_void_p(x) for x in p] + [B, H, Nq, Nk, d, ctypes.c_float(scale)]
+    if fn == "attn_jvp_fwd_ws":
+        nb = ajvp.attn_jvp_workspace_bytes(max(B, 1), max(H, 1), max(Nk, 1), d)
+        args += [ctypes.c_void_p(A + 0x1000000 if ws is None else ws),
+                 ctypes.c_size_t(nb if ws_bytes is None else ws_bytes)]
+    args.append(ctypes.c_void_p(0))
+    return getattr(L, fn)(*args)
+
+
+FNS = ["attn_jvp_fwd", "attn_jvp_fwd_ws", "attn_jvp_fwd_f32"]
+
+
+@pytest.mark.parametrize("fn", FNS)
+def test_null_pointers(fn):
+    for i in range(8):  # q k v tq tk tv o to (lse may be NULL)
+        p = [A + j * 0x100000 for j in range(9)]
+        p[i] = 0
+        assert _call(fn, p) == EINVAL, i
+
+
+@pytest.mark.parametrize("fn", FNS)
+def test_bad_sizes(fn):
+    for kw in (dict(B=0), dict(H=0), dict(Nq=0), dict(Nk=0), dict(B=-1), dict(Nq=-5)):
+        assert _call(fn, **kw) == EINVAL, kw
+
+
+@pytest.mark.parametrize("fn", FNS)
+def test_bad_scale(fn):
+    for s in (float("nan"), float("inf"), -float("inf"), -0.5):
+        assert _call(fn, scale=s) == EINVAL, s
+
+
+@pytest.mark.parametrize("fn", FNS)
+def test_unsupported_head_dim(fn):
+    for d in (0, 32, 96, 256):
+        rc = _call(fn, d=d)
+        assert rc in (EUNSUPPORTED, EINVAL), (d, rc)
+    assert _call(fn, d=96) == EUNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", FNS)
+def test_oversized_slice(fn):
+    # one (b, h) slice of K past 2^31 bytes
+    assert _call(fn, Nk=1 << 24) == EUNSUPPORTED
+    # grid overflow: B*H*ceil(Nq/128) beyond int range
+    assert _call(fn, B=1 << 16, H=1 << 16, Nq=256) == EINVAL
+
+
+@pytest.mark.parametrize("fn", FNS)
+def test_misaligned(fn):
+    for i in range(8):
+        p = [A + j * 0x100000 for j in range(9)]
+        p[i] += 4
+        assert _call(fn, p) == EALIGN, i
+    p = [A + j * 0x100000 for j in range(9)]
+    p[8] += 2  # lse needs 4-byte alignment
+    assert _call(fn, p) == EALIGN
+
+
+def test_workspace_checks():
+    assert _call("attn_jvp_fwd_ws", ws=0) == EINVAL
+    assert _call("attn_jvp_fwd_ws", ws_bytes=100) == EINVAL
+    assert _call("attn_jvp_fwd_ws", ws=A + 0x1000000 + 16) == EALIGN

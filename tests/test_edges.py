@@ -1,0 +1,91 @@
+"""GPU edge cases: tiny and ragged sizes, both head dims, degenerate inputs."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import make_inputs
+
+from _gpu import check, run, to_device
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [1, 17, 63, 64, 65, 129]
+
+
+def _rand(B, H, Nq, Nk, d, dtype, seed, tsig=0.1):
+    g = torch.Generator().manual_seed(seed)
+    r = lambda n, sg=1.0: (torch.randn(B, H, n, d, generator=g) * sg).to(dtype)
+    return {"q": r(Nq), "k": r(Nk), "v": r(Nk), "dq": r(Nq, tsig), "dk": r(Nk, tsig),
+            "dv": r(Nk, tsig)}
+
+
+def _cmp(label, x, s):
+    outs = run(to_device(x), s)
+    refs = oracle.attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], s)
+    check(label, outs, refs, fp32=x["q"].dtype == torch.float32)
+    return outs
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_grid(dtype, d):
+    for i, Nq in enumerate(SIZES):
+        for j, Nk in enumerate(SIZES):
+            x = _rand(1, 2, Nq, Nk, d, dtype, seed=100 * i + j)
+            _cmp(f"{dtype} d={d} Nq={Nq} Nk={Nk}", x, 1.0 / math.sqrt(d))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_batches_and_heads_are_independent(dtype):
+    """B*H*row-tiles both divisible by 8 (remapped order) and not."""
+    for (B, H, Nq) in [(2, 3, 130), (2, 4, 256), (3, 1, 50)]:
+        x = _rand(B, H, Nq, 70, 128, dtype, seed=B * 10 + H)
+        _cmp(f"{dtype} B={B} H={H} Nq={Nq}", x, 1.0 / math.sqrt(128))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_single_key(dtype):
+    """Nk = 1: O = v0, dO = dv0, lse = s q.k0."""
+    x = _rand(1, 2, 77, 1, 128, dtype, seed=5)
+    o, to, lse = _cmp(f"{dtype} Nk=1", x, 0.2)
+    v0 = x["v"].float()[:, :, :1].expand(-1, -1, 77, -1)
+    dv0 = x["dv"].float()[:, :, :1].expand(-1, -1, 77, -1)
+    assert torch.equal(o.cpu(), v0) and torch.equal(to.cpu(), dv0)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_uniform_attention(dtype):
+    """Q = 0 (and scale = 0): P = 1/Nk, O = mean of V rows, lse = ln Nk."""
+    x = _rand(1, 2, 40, 300, 64, dtype, seed=6)
+    x["q"].zero_()
+    o, to, lse = _cmp(f"{dtype} Q=0", x, 0.125)
+    assert torch.allclose(lse.cpu(), torch.full_like(lse.cpu(), math.log(300)), atol=1e-5)
+    y = _rand(1, 2, 40, 300, 64, dtype, seed=7)
+    _cmp(f"{dtype} scale=0", y, 0.0)
+
+
+def test_large_logits():
+    """Row max logits up to ~60 (far past the lazy-rescale headroom) and very negative rows."""
+    x = _rand(1, 2, 130, 700, 128, torch.bfloat16, seed=8)
+    x["q"] = (x["q"].float() * 6.0).to(torch.bfloat16)
+    _cmp("bf16 large logits", x, 1.0 / math.sqrt(128))
+    y = _rand(1, 1, 64, 200, 64, torch.float32, seed=9)
+    y["k"] = y["k"] - 20.0 * y["q"].mean(dim=2, keepdim=True)  # shifts every logit down
+    _cmp("fp32 shifted logits", y, 0.125)
+
+
+def test_increasing_max_along_keys():
+    """Key norms grow with the key index, so the running max rises on every tile."""
+    x = _rand(1, 1, 128, 1024, 128, torch.bfloat16, seed=10)
+    ramp = torch.linspace(0.2, 3.0, 1024)[None, None, :, None]
+    x["k"] = (x["k"].float() * ramp).to(torch.bfloat16)
+    _cmp("bf16 rising max", x, 1.0 / math.sqrt(128))
+
+
+def test_cross_frozen_text_reduced():
+    x, s = make_inputs("text_cross_frozen", Nq=700, heads=[0, 3])
+    _cmp("text_cross_frozen reduced", x, s)
