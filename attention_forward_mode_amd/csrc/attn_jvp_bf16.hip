@@ -13,7 +13,7 @@
 //     for the second contraction keeps P and P*dS at 11 significant bits.
 //  2. attn_jvp_bf16: one workgroup = 4 waves x 32 query rows of one (b, h).
 //     Per 64-key tile: stage K, dK (bf16) and the packed V^T, dV^T (fp16) in
-//     LDS by direct global->LDS loads (double buffered, one tile ahead), then
+//     LDS through registers (double buffered, loads one tile ahead), then
 //     per wave and 32-key block
 //        S^T  = K Q^T            (bf16 MFMA 32x32x16, Q held in registers)
 //        dS^T = dK Q^T + K dQ^T  (same K fragments reused)
@@ -191,8 +191,6 @@ __device__ __attribute__((always_inline)) inline void jvp_block(RowState<D>& st,
   }
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 template <int D>
 __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -227,38 +225,45 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
     dqf[ks] = buf_load16(rtq, off);
   }
 
-  // Staging by direct global->LDS loads (no registers): each wave moves
-  // kDmaPerWave KiB per tile, 16 bytes per lane, into a contiguous KiB of LDS.
-  // K and dK come from the caller's tensors (zero past Nk through the buffer
-  // range check) with each lane fetching the chunk that belongs at its LDS slot
-  // under the XOR swizzle; V^T and dV^T are copied linearly from the packed tiles.
-  constexpr int kKiBPerTensor = G::kTileBytes / 1024;
+  // Staging through registers: per tile each thread loads kChunks 16-byte
+  // chunks of K|dK (from the caller's tensors; rows past Nk read as zero through
+  // the buffer range check) and kChunks of the packed V^T|dV^T tile, one tile
+  // ahead of the compute, and writes them to the other LDS buffer at the end of
+  // the iteration.  K and dK chunks are stored under the XOR swizzle.
+  constexpr int kChunks = G::kTileBytes * 4 / 16 / kThreads / 2;  // per pair of tensors
+  constexpr int kChunksPerTensor = kChunks / 2;
   const uint32_t kbytes = (uint32_t)Nk * D * 2;
   const auto rk = make_rsrc(k + bh * (size_t)Nk * D, kbytes);
   const auto rtk = make_rsrc(tk + bh * (size_t)Nk * D, kbytes);
   const auto rv = make_rsrc(vpack + bh * (size_t)ntiles * G::kPackTileBytes,
                             (uint32_t)ntiles * G::kPackTileBytes);
-  constexpr int kPerTensor = kKiBPerTensor / 4;        // KiB of each tensor per wave
-  auto issue_stage = [&](int kt, int buf) {
-    char* sbase = smem + buf * G::kStageBytes;
+  uint32_t kg_off[kChunks], kl_off[kChunks];
 #pragma unroll
-    for (int tensor = 0; tensor < 4; ++tensor)
+  for (int n = 0; n < kChunks; ++n) {
+    const int c = (tid + kThreads * n) % (kBC * D / 8);   // 16-byte chunk within one tensor
+    const int krow = c / (D / 8), ch = c % (D / 8);
+    kg_off[n] = (uint32_t)(krow * D * 2 + ch * 16);
+    kl_off[n] = (uint32_t)((n / kChunksPerTensor) * G::kTileBytes + krow * D * 2 +
+                           ((ch ^ (krow & 7)) << 4));
+  }
+  u32x4 stg[2 * kChunks];
+  auto load_stage = [&](int kt) {
+    const uint32_t kbase = (uint32_t)kt * kBC * D * 2;
 #pragma unroll
-      for (int j = 0; j < kPerTensor; ++j) {
-        const int kib = wave * kPerTensor + j;         // KiB index within this tensor's tile
-        const int P = kib * 64 + lane;                 // 16-byte slot within the tile
-        lds_void* dst = (lds_void*)(sbase + tensor * G::kTileBytes + kib * 1024);
-        if (tensor < 2) {
-          const int krow = P / (D / 8), phys = P % (D / 8);
-          const uint32_t off =
-              (uint32_t)kt * kBC * D * 2 + krow * D * 2 + ((phys ^ (krow & 7)) << 4);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(tensor == 0 ? rk : rtk, dst, 16, off, 0, 0, 0);
-        } else {
-          const uint32_t off =
-              (uint32_t)kt * G::kPackTileBytes + (tensor - 2) * G::kTileBytes + P * 16;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, off, 0, 0, 0);
-        }
-      }
+    for (int n = 0; n < kChunks; ++n)
+      stg[n] = buf_load16(n < kChunksPerTensor ? rk : rtk, kbase + kg_off[n]);
+    const uint32_t vbase = (uint32_t)kt * G::kPackTileBytes;
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n)
+      stg[kChunks + n] = buf_load16(rv, vbase + (uint32_t)(tid + kThreads * n) * 16);
+  };
+  auto store_stage = [&](int buf) {
+    char* sb = smem + buf * G::kStageBytes;
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n) lds_store16(sb + kl_off[n], stg[n]);
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n)
+      lds_store16(sb + 2 * G::kTileBytes + (tid + kThreads * n) * 16, stg[kChunks + n]);
   };
 
   RowState<D> st;
@@ -271,18 +276,18 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
   st.l = 0.f;
   st.u = 0.f;
 
-  issue_stage(0, 0);
+  load_stage(0);
+  store_stage(0);
   __syncthreads();
   for (int kt = 0; kt < ntiles - 1; ++kt) {
-    // The other buffer was last read in iteration kt-1, which every wave has
-    // finished (barrier below), so the next tile can stream into it now.
-    issue_stage(kt + 1, (kt + 1) & 1);
+    load_stage(kt + 1);  // in flight during this tile's compute
     const char* stage = smem + (kt & 1) * G::kStageBytes;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
       jvp_block<D, false>(st, stage, kb, qf, dqf, l32, g, kt * kBC + 32 * kb, Nk, c_log2, scale);
-    // Own direct loads complete (vmcnt), then everyone's (barrier).
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    // The other buffer was last read in iteration kt-1, which every wave has
+    // finished (barrier at its end), so it can be overwritten now.
+    store_stage((kt + 1) & 1);
     __syncthreads();
   }
   {

@@ -5,8 +5,8 @@
 // in fp32 end to end: it is the precision reference the pages motivate (the
 // record's second takeaway: BF16 JVP error is much larger than BF16 output
 // error, Fig. 11).  Structure: one workgroup = 4 waves x 32 query rows; 32-key
-// tiles of K, dK, V, dV staged in LDS by direct global->LDS loads (double
-// buffered, one tile ahead); fp32 MFMA 32x32x2 for S^T = K Q^T, dS^T = dK Q^T + K dQ^T,
+// tiles of K, dK, V, dV staged in LDS through registers (double buffered,
+// loads one tile ahead); fp32 MFMA 32x32x2 for S^T = K Q^T, dS^T = dK Q^T + K dQ^T,
 // A^T += V^T P^T and G^T += V^T (s P dS)^T + dV^T P^T; online softmax per lane.
 #include "cdna4.hpp"
 #include "launch.hpp"
@@ -28,8 +28,6 @@ struct GeoF {
   static constexpr int kCB = D / 32;
   static constexpr int kRowChunks = D / 4;             // 16-byte chunks per row
 };
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ inline f32x16 mma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -72,6 +70,7 @@ __device__ __attribute__((always_inline)) inline void jvp_tile_f32(
       ds = mma_f32(a[e], dqf[j][e], ds);
       ds = mma_f32(da[e], qf[j][e], ds);
     }
+    if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
   }
   auto masked = [&](int r) { return kMask && key0 + 8 * (r >> 2) + 4 * g + (r & 3) >= Nk; };
   if constexpr (kMask) {
@@ -123,6 +122,9 @@ __device__ __attribute__((always_inline)) inline void jvp_tile_f32(
       st.accA[cb] = mma_f32(a, p[r], st.accA[cb]);
       st.accG[cb] = mma_f32(a, pd[r], st.accG[cb]);
       st.accG[cb] = mma_f32(da, p[r], st.accG[cb]);
+      // Keep the scheduler from hoisting every LDS read of the tile at once
+      // (that alone would exceed the register file next to the fp32 operands).
+      if ((r & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -155,29 +157,36 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_f32_body(
     dqf[j] = __builtin_bit_cast(f32x4, buf_load16(rtq, off));
   }
 
-  // Staging by direct global->LDS loads: each wave moves a quarter of each
-  // tensor's tile, 16 bytes per lane into a contiguous KiB of LDS; each lane
-  // fetches the chunk that belongs at its LDS slot under the XOR swizzle.  Rows
-  // past Nk read as zero through the buffer range check.
+  // Staging through registers: each thread loads kChunks 16-byte chunks of the
+  // four 32-key tiles (rows past Nk read as zero through the buffer range check)
+  // one tile ahead of the compute and writes them, XOR-swizzled, to the other
+  // LDS buffer at the end of the iteration.
+  constexpr int kChunks = G::kStageBytes / 16 / kThreads;
+  constexpr int kChunksPerTensor = kChunks / 4;
   const uint32_t kbytes = (uint32_t)Nk * D * 4;
   const __amdgpu_buffer_rsrc_t rsrc[4] = {make_rsrc(k + bh * (size_t)Nk * D, kbytes),
                                           make_rsrc(tk + bh * (size_t)Nk * D, kbytes),
                                           make_rsrc(v + bh * (size_t)Nk * D, kbytes),
                                           make_rsrc(tv + bh * (size_t)Nk * D, kbytes)};
-  constexpr int kPerTensor = G::kTileBytes / 1024 / 4;  // KiB of each tensor per wave
-  auto issue_stage = [&](int kt, int buf) {
-    char* sbase = smem + buf * G::kStageBytes;
+  uint32_t g_off[kChunks], l_off[kChunks];
 #pragma unroll
-    for (int tensor = 0; tensor < 4; ++tensor)
+  for (int n = 0; n < kChunks; ++n) {
+    const int c = (tid + kThreads * n) % (kBC * G::kRowChunks);
+    const int r = c / G::kRowChunks, ch = c % G::kRowChunks;
+    g_off[n] = (uint32_t)(r * D * 4 + ch * 16);
+    l_off[n] = (uint32_t)((n / kChunksPerTensor) * G::kTileBytes + swz<D>(r, ch));
+  }
+  u32x4 stg[kChunks];
+  auto load_stage = [&](int kt) {
+    const uint32_t base = (uint32_t)kt * kBC * D * 4;
 #pragma unroll
-      for (int j = 0; j < kPerTensor; ++j) {
-        const int kib = wave * kPerTensor + j;
-        const int P = kib * 64 + lane;
-        const int r = P / G::kRowChunks, phys = P % G::kRowChunks;
-        const uint32_t off = (uint32_t)kt * kBC * D * 4 + r * D * 4 + ((phys ^ (r & 7)) << 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc[tensor], (lds_void*)(sbase + tensor * G::kTileBytes + kib * 1024), 16, off, 0, 0, 0);
-      }
+    for (int n = 0; n < kChunks; ++n)
+      stg[n] = buf_load16(rsrc[n / kChunksPerTensor], base + g_off[n]);
+  };
+  auto store_stage = [&](int buf) {
+    char* sb = smem + buf * G::kStageBytes;
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n) lds_store16(sb + l_off[n], stg[n]);
   };
 
   RowStateF<D> st;
@@ -190,13 +199,14 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_f32_body(
   st.l = 0.f;
   st.u = 0.f;
 
-  issue_stage(0, 0);
+  load_stage(0);
+  store_stage(0);
   __syncthreads();
   for (int kt = 0; kt < ntiles - 1; ++kt) {
-    issue_stage(kt + 1, (kt + 1) & 1);
+    load_stage(kt + 1);
     jvp_tile_f32<D, false>(st, smem + (kt & 1) * G::kStageBytes, qf, dqf, l32, g, kt * kBC, Nk,
                            c_log2, scale);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    store_stage((kt + 1) & 1);
     __syncthreads();
   }
   {

@@ -25,6 +25,9 @@ def to_device(x, dev="cuda:0"):
 
 def run(g, scale, lse=True):
     args = [g[n] for n in NAMES]
+    # name the case before the launch, so a device fault can be traced to it
+    print(f"  launch {str(g['q'].dtype)[6:]} q{tuple(g['q'].shape)} k{tuple(g['k'].shape)} "
+          f"scale={scale:.4g}", flush=True)
     if g["q"].dtype == torch.bfloat16:
         out = ajvp.attn_jvp_fwd(*args, scale=scale, lse=lse)
     else:
