@@ -14,7 +14,10 @@
 
 namespace {
 
-constexpr int64_t kMaxSliceBytes = int64_t(1) << 31;  // one (b, h) slice, 32-bit buffer offsets
+// Every tensor is addressed with 32-bit byte offsets from its base (buffer
+// descriptors spanning the whole tensor), and B*H is the grid's y extent.
+constexpr int64_t kMaxTensorBytes = int64_t(1) << 31;
+constexpr int64_t kMaxSlices = 65535;
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -27,12 +30,16 @@ int validate(const void* const* in, float* o, float* to, float* lse, int B, int 
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_JVP_EINVAL;
   if (!(scale >= 0.0f) || std::isinf(scale)) return ATTN_JVP_EINVAL;
   if (d != 64 && d != 128) return ATTN_JVP_EUNSUPPORTED;
-  // Grid and offsets: B*H*ceil(Nq/128) workgroups and B*H*ceil(Nk/64) pack
-  // workgroups must fit an int; per-slice byte counts must fit 2^31 (padded).
+  // Grid: (ceil(Nq/128), B*H) workgroups; pack: (ceil(Nk/64), B*H).  Every
+  // tensor, including the padded fp16 V/dV workspace (2*Nk_pad*d*2 bytes per
+  // slice), must stay under 2^31 bytes.
   const int64_t bh = int64_t(B) * H;
-  const int64_t qpad = (int64_t(Nq) + 127) / 128 * 128, kpad = (int64_t(Nk) + 63) / 64 * 64;
-  if (bh * (qpad / 128) > INT32_MAX || bh * (kpad / 64) > INT32_MAX) return ATTN_JVP_EINVAL;
-  if (qpad * d * esize >= kMaxSliceBytes || kpad * d * esize >= kMaxSliceBytes)
+  const int64_t kpad = (int64_t(Nk) + 63) / 64 * 64;
+  if (bh > kMaxSlices) return ATTN_JVP_EUNSUPPORTED;
+  const int64_t qb = bh * Nq * d * esize, kb = bh * kpad * d * esize, ob = bh * Nq * d * 4;
+  const int64_t wsb = bh * kpad * d * 2 * 2;
+  if (qb >= kMaxTensorBytes || kb >= kMaxTensorBytes || ob >= kMaxTensorBytes ||
+      wsb >= kMaxTensorBytes)
     return ATTN_JVP_EUNSUPPORTED;
   for (int i = 0; i < 6; ++i)
     if (misaligned(in[i], 16)) return ATTN_JVP_EALIGN;
@@ -77,7 +84,7 @@ const char* attn_jvp_strerror(int status) {
   switch (status) {
     case ATTN_JVP_OK: return "ok";
     case ATTN_JVP_EINVAL: return "invalid argument (null pointer, size < 1, bad scale or workspace, or size overflow)";
-    case ATTN_JVP_EUNSUPPORTED: return "unsupported (head dim must be 64 or 128; a (b, h) slice must stay under 2^31 bytes)";
+    case ATTN_JVP_EUNSUPPORTED: return "unsupported (head dim must be 64 or 128, B*H at most 65535, each tensor under 2^31 bytes)";
     case ATTN_JVP_EALIGN: return "misaligned pointer (tensors need 16-byte, workspace 256-byte alignment)";
     case ATTN_JVP_ELAUNCH: return "HIP launch or allocation failed";
     default: return "unknown status";

@@ -59,19 +59,27 @@ template <int D>
 __device__ __attribute__((always_inline)) inline void pack_v_body(const uint16_t* __restrict__ v,
                                                                   const uint16_t* __restrict__ dv,
                                                                   char* __restrict__ ws, int Nk,
-                                                                  int ntiles) {
+                                                                  int ntiles, uint32_t v_bytes,
+                                                                  uint32_t ws_bytes) {
   using G = Geo<D>;
   __shared__ _Float16 sv[2][kBC][D + 2];
-  const int tile = blockIdx.x % ntiles;
-  const size_t bh = blockIdx.x / ntiles;
-  const uint16_t* src[2] = {v + bh * (size_t)Nk * D, dv + bh * (size_t)Nk * D};
+  const int tile = blockIdx.x;                 // 64-key tile
+  const uint32_t bh = blockIdx.y;              // (b, h) slice
+  // Every global access goes through a buffer descriptor spanning the whole
+  // tensor: an offset outside it is dropped (stores) or reads zero (loads).
+  const auto rv = make_rsrc(v, v_bytes);
+  const auto rdv = make_rsrc(dv, v_bytes);
+  const auto rws = make_rsrc(ws, ws_bytes);
   const int key0 = tile * kBC;
   constexpr int kIn = kBC * D / 8;  // 16-byte input chunks per tensor
   for (int c = threadIdx.x; c < 2 * kIn; c += kThreads) {
     const int t = c / kIn, rem = c % kIn, r = rem / (D / 8), col = (rem % (D / 8)) * 8;
     const int key = key0 + r;
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < Nk) x = *reinterpret_cast<const u32x4*>(src[t] + (size_t)key * D + col);
+    if (key < Nk) {
+      const uint32_t off = ((bh * (uint32_t)Nk + key) * D + col) * 2;
+      x = buf_load16(t == 0 ? rv : rdv, off);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t bits = (x[e >> 1] >> (16 * (e & 1))) & 0xffffu;
@@ -79,15 +87,14 @@ __device__ __attribute__((always_inline)) inline void pack_v_body(const uint16_t
     }
   }
   __syncthreads();
-  char* out = ws + ((size_t)bh * ntiles + tile) * G::kPackTileBytes;
+  const uint32_t out = (bh * (uint32_t)ntiles + tile) * G::kPackTileBytes;
   for (int c = threadIdx.x; c < 2 * D * 8; c += kThreads) {
     const int t = c / (D * 8), rem = c % (D * 8), col = rem / 8, p = rem % 8;
     f16x8 h;
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = sv[t][packed_key(8 * p + e)][col];
     const int phys = p ^ (col & 7);
-    *reinterpret_cast<u32x4*>(out + t * G::kTileBytes + col * 128 + phys * 16) =
-        __builtin_bit_cast(u32x4, h);
+    buf_store16(rws, out + t * G::kTileBytes + col * 128 + phys * 16, __builtin_bit_cast(u32x4, h));
   }
 }
 
@@ -129,15 +136,18 @@ __device__ __attribute__((always_inline)) inline void jvp_block(RowState<D>& st,
     ds = mma_bf16(da, qf[ks], ds);
   }
 
-  // Keys past Nk (last tile only) are zero rows of K and dK; they are left out
-  // of the max and get p = 0.
+  // Keys past Nk (last tile only) are left out of the max and get p = 0 and
+  // dS = 0, whatever their staged rows hold.
   auto masked = [&](int r) {
     return kMask && key0 + 8 * (r >> 2) + 4 * g + (r & 3) >= Nk;
   };
   if constexpr (kMask) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (masked(r)) s[r] = -INFINITY;
+      if (masked(r)) {
+        s[r] = -INFINITY;
+        ds[r] = 0.f;
+      }
   }
 
   // ---- online softmax; each lane owns query row l32, lane halves split keys ----
@@ -191,68 +201,78 @@ __device__ __attribute__((always_inline)) inline void jvp_block(RowState<D>& st,
   }
 }
 
+// Sizes of the whole tensors (bytes) the kernel may touch; each global access
+// is checked against them by the buffer descriptor.
+struct Extents {
+  uint32_t q_bytes, k_bytes, ws_bytes, o_bytes, lse_bytes;
+};
+
 template <int D>
 __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ tq, const uint16_t* __restrict__ tk,
     const char* __restrict__ vpack, float* __restrict__ o, float* __restrict__ to,
-    float* __restrict__ lse, int Nq, int Nk, int nqt, int ntiles, int total_wg, float scale,
+    float* __restrict__ lse, int Nq, int Nk, int ntiles, Extents ext, float scale,
     float c_log2) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * G::kStageBytes];
 
-  // Work item.  Hardware deals workgroups round-robin over the 8 XCDs; remap so
-  // that each XCD walks a contiguous range of (b, h, row-tile) ids and its
-  // concurrently resident workgroups share one head's K/V in that XCD's L2.
-  int id = blockIdx.x;
-  if ((total_wg & 7) == 0) id = (id & 7) * (total_wg >> 3) + (id >> 3);
-  const int qt = to_sgpr(id % nqt);
-  const size_t bh = (size_t)to_sgpr(id / nqt);
-
-  const int tid = threadIdx.x, wave = to_sgpr(tid >> 6), lane = tid & 63;
+  // Work item: blockIdx.x = 128-row query tile, blockIdx.y = (b, h) slice.
+  const int qt = blockIdx.x;
+  const uint32_t bh = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
   const int row = qt * kBR + wave * kRowsPerWave + l32;
+  const bool row_ok = row < Nq;
+
+  // Buffer descriptors over whole tensors (see Extents).
+  const auto rq = make_rsrc(q, ext.q_bytes);
+  const auto rtq = make_rsrc(tq, ext.q_bytes);
+  const auto rk = make_rsrc(k, ext.k_bytes);
+  const auto rtk = make_rsrc(tk, ext.k_bytes);
+  const auto rv = make_rsrc(vpack, ext.ws_bytes);
+  const auto ro = make_rsrc(o, ext.o_bytes);
+  const auto rto = make_rsrc(to, ext.o_bytes);
 
   // Q and dQ fragments: the B operand of S^T = K Q^T (lane: row l32, d-slice g).
-  const uint32_t qbytes = (uint32_t)Nq * D * 2;
-  const auto rq = make_rsrc(q + bh * (size_t)Nq * D, qbytes);
-  const auto rtq = make_rsrc(tq + bh * (size_t)Nq * D, qbytes);
+  // Rows past Nq get an offset past the tensor, which the descriptor reads as 0.
   u32x4 qf[G::kKS], dqf[G::kKS];
+  const uint32_t qrow = row_ok ? (bh * (uint32_t)Nq + row) * D * 2 : 0x80000000u;
 #pragma unroll
   for (int ks = 0; ks < G::kKS; ++ks) {
-    const uint32_t off = (uint32_t)row * D * 2 + (16 * ks + 8 * g) * 2;
+    const uint32_t off = qrow + (16 * ks + 8 * g) * 2;
     qf[ks] = buf_load16(rq, off);
     dqf[ks] = buf_load16(rtq, off);
   }
 
   // Staging through registers: per tile each thread loads kChunks 16-byte
-  // chunks of K|dK (from the caller's tensors; rows past Nk read as zero through
-  // the buffer range check) and kChunks of the packed V^T|dV^T tile, one tile
-  // ahead of the compute, and writes them to the other LDS buffer at the end of
-  // the iteration.  K and dK chunks are stored under the XOR swizzle.
+  // chunks of K|dK and kChunks of the packed V^T|dV^T tile, one tile ahead of
+  // the compute, and writes them to the other LDS buffer at the end of the
+  // iteration.  K and dK chunks are stored under the XOR swizzle.  Key rows
+  // past Nk in the last tile hold whatever the descriptor returns; they are
+  // masked in the compute.
   constexpr int kChunks = G::kTileBytes * 4 / 16 / kThreads / 2;  // per pair of tensors
   constexpr int kChunksPerTensor = kChunks / 2;
-  const uint32_t kbytes = (uint32_t)Nk * D * 2;
-  const auto rk = make_rsrc(k + bh * (size_t)Nk * D, kbytes);
-  const auto rtk = make_rsrc(tk + bh * (size_t)Nk * D, kbytes);
-  const auto rv = make_rsrc(vpack + bh * (size_t)ntiles * G::kPackTileBytes,
-                            (uint32_t)ntiles * G::kPackTileBytes);
-  uint32_t kg_off[kChunks], kl_off[kChunks];
-#pragma unroll
-  for (int n = 0; n < kChunks; ++n) {
-    const int c = (tid + kThreads * n) % (kBC * D / 8);   // 16-byte chunk within one tensor
+  const uint32_t kslice = bh * (uint32_t)Nk * D * 2;
+  const uint32_t vslice = bh * (uint32_t)ntiles * G::kPackTileBytes;
+  // Chunk c of a tensor's tile is key row c / (D/8), 16-byte column c % (D/8).
+  auto kg_off = [&](int n) {
+    const int c = (tid + kThreads * n) % (kBC * D / 8);
+    return (uint32_t)((c / (D / 8)) * D * 2 + (c % (D / 8)) * 16);
+  };
+  auto kl_off = [&](int n) {
+    const int c = (tid + kThreads * n) % (kBC * D / 8);
     const int krow = c / (D / 8), ch = c % (D / 8);
-    kg_off[n] = (uint32_t)(krow * D * 2 + ch * 16);
-    kl_off[n] = (uint32_t)((n / kChunksPerTensor) * G::kTileBytes + krow * D * 2 +
-                           ((ch ^ (krow & 7)) << 4));
-  }
+    return (uint32_t)((n / kChunksPerTensor) * G::kTileBytes + krow * D * 2 +
+                      ((ch ^ (krow & 7)) << 4));
+  };
   u32x4 stg[2 * kChunks];
   auto load_stage = [&](int kt) {
-    const uint32_t kbase = (uint32_t)kt * kBC * D * 2;
+    const uint32_t kbase = kslice + (uint32_t)kt * kBC * D * 2;
 #pragma unroll
     for (int n = 0; n < kChunks; ++n)
-      stg[n] = buf_load16(n < kChunksPerTensor ? rk : rtk, kbase + kg_off[n]);
-    const uint32_t vbase = (uint32_t)kt * G::kPackTileBytes;
+      stg[n] = buf_load16(n < kChunksPerTensor ? rk : rtk, kbase + kg_off(n));
+    const uint32_t vbase = vslice + (uint32_t)kt * G::kPackTileBytes;
 #pragma unroll
     for (int n = 0; n < kChunks; ++n)
       stg[kChunks + n] = buf_load16(rv, vbase + (uint32_t)(tid + kThreads * n) * 16);
@@ -260,7 +280,7 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
   auto store_stage = [&](int buf) {
     char* sb = smem + buf * G::kStageBytes;
 #pragma unroll
-    for (int n = 0; n < kChunks; ++n) lds_store16(sb + kl_off[n], stg[n]);
+    for (int n = 0; n < kChunks; ++n) lds_store16(sb + kl_off(n), stg[n]);
 #pragma unroll
     for (int n = 0; n < kChunks; ++n)
       lds_store16(sb + 2 * G::kTileBytes + (tid + kThreads * n) * 16, stg[kChunks + n]);
@@ -304,9 +324,8 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
   const float u = st.u + swap_halves(st.u);
   const float inv_l = 1.0f / l;
   const float mu = u * scale * inv_l;
-  if (row < Nq) {
-    float* orow = o + (bh * (size_t)Nq + row) * D;
-    float* trow = to + (bh * (size_t)Nq + row) * D;
+  if (row_ok) {
+    const uint32_t orow = (bh * (uint32_t)Nq + row) * D * 4;
 #pragma unroll
     for (int cb = 0; cb < G::kCB; ++cb)
 #pragma unroll
@@ -319,39 +338,43 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
           ov[e] = a;
           tv[e] = st.accG[cb][4 * qq + e] * inv_l - mu * a;
         }
-        *reinterpret_cast<f32x4*>(orow + c0) = ov;
-        *reinterpret_cast<f32x4*>(trow + c0) = tv;
+        buf_store16(ro, orow + c0 * 4, __builtin_bit_cast(u32x4, ov));
+        buf_store16(rto, orow + c0 * 4, __builtin_bit_cast(u32x4, tv));
       }
-    if (lse != nullptr && g == 0) lse[bh * (size_t)Nq + row] = (st.m + __log2f(l)) * kLn2;
+    if (lse != nullptr && g == 0) {
+      const auto rl = make_rsrc(lse, ext.lse_bytes);
+      buf_store4(rl, (bh * (uint32_t)Nq + row) * 4, (st.m + __log2f(l)) * kLn2);
+    }
   }
 }
 
-#define AJVP_BF16_KERNEL(D)                                                                  \
-  __global__ __launch_bounds__(kThreads, 1) void attn_jvp_bf16_d##D(                          \
-      const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,                         \
-      const uint16_t* __restrict__ tq, const uint16_t* __restrict__ tk,                       \
-      const char* __restrict__ vpack, float* __restrict__ o, float* __restrict__ to,          \
-      float* __restrict__ lse, int Nq, int Nk, int nqt, int ntiles, int total_wg, float scale,  \
-      float c_log2) {                                                                          \
-    attn_jvp_bf16_body<D>(q, k, tq, tk, vpack, o, to, lse, Nq, Nk, nqt, ntiles, total_wg, scale, \
-                          c_log2);                                                             \
-  }                                                                                            \
-  __global__ __launch_bounds__(kThreads) void pack_v_d##D(const uint16_t* __restrict__ v,     \
-                                                          const uint16_t* __restrict__ dv,    \
-                                                          char* __restrict__ ws, int Nk,      \
-                                                          int ntiles) {                       \
-    pack_v_body<D>(v, dv, ws, Nk, ntiles);                                                     \
+#define AJVP_BF16_KERNEL(D)                                                                 \
+  __global__ __launch_bounds__(kThreads, 1) void attn_jvp_bf16_d##D(                         \
+      const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,                        \
+      const uint16_t* __restrict__ tq, const uint16_t* __restrict__ tk,                      \
+      const char* __restrict__ vpack, float* __restrict__ o, float* __restrict__ to,         \
+      float* __restrict__ lse, int Nq, int Nk, int ntiles, Extents ext, float scale,         \
+      float c_log2) {                                                                         \
+    attn_jvp_bf16_body<D>(q, k, tq, tk, vpack, o, to, lse, Nq, Nk, ntiles, ext, scale, c_log2); \
+  }                                                                                           \
+  __global__ __launch_bounds__(kThreads) void pack_v_d##D(                                   \
+      const uint16_t* __restrict__ v, const uint16_t* __restrict__ dv, char* __restrict__ ws, \
+      int Nk, int ntiles, uint32_t v_bytes, uint32_t ws_bytes) {                              \
+    pack_v_body<D>(v, dv, ws, Nk, ntiles, v_bytes, ws_bytes);                                 \
   }
 AJVP_BF16_KERNEL(64)
 AJVP_BF16_KERNEL(128)
 #undef AJVP_BF16_KERNEL
 
-template <int D> struct Kernels;
-template <> struct Kernels<64> {
+template <int D>
+struct Kernels;
+template <>
+struct Kernels<64> {
   static constexpr auto main = attn_jvp_bf16_d64;
   static constexpr auto pack = pack_v_d64;
 };
-template <> struct Kernels<128> {
+template <>
+struct Kernels<128> {
   static constexpr auto main = attn_jvp_bf16_d128;
   static constexpr auto pack = pack_v_d128;
 };
@@ -363,16 +386,21 @@ hipError_t launch_bf16_d(const void* q, const void* k, const void* v, const void
   const int ntiles = (Nk + kBC - 1) / kBC;
   const int nqt = (Nq + kBR - 1) / kBR;
   const int bh = B * H;
-  hipLaunchKernelGGL(Kernels<D>::pack, dim3(ntiles * bh), dim3(kThreads), 0, stream,
+  Extents ext;
+  ext.q_bytes = (uint32_t)((size_t)bh * Nq * D * 2);
+  ext.k_bytes = (uint32_t)((size_t)bh * Nk * D * 2);
+  ext.ws_bytes = (uint32_t)bf16_workspace_bytes(B, H, Nk, D);
+  ext.o_bytes = (uint32_t)((size_t)bh * Nq * D * 4);
+  ext.lse_bytes = (uint32_t)((size_t)bh * Nq * 4);
+  hipLaunchKernelGGL(Kernels<D>::pack, dim3(ntiles, bh), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(tv),
-                     static_cast<char*>(ws), Nk, ntiles);
+                     static_cast<char*>(ws), Nk, ntiles, ext.k_bytes, ext.ws_bytes);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int total = bh * nqt;
-  hipLaunchKernelGGL(Kernels<D>::main, dim3(total), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(Kernels<D>::main, dim3(nqt, bh), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(tq), static_cast<const uint16_t*>(tk),
-                     static_cast<const char*>(ws), o, to, lse, Nq, Nk, nqt, ntiles, total, scale,
+                     static_cast<const char*>(ws), o, to, lse, Nq, Nk, ntiles, ext, scale,
                      scale * kLog2e);
   return hipGetLastError();
 }

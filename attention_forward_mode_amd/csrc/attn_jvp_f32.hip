@@ -129,59 +129,69 @@ __device__ __attribute__((always_inline)) inline void jvp_tile_f32(
   }
 }
 
+// Sizes of the whole tensors (bytes); every global access is checked against
+// them by its buffer descriptor.
+struct ExtentsF {
+  uint32_t q_bytes, k_bytes, o_bytes, lse_bytes;
+};
+
 template <int D>
 __device__ __attribute__((always_inline)) inline void attn_jvp_f32_body(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ tq, const float* __restrict__ tk, const float* __restrict__ tv,
     float* __restrict__ o, float* __restrict__ to, float* __restrict__ lse, int Nq, int Nk,
-    int nqt, int ntiles, int total_wg, float scale, float c_log2) {
+    int ntiles, ExtentsF ext, float scale, float c_log2) {
   using G = GeoF<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * G::kStageBytes];
 
-  int id = blockIdx.x;
-  if ((total_wg & 7) == 0) id = (id & 7) * (total_wg >> 3) + (id >> 3);
-  const int qt = to_sgpr(id % nqt);
-  const size_t bh = (size_t)to_sgpr(id / nqt);
-  const int tid = threadIdx.x, wave = to_sgpr(tid >> 6), lane = tid & 63;
+  // Work item: blockIdx.x = 128-row query tile, blockIdx.y = (b, h) slice.
+  const int qt = blockIdx.x;
+  const uint32_t bh = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
   const int row = qt * kBR + wave * kRowsPerWave + l32;
+  const bool row_ok = row < Nq;
 
-  const uint32_t qbytes = (uint32_t)Nq * D * 4;
-  const auto rq = make_rsrc(q + bh * (size_t)Nq * D, qbytes);
-  const auto rtq = make_rsrc(tq + bh * (size_t)Nq * D, qbytes);
+  const auto rq = make_rsrc(q, ext.q_bytes);
+  const auto rtq = make_rsrc(tq, ext.q_bytes);
+  // Rows past Nq get an offset past the tensor, which the descriptor reads as 0.
   f32x4 qf[G::kQ4], dqf[G::kQ4];
+  const uint32_t qrow = row_ok ? (bh * (uint32_t)Nq + row) * D * 4 : 0x80000000u;
 #pragma unroll
   for (int j = 0; j < G::kQ4; ++j) {
-    const uint32_t off = (uint32_t)row * D * 4 + (8 * j + 4 * g) * 4;
+    const uint32_t off = qrow + (8 * j + 4 * g) * 4;
     qf[j] = __builtin_bit_cast(f32x4, buf_load16(rq, off));
     dqf[j] = __builtin_bit_cast(f32x4, buf_load16(rtq, off));
   }
 
   // Staging through registers: each thread loads kChunks 16-byte chunks of the
-  // four 32-key tiles (rows past Nk read as zero through the buffer range check)
-  // one tile ahead of the compute and writes them, XOR-swizzled, to the other
-  // LDS buffer at the end of the iteration.
+  // four 32-key tiles one tile ahead of the compute (key rows past Nk are set
+  // to zero) and writes them, XOR-swizzled, to the other LDS buffer at the end
+  // of the iteration.
   constexpr int kChunks = G::kStageBytes / 16 / kThreads;
   constexpr int kChunksPerTensor = kChunks / 4;
-  const uint32_t kbytes = (uint32_t)Nk * D * 4;
-  const __amdgpu_buffer_rsrc_t rsrc[4] = {make_rsrc(k + bh * (size_t)Nk * D, kbytes),
-                                          make_rsrc(tk + bh * (size_t)Nk * D, kbytes),
-                                          make_rsrc(v + bh * (size_t)Nk * D, kbytes),
-                                          make_rsrc(tv + bh * (size_t)Nk * D, kbytes)};
+  const __amdgpu_buffer_rsrc_t rsrc[4] = {make_rsrc(k, ext.k_bytes), make_rsrc(tk, ext.k_bytes),
+                                          make_rsrc(v, ext.k_bytes), make_rsrc(tv, ext.k_bytes)};
+  const uint32_t kslice = bh * (uint32_t)Nk * D * 4;
   uint32_t g_off[kChunks], l_off[kChunks];
+  int c_row[kChunks];
 #pragma unroll
   for (int n = 0; n < kChunks; ++n) {
     const int c = (tid + kThreads * n) % (kBC * G::kRowChunks);
     const int r = c / G::kRowChunks, ch = c % G::kRowChunks;
+    c_row[n] = r;
     g_off[n] = (uint32_t)(r * D * 4 + ch * 16);
     l_off[n] = (uint32_t)((n / kChunksPerTensor) * G::kTileBytes + swz<D>(r, ch));
   }
   u32x4 stg[kChunks];
   auto load_stage = [&](int kt) {
-    const uint32_t base = (uint32_t)kt * kBC * D * 4;
+    const uint32_t base = kslice + (uint32_t)kt * kBC * D * 4;
 #pragma unroll
-    for (int n = 0; n < kChunks; ++n)
-      stg[n] = buf_load16(rsrc[n / kChunksPerTensor], base + g_off[n]);
+    for (int n = 0; n < kChunks; ++n) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const u32x4 x = buf_load16(rsrc[n / kChunksPerTensor], base + g_off[n]);
+      stg[n] = (kt * kBC + c_row[n] < Nk) ? x : zero;
+    }
   };
   auto store_stage = [&](int buf) {
     char* sb = smem + buf * G::kStageBytes;
@@ -219,9 +229,10 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_f32_body(
   const float u = st.u + swap_halves(st.u);
   const float inv_l = 1.0f / l;
   const float mu = u * scale * inv_l;
-  if (row < Nq) {
-    float* orow = o + (bh * (size_t)Nq + row) * D;
-    float* trow = to + (bh * (size_t)Nq + row) * D;
+  if (row_ok) {
+    const auto ro = make_rsrc(o, ext.o_bytes);
+    const auto rto = make_rsrc(to, ext.o_bytes);
+    const uint32_t orow = (bh * (uint32_t)Nq + row) * D * 4;
 #pragma unroll
     for (int cb = 0; cb < G::kCB; ++cb)
 #pragma unroll
@@ -234,21 +245,23 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_f32_body(
           ov[e] = a;
           tv4[e] = st.accG[cb][4 * qq + e] * inv_l - mu * a;
         }
-        *reinterpret_cast<f32x4*>(orow + c0) = ov;
-        *reinterpret_cast<f32x4*>(trow + c0) = tv4;
+        buf_store16(ro, orow + c0 * 4, __builtin_bit_cast(u32x4, ov));
+        buf_store16(rto, orow + c0 * 4, __builtin_bit_cast(u32x4, tv4));
       }
-    if (lse != nullptr && g == 0) lse[bh * (size_t)Nq + row] = (st.m + __log2f(l)) * kLn2;
+    if (lse != nullptr && g == 0) {
+      const auto rl = make_rsrc(lse, ext.lse_bytes);
+      buf_store4(rl, (bh * (uint32_t)Nq + row) * 4, (st.m + __log2f(l)) * kLn2);
+    }
   }
 }
 
-#define AJVP_F32_KERNEL(D)                                                                      \
-  __global__ __launch_bounds__(kThreads, 1) void attn_jvp_f32_d##D(                              \
-      const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,     \
-      const float* __restrict__ tq, const float* __restrict__ tk, const float* __restrict__ tv,  \
-      float* __restrict__ o, float* __restrict__ to, float* __restrict__ lse, int Nq, int Nk,    \
-      int nqt, int ntiles, int total_wg, float scale, float c_log2) {                            \
-    attn_jvp_f32_body<D>(q, k, v, tq, tk, tv, o, to, lse, Nq, Nk, nqt, ntiles, total_wg, scale,  \
-                         c_log2);                                                                 \
+#define AJVP_F32_KERNEL(D)                                                                     \
+  __global__ __launch_bounds__(kThreads, 1) void attn_jvp_f32_d##D(                             \
+      const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,    \
+      const float* __restrict__ tq, const float* __restrict__ tk, const float* __restrict__ tv, \
+      float* __restrict__ o, float* __restrict__ to, float* __restrict__ lse, int Nq, int Nk,   \
+      int ntiles, ExtentsF ext, float scale, float c_log2) {                                    \
+    attn_jvp_f32_body<D>(q, k, v, tq, tk, tv, o, to, lse, Nq, Nk, ntiles, ext, scale, c_log2);  \
   }
 AJVP_F32_KERNEL(64)
 AJVP_F32_KERNEL(128)
@@ -260,9 +273,15 @@ hipError_t launch_f32_d(const float* q, const float* k, const float* v, const fl
                         int H, int Nq, int Nk, float scale, hipStream_t stream) {
   const int ntiles = (Nk + kBC - 1) / kBC;
   const int nqt = (Nq + kBR - 1) / kBR;
-  const int total = B * H * nqt;
-  hipLaunchKernelGGL((D == 128 ? attn_jvp_f32_d128 : attn_jvp_f32_d64), dim3(total), dim3(kThreads), 0, stream, q, k, v, tq,
-                     tk, tv, o, to, lse, Nq, Nk, nqt, ntiles, total, scale, scale * kLog2e);
+  const int bh = B * H;
+  ExtentsF ext;
+  ext.q_bytes = (uint32_t)((size_t)bh * Nq * D * 4);
+  ext.k_bytes = (uint32_t)((size_t)bh * Nk * D * 4);
+  ext.o_bytes = ext.q_bytes;
+  ext.lse_bytes = (uint32_t)((size_t)bh * Nq * 4);
+  hipLaunchKernelGGL((D == 128 ? attn_jvp_f32_d128 : attn_jvp_f32_d64), dim3(nqt, bh),
+                     dim3(kThreads), 0, stream, q, k, v, tq, tk, tv, o, to, lse, Nq, Nk, ntiles,
+                     ext, scale, scale * kLog2e);
   return hipGetLastError();
 }
 

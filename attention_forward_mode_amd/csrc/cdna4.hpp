@@ -18,15 +18,24 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Buffer resource over [base, base + bytes): loads at or past `bytes` return 0,
-// which zero-fills ragged tails without branches.  Word 3 is the gfx9 raw
-// buffer format (32-bit data, no swizzle, no stride).
+// Buffer resource over [base, base + bytes): loads at or past `bytes` return 0
+// and stores there are dropped, so no index can reach memory outside the
+// tensor the descriptor names.  Word 3 is the gfx9 raw buffer format (32-bit
+// data, no swizzle, no stride).
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+// Stores at or past the descriptor's size are dropped by the hardware.
+__device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, 0);
+}
+__device__ inline void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)byte_off, 0, 0);
 }
 
 __device__ inline u32x4 lds_load16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -58,14 +67,5 @@ __device__ inline u32x4 pack_f16x8(float a0, float a1, float a2, float a3,
 __device__ inline float swap_halves(float x) { return __shfl_xor(x, 32); }
 
 __device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
-
-// Pin a wave-uniform value to a scalar register.  Values computed on the vector
-// ALU (integer division, for one) would otherwise stay in VGPRs, and buffer
-// descriptors built from them would need per-lane waterfall loops.
-__device__ inline int to_sgpr(int x) {
-  int r;
-  asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(r) : "v"(x));
-  return r;
-}
 
 }  // namespace ajvp

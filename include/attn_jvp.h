@@ -20,8 +20,9 @@
  * Layout.  Every tensor is dense, row-major and contiguous:
  *   q, tq, o, to : [B, H, Nq, d]      k, v, tk, tv : [B, H, Nk, d]
  *   lse          : [B, H, Nq]
- * A tangent has exactly its primal's shape, dtype and layout.  Offsets are
- * computed in 64-bit.
+ * A tangent has exactly its primal's shape, dtype and layout.  The kernels
+ * address every tensor through buffer descriptors that span exactly that
+ * tensor, so an access outside it reads zero or is dropped.
  *
  * Precision.  attn_jvp_fwd takes bf16 inputs (uint16 storage holding IEEE
  * bfloat16 bit patterns); all products are formed on bf16/fp16 matrix cores
@@ -44,10 +45,10 @@
  * Errors.  Argument errors are detected before anything is launched and leave
  * every output untouched:
  *   ATTN_JVP_EINVAL       a required pointer is NULL; B, H, Nq or Nk < 1;
- *                         `scale` is negative, NaN or infinite; a size product
- *                         overflows; the workspace is NULL or too small
- *   ATTN_JVP_EUNSUPPORTED d is not 64 or 128, or one (b, h) slice of K/V
- *                         exceeds 2^31 bytes
+ *                         `scale` is negative, NaN or infinite; the workspace
+ *                         is NULL or too small
+ *   ATTN_JVP_EUNSUPPORTED d is not 64 or 128, B*H exceeds 65535, or a tensor
+ *                         (or the bf16 path's workspace) reaches 2^31 bytes
  *   ATTN_JVP_EALIGN       a tensor pointer is not 16-byte aligned (workspace:
  *                         256-byte aligned)
  *   ATTN_JVP_ELAUNCH      the HIP runtime rejected a launch or an allocation

@@ -109,10 +109,18 @@ def test_unsupported_head_dim(fn):
 
 @pytest.mark.parametrize("fn", FNS)
 def test_oversized_slice(fn):
-    # one (b, h) slice of K past 2^31 bytes
+    # K (one slice) past 2^31 bytes: outside what 32-bit buffer offsets reach
     assert _call(fn, Nk=1 << 24) == EUNSUPPORTED
-    # grid overflow: B*H*ceil(Nq/128) beyond int range
-    assert _call(fn, B=1 << 16, H=1 << 16, Nq=256) == EINVAL
+    # Q and O past 2^31 bytes over many slices of modest size
+    assert _call(fn, B=64, H=64, Nq=4096) == EUNSUPPORTED
+    # more (b, h) slices than the grid's y extent holds
+    assert _call(fn, B=256, H=256, Nq=1, Nk=1) == EUNSUPPORTED
+    assert _call(fn, B=1 << 16, H=1 << 16, Nq=256) == EUNSUPPORTED
+    # the largest slice count passes the size checks (and then stops at the
+    # misaligned pointer, so nothing is launched)
+    p = [A + j * 0x100000 for j in range(9)]
+    p[0] += 4
+    assert _call(fn, p, B=65535, H=1, Nq=1, Nk=1) == EALIGN
 
 
 @pytest.mark.parametrize("fn", FNS)
