@@ -21,18 +21,13 @@ constexpr int64_t kMaxSlices = 65535;
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
-// Shared checks of sizes, scale and pointers; esize is the input element size.
-int validate(const void* const* in, float* o, float* to, float* lse, int B, int H, int Nq, int Nk,
-             int d, float scale, int esize) {
-  for (int i = 0; i < 6; ++i)
-    if (in[i] == nullptr) return ATTN_JVP_EINVAL;
-  if (o == nullptr || to == nullptr) return ATTN_JVP_EINVAL;
+// Sizes shared by every entry point: counts >= 1, d in {64, 128}, and every
+// tensor (including the bf16 path's padded fp16 V/dV workspace, 2*Nk_pad*d*2
+// bytes per slice) under 2^31 bytes.  Grid: (ceil(Nq/128), B*H) workgroups;
+// pack: (ceil(Nk/64), B*H).  esize is the input element size.
+int check_sizes(int B, int H, int Nq, int Nk, int d, int esize) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_JVP_EINVAL;
-  if (!(scale >= 0.0f) || std::isinf(scale)) return ATTN_JVP_EINVAL;
   if (d != 64 && d != 128) return ATTN_JVP_EUNSUPPORTED;
-  // Grid: (ceil(Nq/128), B*H) workgroups; pack: (ceil(Nk/64), B*H).  Every
-  // tensor, including the padded fp16 V/dV workspace (2*Nk_pad*d*2 bytes per
-  // slice), must stay under 2^31 bytes.
   const int64_t bh = int64_t(B) * H;
   const int64_t kpad = (int64_t(Nk) + 63) / 64 * 64;
   if (bh > kMaxSlices) return ATTN_JVP_EUNSUPPORTED;
@@ -41,10 +36,32 @@ int validate(const void* const* in, float* o, float* to, float* lse, int B, int 
   if (qb >= kMaxTensorBytes || kb >= kMaxTensorBytes || ob >= kMaxTensorBytes ||
       wsb >= kMaxTensorBytes)
     return ATTN_JVP_EUNSUPPORTED;
-  for (int i = 0; i < 6; ++i)
+  return ATTN_JVP_OK;
+}
+
+bool bad_scale(float scale) { return !(scale >= 0.0f) || std::isinf(scale); }
+
+// Checks of the forward entry points: null pointers, sizes, scale, then
+// alignment (16 bytes for tensors, 4 for lse).  `in` holds n input pointers.
+int validate(const void* const* in, int n, float* o, float* to, float* lse, int B, int H,
+             int Nq, int Nk, int d, float scale, int esize) {
+  for (int i = 0; i < n; ++i)
+    if (in[i] == nullptr) return ATTN_JVP_EINVAL;
+  if (o == nullptr || to == nullptr) return ATTN_JVP_EINVAL;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || bad_scale(scale)) return ATTN_JVP_EINVAL;
+  const int rc = check_sizes(B, H, Nq, Nk, d, esize);
+  if (rc != ATTN_JVP_OK) return rc;
+  for (int i = 0; i < n; ++i)
     if (misaligned(in[i], 16)) return ATTN_JVP_EALIGN;
   if (misaligned(o, 16) || misaligned(to, 16) || (lse != nullptr && misaligned(lse, 4)))
     return ATTN_JVP_EALIGN;
+  return ATTN_JVP_OK;
+}
+
+// Workspace of the bf16 path: present, large enough, 256-byte aligned.
+int check_workspace(const void* ws, size_t bytes, int B, int H, int Nk, int d) {
+  if (ws == nullptr || bytes < ajvp::bf16_workspace_bytes(B, H, Nk, d)) return ATTN_JVP_EINVAL;
+  if (misaligned(ws, 256)) return ATTN_JVP_EALIGN;
   return ATTN_JVP_OK;
 }
 
@@ -101,13 +118,39 @@ int attn_jvp_fwd_ws(const void* q, const void* k, const void* v, const void* tq,
                     int d, float scale, void* workspace, size_t workspace_bytes,
                     attn_jvp_stream_t stream) {
   const void* in[6] = {q, k, v, tq, tk, tv};
-  int rc = validate(in, o, to, lse, B, H, Nq, Nk, d, scale, 2);
+  int rc = validate(in, 6, o, to, lse, B, H, Nq, Nk, d, scale, 2);
   if (rc != ATTN_JVP_OK) return rc;
-  if (workspace == nullptr || workspace_bytes < ajvp::bf16_workspace_bytes(B, H, Nk, d))
-    return ATTN_JVP_EINVAL;
-  if (misaligned(workspace, 256)) return ATTN_JVP_EALIGN;
+  rc = check_workspace(workspace, workspace_bytes, B, H, Nk, d);
+  if (rc != ATTN_JVP_OK) return rc;
   hipError_t e = ajvp::launch_bf16(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, d, scale,
                                    workspace, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+}
+
+int attn_jvp_pack_v(const void* v, const void* tv, int B, int H, int Nk, int d, void* workspace,
+                    size_t workspace_bytes, attn_jvp_stream_t stream) {
+  if (v == nullptr || tv == nullptr) return ATTN_JVP_EINVAL;
+  int rc = check_sizes(B, H, 1, Nk, d, 2);
+  if (rc != ATTN_JVP_OK) return rc;
+  rc = check_workspace(workspace, workspace_bytes, B, H, Nk, d);
+  if (rc != ATTN_JVP_OK) return rc;
+  if (misaligned(v, 16) || misaligned(tv, 16)) return ATTN_JVP_EALIGN;
+  hipError_t e = ajvp::launch_pack_v(v, tv, B, H, Nk, d, workspace,
+                                     reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+}
+
+int attn_jvp_fwd_packed(const void* q, const void* k, const void* tq, const void* tk,
+                        const void* workspace, size_t workspace_bytes, float* o, float* to,
+                        float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                        attn_jvp_stream_t stream) {
+  const void* in[4] = {q, k, tq, tk};
+  int rc = validate(in, 4, o, to, lse, B, H, Nq, Nk, d, scale, 2);
+  if (rc != ATTN_JVP_OK) return rc;
+  rc = check_workspace(workspace, workspace_bytes, B, H, Nk, d);
+  if (rc != ATTN_JVP_OK) return rc;
+  hipError_t e = ajvp::launch_bf16_packed(q, k, tq, tk, workspace, o, to, lse, B, H, Nq, Nk, d,
+                                          scale, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
 }
 
@@ -115,7 +158,7 @@ int attn_jvp_fwd(const void* q, const void* k, const void* v, const void* tq, co
                  const void* tv, float* o, float* to, float* lse, int B, int H, int Nq, int Nk,
                  int d, float scale, attn_jvp_stream_t stream) {
   const void* in[6] = {q, k, v, tq, tk, tv};
-  int rc = validate(in, o, to, lse, B, H, Nq, Nk, d, scale, 2);
+  int rc = validate(in, 6, o, to, lse, B, H, Nq, Nk, d, scale, 2);
   if (rc != ATTN_JVP_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipMemPool_t pool = nullptr;
@@ -132,7 +175,7 @@ int attn_jvp_fwd_f32(const float* q, const float* k, const float* v, const float
                      const float* tk, const float* tv, float* o, float* to, float* lse, int B,
                      int H, int Nq, int Nk, int d, float scale, attn_jvp_stream_t stream) {
   const void* in[6] = {q, k, v, tq, tk, tv};
-  int rc = validate(in, o, to, lse, B, H, Nq, Nk, d, scale, 4);
+  int rc = validate(in, 6, o, to, lse, B, H, Nq, Nk, d, scale, 4);
   if (rc != ATTN_JVP_OK) return rc;
   hipError_t e = ajvp::launch_f32(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, d, scale,
                                   reinterpret_cast<hipStream_t>(stream));

@@ -380,9 +380,22 @@ struct Kernels<128> {
 };
 
 template <int D>
-hipError_t launch_bf16_d(const void* q, const void* k, const void* v, const void* tq,
-                         const void* tk, const void* tv, float* o, float* to, float* lse, int B,
-                         int H, int Nq, int Nk, float scale, void* ws, hipStream_t stream) {
+hipError_t launch_pack_d(const void* v, const void* tv, int B, int H, int Nk, void* ws,
+                         hipStream_t stream) {
+  const int ntiles = (Nk + kBC - 1) / kBC;
+  const int bh = B * H;
+  const uint32_t v_bytes = (uint32_t)((size_t)bh * Nk * D * 2);
+  const uint32_t ws_bytes = (uint32_t)bf16_workspace_bytes(B, H, Nk, D);
+  hipLaunchKernelGGL(Kernels<D>::pack, dim3(ntiles, bh), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(tv),
+                     static_cast<char*>(ws), Nk, ntiles, v_bytes, ws_bytes);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_main_d(const void* q, const void* k, const void* tq, const void* tk,
+                         const void* ws, float* o, float* to, float* lse, int B, int H, int Nq,
+                         int Nk, float scale, hipStream_t stream) {
   const int ntiles = (Nk + kBC - 1) / kBC;
   const int nqt = (Nq + kBR - 1) / kBR;
   const int bh = B * H;
@@ -392,11 +405,6 @@ hipError_t launch_bf16_d(const void* q, const void* k, const void* v, const void
   ext.ws_bytes = (uint32_t)bf16_workspace_bytes(B, H, Nk, D);
   ext.o_bytes = (uint32_t)((size_t)bh * Nq * D * 4);
   ext.lse_bytes = (uint32_t)((size_t)bh * Nq * 4);
-  hipLaunchKernelGGL(Kernels<D>::pack, dim3(ntiles, bh), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(tv),
-                     static_cast<char*>(ws), Nk, ntiles, ext.k_bytes, ext.ws_bytes);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(Kernels<D>::main, dim3(nqt, bh), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(tq), static_cast<const uint16_t*>(tk),
@@ -413,12 +421,25 @@ size_t bf16_workspace_bytes(int B, int H, int Nk, int d) {
   return (size_t)B * H * ntiles * 2 * kBC * (size_t)d * 2;
 }
 
+hipError_t launch_pack_v(const void* v, const void* tv, int B, int H, int Nk, int d, void* ws,
+                         hipStream_t stream) {
+  return d == 128 ? launch_pack_d<128>(v, tv, B, H, Nk, ws, stream)
+                  : launch_pack_d<64>(v, tv, B, H, Nk, ws, stream);
+}
+
+hipError_t launch_bf16_packed(const void* q, const void* k, const void* tq, const void* tk,
+                              const void* ws, float* o, float* to, float* lse, int B, int H,
+                              int Nq, int Nk, int d, float scale, hipStream_t stream) {
+  return d == 128 ? launch_main_d<128>(q, k, tq, tk, ws, o, to, lse, B, H, Nq, Nk, scale, stream)
+                  : launch_main_d<64>(q, k, tq, tk, ws, o, to, lse, B, H, Nq, Nk, scale, stream);
+}
+
 hipError_t launch_bf16(const void* q, const void* k, const void* v, const void* tq,
                        const void* tk, const void* tv, float* o, float* to, float* lse, int B,
                        int H, int Nq, int Nk, int d, float scale, void* ws, hipStream_t stream) {
-  if (d == 128)
-    return launch_bf16_d<128>(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, scale, ws, stream);
-  return launch_bf16_d<64>(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, scale, ws, stream);
+  const hipError_t e = launch_pack_v(v, tv, B, H, Nk, d, ws, stream);
+  if (e != hipSuccess) return e;
+  return launch_bf16_packed(q, k, tq, tk, ws, o, to, lse, B, H, Nq, Nk, d, scale, stream);
 }
 
 }  // namespace ajvp

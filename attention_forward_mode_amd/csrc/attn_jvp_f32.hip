@@ -58,40 +58,56 @@ __device__ __attribute__((always_inline)) inline void jvp_tile_f32(
   const char* sdV = stage + 3 * G::kTileBytes;
 
   // S^T, dS^T: contraction slot (j, e, half g) <-> d = 8j + 4g + e.
-  f32x16 s = f32x16{}, ds = f32x16{};
+  // S is accumulated in fp32 over chunks of 32 d-values and the chunk sums are
+  // added in fp64: a logit rounded to fp32 carries an absolute error of
+  // 2^-24 |S|, which for large logits (outlier rows) moves p by more than the
+  // fp32 path's error budget.  The exponent argument is formed from the fp64
+  // sum.  dS stays a single fp32 chain (its rounding enters dO only linearly).
+  constexpr int kChunkJ = 4;  // 4 x 8 = 32 d-values per fp32 chunk
+  double s64[16];
 #pragma unroll
-  for (int j = 0; j < G::kQ4; ++j) {
-    const int off = swz<D>(l32, 2 * j + g);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(sK + off);
-    const f32x4 da = *reinterpret_cast<const f32x4*>(sdK + off);
+  for (int r = 0; r < 16; ++r) s64[r] = 0.0;
+  f32x16 ds = f32x16{};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s = mma_f32(a[e], qf[j][e], s);
-      ds = mma_f32(a[e], dqf[j][e], ds);
-      ds = mma_f32(da[e], qf[j][e], ds);
+  for (int j0 = 0; j0 < G::kQ4; j0 += kChunkJ) {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int j = j0; j < j0 + kChunkJ; ++j) {
+      const int off = swz<D>(l32, 2 * j + g);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(sK + off);
+      const f32x4 da = *reinterpret_cast<const f32x4*>(sdK + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s = mma_f32(a[e], qf[j][e], s);
+        ds = mma_f32(a[e], dqf[j][e], ds);
+        ds = mma_f32(da[e], qf[j][e], ds);
+      }
     }
-    if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s64[r] += (double)s[r];
+    __builtin_amdgcn_sched_barrier(0);
   }
   auto masked = [&](int r) { return kMask && key0 + 8 * (r >> 2) + 4 * g + (r & 3) >= Nk; };
   if constexpr (kMask) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (masked(r)) s[r] = -INFINITY;
+      if (masked(r)) s64[r] = -INFINITY;
   }
 
-  float mx = s[0];
+  float mx = (float)s64[0];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, (float)s64[r]);
   mx = fmaxf(mx, swap_halves(mx));
   const float mt = mx * c_log2;
   const float m_new = (mt > st.m + kTau) ? mt : st.m;
   const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   st.m = m_new;
 
+  const double c64 = (double)scale * 1.4426950408889634;
   float p[16], pd[16], lsum = 0.f, usum = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -m_new));
+    p[r] = __builtin_amdgcn_exp2f((float)__builtin_fma(s64[r], c64, -(double)m_new));
     if (masked(r)) p[r] = 0.f;
     lsum += p[r];
     const float t = p[r] * ds[r];

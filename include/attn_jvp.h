@@ -121,6 +121,34 @@ ATTN_JVP_API int attn_jvp_fwd_ws(const void *q, const void *k, const void *v,
                     attn_jvp_stream_t stream);
 
 /*
+ * The two phases of attn_jvp_fwd_ws, for callers that schedule, time or reuse
+ * them separately (one packed V/dV serves every call with the same V, dV, B,
+ * H, Nk and d, e.g. several query batches against one set of keys).
+ *
+ * attn_jvp_pack_v converts v and tv (bf16, [B, H, Nk, d]) to the fp16 tile
+ * layout of the second contraction and writes it to `workspace` (256-byte
+ * aligned, at least attn_jvp_workspace_bytes(B, H, Nk, d) bytes), overwriting
+ * all of it.  Errors as above (EINVAL for NULL v, tv or workspace, or a short
+ * workspace).
+ *
+ * attn_jvp_fwd_packed computes O, dO and lse from q, k, tq, tk and a workspace
+ * that attn_jvp_pack_v filled for the same B, H, Nk, d, ordered before this
+ * call (same stream, or synchronised).  The workspace is only read.  Other
+ * arguments and errors as attn_jvp_fwd.  Allocates nothing.
+ */
+ATTN_JVP_API int attn_jvp_pack_v(const void *v, const void *tv,
+                    int B, int H, int Nk, int d,
+                    void *workspace, size_t workspace_bytes,
+                    attn_jvp_stream_t stream);
+
+ATTN_JVP_API int attn_jvp_fwd_packed(const void *q, const void *k,
+                        const void *tq, const void *tk,
+                        const void *workspace, size_t workspace_bytes,
+                        float *o, float *to, float *lse,
+                        int B, int H, int Nq, int Nk, int d, float scale,
+                        attn_jvp_stream_t stream);
+
+/*
  * The same operation with fp32 inputs and fp32 arithmetic throughout (the
  * precision reference path).  Same layouts, arguments and errors; needs no
  * workspace and allocates nothing.

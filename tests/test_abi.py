@@ -138,3 +138,50 @@ def test_workspace_checks():
     assert _call("attn_jvp_fwd_ws", ws=0) == EINVAL
     assert _call("attn_jvp_fwd_ws", ws_bytes=100) == EINVAL
     assert _call("attn_jvp_fwd_ws", ws=A + 0x1000000 + 16) == EALIGN
+
+
+def _pack(v=A, tv=A + 0x100000, B=1, H=1, Nk=4, d=128, ws=A + 0x1000000, ws_bytes=None):
+    nb = ajvp.attn_jvp_workspace_bytes(max(B, 1), max(H, 1), max(Nk, 1), d)
+    return ajvp.lib().attn_jvp_pack_v(
+        ctypes.c_void_p(v), ctypes.c_void_p(tv), B, H, Nk, d, ctypes.c_void_p(ws),
+        ctypes.c_size_t(nb if ws_bytes is None else ws_bytes), ctypes.c_void_p(0))
+
+
+def _packed(ptrs=None, B=1, H=1, Nq=4, Nk=4, d=128, scale=0.1, ws=A + 0x1000000,
+            ws_bytes=None):
+    p = [A + i * 0x100000 for i in range(7)] if ptrs is None else ptrs  # q k tq tk o to lse
+    nb = ajvp.attn_jvp_workspace_bytes(max(B, 1), max(H, 1), max(Nk, 1), d)
+    return ajvp.lib().attn_jvp_fwd_packed(
+        *[ctypes.c_void_p(x) for x in p[:4]], ctypes.c_void_p(ws),
+        ctypes.c_size_t(nb if ws_bytes is None else ws_bytes),
+        *[ctypes.c_void_p(x) for x in p[4:]], B, H, Nq, Nk, d, ctypes.c_float(scale),
+        ctypes.c_void_p(0))
+
+
+def test_pack_v_rejects_bad_arguments():
+    assert _pack(v=0) == EINVAL and _pack(tv=0) == EINVAL and _pack(ws=0) == EINVAL
+    assert _pack(ws_bytes=100) == EINVAL
+    assert _pack(B=0) == EINVAL and _pack(Nk=0) == EINVAL
+    assert _pack(d=96) == EUNSUPPORTED and _pack(Nk=1 << 24) == EUNSUPPORTED
+    assert _pack(B=1 << 16) == EUNSUPPORTED
+    assert _pack(v=A + 4) == EALIGN and _pack(tv=A + 8) == EALIGN
+    assert _pack(ws=A + 0x1000000 + 16) == EALIGN
+
+
+def test_fwd_packed_rejects_bad_arguments():
+    for i in range(6):  # q k tq tk o to (lse may be NULL)
+        p = [A + j * 0x100000 for j in range(7)]
+        p[i] = 0
+        assert _packed(p) == EINVAL, i
+    assert _packed(ws=0) == EINVAL and _packed(ws_bytes=100) == EINVAL
+    assert _packed(scale=-1.0) == EINVAL and _packed(scale=float("nan")) == EINVAL
+    assert _packed(Nq=0) == EINVAL
+    assert _packed(d=64 + 1) == EUNSUPPORTED and _packed(Nk=1 << 24) == EUNSUPPORTED
+    for i in range(6):
+        p = [A + j * 0x100000 for j in range(7)]
+        p[i] += 4
+        assert _packed(p) == EALIGN, i
+    p = [A + j * 0x100000 for j in range(7)]
+    p[6] += 2
+    assert _packed(p) == EALIGN
+    assert _packed(ws=A + 0x1000000 + 64) == EALIGN

@@ -49,12 +49,23 @@ def test_batches_and_heads_are_independent(dtype):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
 def test_single_key(dtype):
-    """Nk = 1: O = v0, dO = dv0, lse = s q.k0."""
+    """Nk = 1 closed form: P = 1, so O = v0, dO = dv0 (mu equals s dS) and lse = s q.k0.
+
+    The bf16 path rounds s*P*dS to fp16 before the second contraction, so dO
+    differs from dv0 by (fp16(s dS) - s dS) v0: at most 2^-11 |s dS| |v0|.
+    """
+    s = 0.2
     x = _rand(1, 2, 77, 1, 128, dtype, seed=5)
-    o, to, lse = _cmp(f"{dtype} Nk=1", x, 0.2)
-    v0 = x["v"].float()[:, :, :1].expand(-1, -1, 77, -1)
-    dv0 = x["dv"].float()[:, :, :1].expand(-1, -1, 77, -1)
-    assert torch.equal(o.cpu(), v0) and torch.equal(to.cpu(), dv0)
+    o, to, lse = _cmp(f"{dtype} Nk=1", x, s)
+    q, k, v, dq, dk, dv = (x[n].double() for n in ("q", "k", "v", "dq", "dk", "dv"))
+    v0, dv0 = v[:, :, :1].expand(-1, -1, 77, -1), dv[:, :, :1].expand(-1, -1, 77, -1)
+    sds = (s * ((dq * k[:, :, :1]).sum(-1) + (q * dk[:, :, :1]).sum(-1))).abs()[..., None]
+    u = 1.01 * 2.0 ** -11 if dtype == torch.bfloat16 else 1e-6
+    o, to, lse = (t.double().cpu() for t in (o, to, lse))
+    assert ((o - v0).abs() <= 1e-6 * v0.abs() + 1e-7).all()
+    assert ((to - dv0).abs() <= u * sds * v0.abs() + 1e-6 * (v0.abs() + dv0.abs()) + 1e-7).all()
+    lse_ref = s * (q * k[:, :, :1]).sum(-1)
+    assert ((lse - lse_ref).abs() <= 1e-6 * (1 + lse_ref.abs())).all()
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])

@@ -102,3 +102,24 @@ def test_python_binding_validation():
         ajvp.attn_jvp_fwd(g["q"], g["k"][:, :, :10], *[g[n] for n in NAMES[2:]])
     with pytest.raises(ValueError):
         ajvp.attn_jvp_fwd(g["q"].transpose(2, 3), *[g[n] for n in NAMES[1:]])
+    # a host workspace never reaches the kernels
+    with pytest.raises(ValueError):
+        ajvp.attn_jvp_fwd(*[g[n] for n in NAMES], workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        ajvp.attn_jvp_pack_v(g["v"], g["dv"], workspace=torch.empty(1 << 20, dtype=torch.uint8))
+
+
+def test_two_phases_match_fused_and_packed_workspace_is_reusable():
+    """attn_jvp_pack_v + attn_jvp_fwd_packed == attn_jvp_fwd bit for bit; one
+    packed V/dV serves two query batches of different lengths."""
+    g, s = _inputs()
+    ref = ajvp.attn_jvp_fwd(*[g[n] for n in NAMES], scale=s)
+    ws = ajvp.attn_jvp_pack_v(g["v"], g["dv"])
+    got = ajvp.attn_jvp_fwd_packed(g["q"], g["k"], g["dq"], g["dk"], ws, scale=s)
+    q2, dq2 = g["q"][:, :, :97].contiguous(), g["dq"][:, :, :97].contiguous()
+    got2 = ajvp.attn_jvp_fwd_packed(q2, g["k"], dq2, g["dk"], ws, scale=s)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    for a, b in zip(ref, got2):
+        assert torch.equal(a[:, :, :97], b)
