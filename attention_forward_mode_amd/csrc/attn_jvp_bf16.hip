@@ -8,7 +8,7 @@
 //
 // Two kernels per call:
 //  1. pack_v: V and dV -> fp16, transposed to [d][64 keys] tiles in matrix-core
-//     operand order (XOR-swizzled 16-byte chunks), zero-padded past Nk.  HBM
+//     operand order, zero-padded past Nk.  HBM
 //     bound, ~1% of the fused kernel's time at N = 32760.  fp16 instead of bf16
 //     for the second contraction keeps P and P*dS at 11 significant bits.
 //  2. attn_jvp_bf16: one workgroup = 4 waves x 32 query rows of one (b, h).
@@ -40,8 +40,16 @@ constexpr float kTau = 4.0f;        // lazy-rescale headroom, log2 units
 template <int D>
 struct Geo {
   static constexpr int kTileBytes = kBC * D * 2;          // one tile of K (bf16) or V^T (fp16)
-  static constexpr int kStageBytes = 4 * kTileBytes;      // K | dK | V^T | dV^T
   static constexpr int kPackTileBytes = 2 * kTileBytes;   // V^T | dV^T in the workspace
+  // LDS rows are padded by 16 bytes: the 8 rows that one phase of a 16-byte
+  // matrix-operand read touches then start 16 bytes apart modulo the bank
+  // width, so the reads are conflict-free, and every address is a per-lane
+  // base plus a constant.
+  static constexpr int kKRow = D * 2 + 16;                // K, dK: 64 key rows
+  static constexpr int kVRow = kBC * 2 + 16;              // V^T, dV^T: D rows of 64 keys
+  static constexpr int kKTile = kBC * kKRow;
+  static constexpr int kVTile = D * kVRow;
+  static constexpr int kStageBytes = 2 * kKTile + 2 * kVTile;  // K | dK | V^T | dV^T
   static constexpr int kKS = D / 16;                      // contraction steps over d
   static constexpr int kCB = D / 32;                      // 32-column output blocks
 };
@@ -93,8 +101,7 @@ __device__ __attribute__((always_inline)) inline void pack_v_body(const uint16_t
     f16x8 h;
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = sv[t][packed_key(8 * p + e)][col];
-    const int phys = p ^ (col & 7);
-    buf_store16(rws, out + t * G::kTileBytes + col * 128 + phys * 16, __builtin_bit_cast(u32x4, h));
+    buf_store16(rws, out + t * G::kTileBytes + col * 128 + p * 16, __builtin_bit_cast(u32x4, h));
   }
 }
 
@@ -107,50 +114,65 @@ struct RowState {
   float u;                   // this lane's half of sum p * dS_raw
 };
 
-// One 32-key block of a staged tile for one wave: S^T, dS^T, the online
-// softmax update and the second contraction.  `blk` points at the block's first
-// key row of K inside the LDS stage; `key0` is the block's first key.
-template <int D, bool kMask>
-__device__ __attribute__((always_inline)) inline void jvp_block(RowState<D>& st, const char* stage,
-                                                                int kb, const u32x4* qf,
-                                                                const u32x4* dqf, int l32, int g,
-                                                                int key0, int Nk, float c_log2,
-                                                                float scale) {
+// ---- one 32-key block of a staged tile, in four pieces ----
+// The main loop software-pipelines them: the S/dS products of block j+1 (matrix
+// cores) are issued in the same scheduling region as the softmax of block j
+// (vector ALU), so the two units overlap within one wave.
+
+// S^T = K Q^T and dS^T = dK Q^T + K dQ^T for keys 32kb..32kb+31 of the staged
+// tile (rows: key, columns: this wave's 32 queries).
+template <int D>
+__device__ __attribute__((always_inline)) inline void qk_block(const char* stage, int kb,
+                                                               const u32x4* qf, const u32x4* dqf,
+                                                               int l32, int g, f32x16& s,
+                                                               f32x16& ds) {
   using G = Geo<D>;
   const char* sK = stage;
-  const char* sdK = stage + G::kTileBytes;
-  const char* sV = stage + 2 * G::kTileBytes;
-  const char* sdV = stage + 3 * G::kTileBytes;
-  const int sw = l32 & 7;
-
-  // ---- S^T = K Q^T and dS^T = dK Q^T + K dQ^T for 32 keys x 32 queries ----
-  f32x16 s = f32x16{}, ds = f32x16{};
-  const int rowoff = (32 * kb + l32) * D * 2;
+  const char* sdK = stage + G::kKTile;
+  const int rowoff = (32 * kb + l32) * G::kKRow + 16 * g;
+  s = f32x16{};
+  ds = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < G::kKS; ++ks) {
-    const int off = rowoff + (((2 * ks + g) ^ sw) << 4);
+    const int off = rowoff + 32 * ks;
     const u32x4 a = lds_load16(sK + off);
     const u32x4 da = lds_load16(sdK + off);
     s = mma_bf16(a, qf[ks], s);
     ds = mma_bf16(a, dqf[ks], ds);
     ds = mma_bf16(da, qf[ks], ds);
   }
+}
 
-  // Keys past Nk (last tile only) are left out of the max and get p = 0 and
-  // dS = 0, whatever their staged rows hold.
-  auto masked = [&](int r) {
-    return kMask && key0 + 8 * (r >> 2) + 4 * g + (r & 3) >= Nk;
-  };
-  if constexpr (kMask) {
+// Keys at or past Nk (last tile only) leave the max and get p = 0, dS = 0,
+// whatever their staged rows hold.  Slot r of lane half g holds key
+// key0 + 8(r/4) + 4g + r%4.
+__device__ __attribute__((always_inline)) inline void mask_block(f32x16& s, f32x16& ds, int key0,
+                                                                 int Nk, int g) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (masked(r)) {
-        s[r] = -INFINITY;
-        ds[r] = 0.f;
-      }
-  }
+  for (int r = 0; r < 16; ++r)
+    if (key0 + 8 * (r >> 2) + 4 * g + (r & 3) >= Nk) {
+      s[r] = -INFINITY;
+      ds[r] = 0.f;
+    }
+}
 
-  // ---- online softmax; each lane owns query row l32, lane halves split keys ----
+// Operands of the second contraction for one block: P and s*P*dS in fp16.
+struct PBlock {
+  u32x4 p[2], pd[2];
+};
+
+// Online softmax in the accumulator layout: each lane owns one query row and
+// half of the block's keys (the other half is in lane l ^ 32).  Updates m, l, u
+// and returns the factor alpha by which the accumulators must be rescaled
+// before this block's products are added.  kMask: keys >= Nk (already -inf in
+// s) get p = 0 explicitly, which also covers scale = 0 (-inf * 0 is NaN).
+template <int D, bool kMask>
+__device__ __attribute__((always_inline)) inline float softmax_block(RowState<D>& st,
+                                                                     const f32x16& s,
+                                                                     const f32x16& ds,
+                                                                     float c_log2, float scale,
+                                                                     int key0, int Nk, int g,
+                                                                     PBlock& pb) {
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
@@ -159,46 +181,91 @@ __device__ __attribute__((always_inline)) inline void jvp_block(RowState<D>& st,
   const float m_new = (mt > st.m + kTau) ? mt : st.m;
   const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   st.m = m_new;
-
   float p[16], pd[16], lsum = 0.f, usum = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -m_new));
-    if (masked(r)) p[r] = 0.f;
+    if (kMask && key0 + 8 * (r >> 2) + 4 * g + (r & 3) >= Nk) p[r] = 0.f;
     lsum += p[r];
     const float t = p[r] * ds[r];
     usum += t;
     pd[r] = t * scale;
   }
-  u32x4 pb[2], pdb[2];
-  pb[0] = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-  pb[1] = pack_f16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-  pdb[0] = pack_f16x8(pd[0], pd[1], pd[2], pd[3], pd[4], pd[5], pd[6], pd[7]);
-  pdb[1] = pack_f16x8(pd[8], pd[9], pd[10], pd[11], pd[12], pd[13], pd[14], pd[15]);
+  pb.p[0] = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+  pb.p[1] = pack_f16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+  pb.pd[0] = pack_f16x8(pd[0], pd[1], pd[2], pd[3], pd[4], pd[5], pd[6], pd[7]);
+  pb.pd[1] = pack_f16x8(pd[8], pd[9], pd[10], pd[11], pd[12], pd[13], pd[14], pd[15]);
   st.l = st.l * alpha + lsum;
   st.u = st.u * alpha + usum;
+  return alpha;
+}
+
+// The running max moved (rare with the kTau headroom): rescale A and G.  One
+// 16-register block at a time (scheduling barriers in between), so this rare
+// path needs few temporaries and does not raise the register pressure of the
+// main path.
+template <int D>
+__device__ __attribute__((always_inline)) inline void rescale(RowState<D>& st, float alpha) {
   if (wave_any(alpha != 1.0f)) {
 #pragma unroll
-    for (int cb = 0; cb < G::kCB; ++cb) {
+    for (int cb = 0; cb < Geo<D>::kCB; ++cb) {
       st.accA[cb] *= alpha;
+      __builtin_amdgcn_sched_barrier(0);
       st.accG[cb] *= alpha;
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+}
 
-  // ---- A^T += V^T P^T ; G^T += V^T (s P dS)^T + dV^T P^T ----
+// A^T += V^T P^T ; G^T += V^T (s P dS)^T + dV^T P^T for keys 32kb.. of the tile.
+template <int D>
+__device__ __attribute__((always_inline)) inline void pv_block(RowState<D>& st, const char* stage,
+                                                               int kb, const PBlock& pb, int l32,
+                                                               int g) {
+  using G = Geo<D>;
+  const char* sV = stage + 2 * G::kKTile;
+  const char* sdV = sV + G::kVTile;
 #pragma unroll
   for (int cb = 0; cb < G::kCB; ++cb) {
-    const int vrow = (32 * cb + l32) * 128;
+    const int vrow = (32 * cb + l32) * G::kVRow + 16 * g;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int off = vrow + (((4 * kb + 2 * t + g) ^ sw) << 4);
+      const int off = vrow + 16 * (4 * kb + 2 * t);
       const u32x4 a = lds_load16(sV + off);
       const u32x4 da = lds_load16(sdV + off);
-      st.accA[cb] = mma_f16(a, pb[t], st.accA[cb]);
-      st.accG[cb] = mma_f16(a, pdb[t], st.accG[cb]);
-      st.accG[cb] = mma_f16(da, pb[t], st.accG[cb]);
+      st.accA[cb] = mma_f16(a, pb.p[t], st.accA[cb]);
+      st.accG[cb] = mma_f16(a, pb.pd[t], st.accG[cb]);
+      st.accG[cb] = mma_f16(da, pb.p[t], st.accG[cb]);
     }
   }
+}
+
+// Keeps the softmax outputs of a block in registers at this point, so the
+// compiler does not sink their computation past the rescale branch into the
+// next region.  Emits no instruction.
+__device__ __attribute__((always_inline)) inline void pin(PBlock& pb) {
+  asm volatile("" : "+v"(pb.p[0]), "+v"(pb.p[1]), "+v"(pb.pd[0]), "+v"(pb.pd[1]));
+}
+
+// One pipeline region for block j of the key sequence: S/dS of block j, then
+// the products P V of block j-1 (kPrev; operands `prev` from the previous
+// region), which are independent of block j's softmax, so the scheduler can
+// keep the matrix cores busy with them while the vector ALU runs the softmax.
+// kMask: block j lies in the last tile (keys >= Nk masked).  The accumulators
+// are rescaled by block j's alpha after P V of block j-1 has been added and
+// before that of block j is, as the online update requires.
+template <int D, bool kPrev, bool kMask>
+__device__ __attribute__((always_inline)) inline void region(
+    RowState<D>& st, const char* stage_cur, int kb_cur, const char* stage_prev, int kb_prev,
+    const u32x4* qf, const u32x4* dqf, int l32, int g, const PBlock& prev, PBlock& cur, int Nk,
+    int key0, float c_log2, float scale) {
+  f32x16 s, ds;
+  qk_block<D>(stage_cur, kb_cur, qf, dqf, l32, g, s, ds);
+  if constexpr (kPrev) pv_block<D>(st, stage_prev, kb_prev, prev, l32, g);
+  if constexpr (kMask) mask_block(s, ds, key0, Nk, g);
+  const float alpha = softmax_block<D, kMask>(st, s, ds, c_log2, scale, key0, Nk, g, cur);
+  pin(cur);
+  rescale<D>(st, alpha);
 }
 
 // Sizes of the whole tensors (bytes) the kernel may touch; each global access
@@ -245,45 +312,49 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
     dqf[ks] = buf_load16(rtq, off);
   }
 
-  // Staging through registers: per tile each thread loads kChunks 16-byte
-  // chunks of K|dK and kChunks of the packed V^T|dV^T tile, one tile ahead of
-  // the compute, and writes them to the other LDS buffer at the end of the
-  // iteration.  K and dK chunks are stored under the XOR swizzle.  Key rows
-  // past Nk in the last tile hold whatever the descriptor returns; they are
-  // masked in the compute.
-  constexpr int kChunks = G::kTileBytes * 4 / 16 / kThreads / 2;  // per pair of tensors
+  // Staging through registers, one tensor pair at a time: each thread loads
+  // kChunks 16-byte chunks of K|dK (or of the packed V^T|dV^T tile) into stg
+  // and later writes them to LDS.  Chunk n of thread tid is chunk tid + 256 n
+  // of the tile pair: its row advances by a constant per n, so the per-lane
+  // part of every offset is fixed and the rest is a constant or wave-uniform.
+  // Key rows past Nk in the last tile hold whatever the descriptor returns;
+  // they are masked in the compute.
+  constexpr int kChunks = G::kTileBytes * 2 / 16 / kThreads;  // per pair of tensors
   constexpr int kChunksPerTensor = kChunks / 2;
+  constexpr int kKRowsPerN = kThreads / (D / 8);   // K rows advanced per chunk step
+  constexpr int kVRowsPerN = kThreads / 8;         // V^T rows advanced per chunk step
   const uint32_t kslice = bh * (uint32_t)Nk * D * 2;
   const uint32_t vslice = bh * (uint32_t)ntiles * G::kPackTileBytes;
-  // Chunk c of a tensor's tile is key row c / (D/8), 16-byte column c % (D/8).
-  auto kg_off = [&](int n) {
-    const int c = (tid + kThreads * n) % (kBC * D / 8);
-    return (uint32_t)((c / (D / 8)) * D * 2 + (c % (D / 8)) * 16);
-  };
-  auto kl_off = [&](int n) {
-    const int c = (tid + kThreads * n) % (kBC * D / 8);
-    const int krow = c / (D / 8), ch = c % (D / 8);
-    return (uint32_t)((n / kChunksPerTensor) * G::kTileBytes + krow * D * 2 +
-                      ((ch ^ (krow & 7)) << 4));
-  };
-  u32x4 stg[2 * kChunks];
-  auto load_stage = [&](int kt) {
+  const uint32_t k_lane = (uint32_t)tid * 16;  // global: row tid/(D/8), chunk tid%(D/8)
+  const int k_lds = (tid / (D / 8)) * G::kKRow + (tid % (D / 8)) * 16;
+  const int v_lds = (tid / 8) * G::kVRow + (tid % 8) * 16;
+  u32x4 stg[kChunks];
+  auto load_k = [&](int kt) {
     const uint32_t kbase = kslice + (uint32_t)kt * kBC * D * 2;
 #pragma unroll
     for (int n = 0; n < kChunks; ++n)
-      stg[n] = buf_load16(n < kChunksPerTensor ? rk : rtk, kbase + kg_off(n));
+      stg[n] = buf_load16(n < kChunksPerTensor ? rk : rtk, k_lane,
+                          kbase + (uint32_t)(n % kChunksPerTensor) * kThreads * 16);
+  };
+  auto load_v = [&](int kt) {
     const uint32_t vbase = vslice + (uint32_t)kt * G::kPackTileBytes;
 #pragma unroll
     for (int n = 0; n < kChunks; ++n)
-      stg[kChunks + n] = buf_load16(rv, vbase + (uint32_t)(tid + kThreads * n) * 16);
+      stg[n] = buf_load16(rv, k_lane, vbase + (uint32_t)n * kThreads * 16);
   };
-  auto store_stage = [&](int buf) {
-    char* sb = smem + buf * G::kStageBytes;
-#pragma unroll
-    for (int n = 0; n < kChunks; ++n) lds_store16(sb + kl_off(n), stg[n]);
+  auto store_k = [&](char* sb) {
 #pragma unroll
     for (int n = 0; n < kChunks; ++n)
-      lds_store16(sb + 2 * G::kTileBytes + (tid + kThreads * n) * 16, stg[kChunks + n]);
+      lds_store16(sb + k_lds + (n / kChunksPerTensor) * G::kKTile +
+                      (n % kChunksPerTensor) * kKRowsPerN * G::kKRow,
+                  stg[n]);
+  };
+  // The V^T and dV^T tiles are D rows each, so row r >= D of the pair is row
+  // r - D of dV^T, which starts kVTile bytes after V^T: one formula covers both.
+  auto store_v = [&](char* sb) {
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n)
+      lds_store16(sb + 2 * G::kKTile + v_lds + n * kVRowsPerN * G::kVRow, stg[n]);
   };
 
   RowState<D> st;
@@ -296,28 +367,58 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
   st.l = 0.f;
   st.u = 0.f;
 
-  load_stage(0);
-  store_stage(0);
+  // Software pipeline over 32-key blocks j = 0 .. 2*ntiles-1 (block j is half
+  // j % 2 of tile j / 2): region j forms S/dS and the softmax of block j and
+  // the products P V of block j-1.  K|dK(t) and V|dV(t) live in LDS buffer
+  // t % 2; K(t) is read in regions 2t, 2t+1 and V(t) in regions 2t+1, 2t+2.
+  // Per tile kt, with barrier B_j after region j:
+  //   K|dK(kt+1) -> LDS, V|dV(kt+1) loads issued   (K|dK(kt-1) last read in region 2kt-1)
+  //   region 2kt,   B_2kt
+  //   V|dV(kt+1) -> LDS, K|dK(kt+2) loads issued   (V|dV(kt-1) last read in region 2kt)
+  //   region 2kt+1, B_2kt+1
+  // so K|dK(kt+1) is visible from region 2kt+1 on and V|dV(kt+1) from 2kt+2 on.
+  PBlock pa, pb;  // softmax outputs of the even / odd block
+  const int kLast = ntiles - 1;
+  auto stage = [&](int t) { return smem + (t & 1) * G::kStageBytes; };
+  load_k(0);
+  store_k(smem);
+  load_v(0);
+  store_v(smem);
+  load_k(1);  // past the last tile the descriptors read zeros or unused data
   __syncthreads();
-  for (int kt = 0; kt < ntiles - 1; ++kt) {
-    load_stage(kt + 1);  // in flight during this tile's compute
-    const char* stage = smem + (kt & 1) * G::kStageBytes;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      jvp_block<D, false>(st, stage, kb, qf, dqf, l32, g, kt * kBC + 32 * kb, Nk, c_log2, scale);
-    // The other buffer was last read in iteration kt-1, which every wave has
-    // finished (barrier at its end), so it can be overwritten now.
-    store_stage((kt + 1) & 1);
+  if (ntiles == 1) {
+    region<D, false, true>(st, smem, 0, nullptr, 0, qf, dqf, l32, g, pb, pa, Nk, 0, c_log2, scale);
+    region<D, true, true>(st, smem, 1, smem, 0, qf, dqf, l32, g, pa, pb, Nk, 32, c_log2, scale);
+  } else {
+    // tile 0
+    store_k(stage(1));
+    load_v(1);
+    region<D, false, false>(st, smem, 0, nullptr, 0, qf, dqf, l32, g, pb, pa, Nk, 0, c_log2, scale);
     __syncthreads();
+    store_v(stage(1));
+    load_k(2);
+    region<D, true, false>(st, smem, 1, smem, 0, qf, dqf, l32, g, pa, pb, Nk, 0, c_log2, scale);
+    __syncthreads();
+    // tiles 1 .. ntiles-2
+    for (int kt = 1; kt < kLast; ++kt) {
+      store_k(stage(kt + 1));
+      load_v(kt + 1);
+      region<D, true, false>(st, stage(kt), 0, stage(kt - 1), 1, qf, dqf, l32, g, pb, pa, Nk, 0,
+                             c_log2, scale);
+      __syncthreads();
+      store_v(stage(kt + 1));
+      load_k(kt + 2);
+      region<D, true, false>(st, stage(kt), 1, stage(kt), 0, qf, dqf, l32, g, pa, pb, Nk, 0,
+                             c_log2, scale);
+      __syncthreads();
+    }
+    // last tile: keys past Nk are masked
+    region<D, true, true>(st, stage(kLast), 0, stage(kLast - 1), 1, qf, dqf, l32, g, pb, pa, Nk,
+                          kLast * kBC, c_log2, scale);
+    region<D, true, true>(st, stage(kLast), 1, stage(kLast), 0, qf, dqf, l32, g, pa, pb, Nk,
+                          kLast * kBC + 32, c_log2, scale);
   }
-  {
-    // Last tile, peeled so the loop has one code path: keys past Nk are masked.
-    const int kt = ntiles - 1;
-    const char* stage = smem + (kt & 1) * G::kStageBytes;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      jvp_block<D, true>(st, stage, kb, qf, dqf, l32, g, kt * kBC + 32 * kb, Nk, c_log2, scale);
-  }
+  pv_block<D>(st, stage(kLast), 1, pb, l32, g);
 
   // ---- epilogue: O = A / l, mu = s u / l, dO = G / l - mu O, lse ----
   const float l = st.l + swap_halves(st.l);

@@ -29,6 +29,12 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
+// Same, with the offset split into a per-lane part and a wave-uniform part
+// (kept in a scalar register); the range check applies to their sum.
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t uniform_off) {
+  return __builtin_bit_cast(
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, (int)uniform_off, 0));
+}
 
 // Stores at or past the descriptor's size are dropped by the hardware.
 __device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
