@@ -21,7 +21,7 @@
 //     so row state is per lane), and
 //        A^T += V^T P^T,  G^T += V^T (s P dS)^T + dV^T P^T  (fp16 MFMA)
 //     with P, s*P*dS rounded to fp16.  The epilogue forms O = A / l,
-//     mu = s u / l (u = rowsum P dS), dO = G / l - mu O and lse.
+//     mu = u / l (u = rowsum s P dS), dO = G / l - mu O and lse.
 //  The running max is only raised when a tile's max exceeds it by more than
 //  kTau (log2 units): results are exact either way, p stays <= 2^kTau, and the
 //  accumulator rescale is skipped on most tiles.
@@ -110,162 +110,183 @@ struct RowState {
   f32x16 accA[Geo<D>::kCB];  // A^T = sum p v      (rows: output column, cols: query)
   f32x16 accG[Geo<D>::kCB];  // G^T = sum p (s dS v + dv)
   float m;                   // running max of s*log2e*S (log2 units), per query row
-  float l;                   // this lane's half of sum p
-  float u;                   // this lane's half of sum p * dS_raw
+  float alpha;               // 2^(m_prev - m) of the latest max update
+  float l;                   // this lane's half of sum p         (of the fp16-rounded p)
+  float u;                   // this lane's half of sum s p dS    (of the fp16-rounded values)
 };
 
-// ---- one 32-key block of a staged tile, in four pieces ----
-// The main loop software-pipelines them: the S/dS products of block j+1 (matrix
-// cores) are issued in the same scheduling region as the softmax of block j
-// (vector ALU), so the two units overlap within one wave.
-
-// S^T = K Q^T and dS^T = dK Q^T + K dQ^T for keys 32kb..32kb+31 of the staged
-// tile (rows: key, columns: this wave's 32 queries).
-template <int D>
-__device__ __attribute__((always_inline)) inline void qk_block(const char* stage, int kb,
-                                                               const u32x4* qf, const u32x4* dqf,
-                                                               int l32, int g, f32x16& s,
-                                                               f32x16& ds) {
-  using G = Geo<D>;
-  const char* sK = stage;
-  const char* sdK = stage + G::kKTile;
-  const int rowoff = (32 * kb + l32) * G::kKRow + 16 * g;
-  s = f32x16{};
-  ds = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < G::kKS; ++ks) {
-    const int off = rowoff + 32 * ks;
-    const u32x4 a = lds_load16(sK + off);
-    const u32x4 da = lds_load16(sdK + off);
-    s = mma_bf16(a, qf[ks], s);
-    ds = mma_bf16(a, dqf[ks], ds);
-    ds = mma_bf16(da, qf[ks], ds);
-  }
-}
-
-// Keys at or past Nk (last tile only) leave the max and get p = 0, dS = 0,
-// whatever their staged rows hold.  Slot r of lane half g holds key
-// key0 + 8(r/4) + 4g + r%4.
-__device__ __attribute__((always_inline)) inline void mask_block(f32x16& s, f32x16& ds, int key0,
-                                                                 int Nk, int g) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r)
-    if (key0 + 8 * (r >> 2) + 4 * g + (r & 3) >= Nk) {
-      s[r] = -INFINITY;
-      ds[r] = 0.f;
-    }
-}
+// S^T and dS^T of one 32-key block (rows: key, columns: this wave's queries).
+struct SBlock {
+  f32x16 s, ds;
+};
 
 // Operands of the second contraction for one block: P and s*P*dS in fp16.
 struct PBlock {
   u32x4 p[2], pd[2];
 };
 
-// Online softmax in the accumulator layout: each lane owns one query row and
-// half of the block's keys (the other half is in lane l ^ 32).  Updates m, l, u
-// and returns the factor alpha by which the accumulators must be rescaled
-// before this block's products are added.  kMask: keys >= Nk (already -inf in
-// s) get p = 0 explicitly, which also covers scale = 0 (-inf * 0 is NaN).
-template <int D, bool kMask>
-__device__ __attribute__((always_inline)) inline float softmax_block(RowState<D>& st,
-                                                                     const f32x16& s,
-                                                                     const f32x16& ds,
-                                                                     float c_log2, float scale,
-                                                                     int key0, int Nk, int g,
-                                                                     PBlock& pb) {
-  float mx = s[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = fmaxf(mx, swap_halves(mx));
-  const float mt = mx * c_log2;
-  const float m_new = (mt > st.m + kTau) ? mt : st.m;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-  st.m = m_new;
-  float p[16], pd[16], lsum = 0.f, usum = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -m_new));
-    if (kMask && key0 + 8 * (r >> 2) + 4 * g + (r & 3) >= Nk) p[r] = 0.f;
-    lsum += p[r];
-    const float t = p[r] * ds[r];
-    usum += t;
-    pd[r] = t * scale;
-  }
-  pb.p[0] = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-  pb.p[1] = pack_f16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-  pb.pd[0] = pack_f16x8(pd[0], pd[1], pd[2], pd[3], pd[4], pd[5], pd[6], pd[7]);
-  pb.pd[1] = pack_f16x8(pd[8], pd[9], pd[10], pd[11], pd[12], pd[13], pd[14], pd[15]);
-  st.l = st.l * alpha + lsum;
-  st.u = st.u * alpha + usum;
-  return alpha;
+// Slot r of lane half g holds key 8(r/4) + 4g + r%4 of its 32-key block.
+__device__ __attribute__((always_inline)) inline int slot_key(int r, int g) {
+  return 8 * (r >> 2) + 4 * g + (r & 3);
 }
 
-// The running max moved (rare with the kTau headroom): rescale A and G.  One
-// 16-register block at a time (scheduling barriers in between), so this rare
-// path needs few temporaries and does not raise the register pressure of the
-// main path.
-template <int D>
-__device__ __attribute__((always_inline)) inline void rescale(RowState<D>& st, float alpha) {
-  if (wave_any(alpha != 1.0f)) {
+// ---- the per-block pipeline ----
+// Block j of the key sequence passes through two scheduling regions:
+//   R1(j): S/dS of block j on the matrix cores, while the vector ALU turns
+//          block j-1 into P, s*P*dS (fp16) and its row sums;
+//   R2(j): P V of block j-1 on the matrix cores, while the vector ALU finds
+//          the max of block j's S and the new running max / rescale factor;
+//   then the accumulators are rescaled (rare, see kTau).
+// Both regions are written as slots of one matrix-core instruction plus a
+// share of vector work, separated by scheduling barriers, so the two units
+// run side by side within one wave.  Operand fragments are read from LDS two
+// slots-of-three ahead of their use.
+// Online-softmax order: P V of block j-1 (normalised to m_{j-1}) is added
+// before the rescale by alpha_j = 2^(m_{j-1} - m_j), and P of block j is
+// formed with m_j, so the accumulators always hold sums normalised to the
+// current m.
+
+// R1.  kQK: form S/dS of block `kb` of `stage` into `snew`.  kEW: finish block
+// `sold` (max already applied to st.m): P, s*P*dS -> `pb`, and l, u updated
+// with the rescale factor of that block.  kMask: `sold` lies in the last tile
+// (keys >= Nk get p = 0 and contribute nothing to u).  Each pair of results is
+// rounded to fp16 as soon as it exists, and l, u sum exactly those rounded
+// values (one dot instruction per pair): the weights that the normalisation
+// uses are the ones the matrix cores multiply, so O is an exact convex
+// combination of V's rows and sum_j (p_j dS_j - mu p_j) cancels as it must.
+template <int D, bool kQK, bool kEW, bool kMask>
+__device__ __attribute__((always_inline)) inline void region1(
+    RowState<D>& st, const char* stage, int kb, const u32x4* qf, const u32x4* dqf, int l32,
+    int g, SBlock& snew, const SBlock& sold, int key0_old, int Nk, float c_log2, float scale,
+    PBlock& pb) {
+  using G = Geo<D>;
+  constexpr int kSlots = 3 * G::kKS;
+  constexpr int kPairSlots = kSlots - 1;  // element pairs spread over these slots
+  const char* sK = stage;
+  const char* sdK = stage + G::kKTile;
+  const int rowoff = (32 * kb + l32) * G::kKRow + 16 * g;
+  u32x4 ka[3], kda[3];
+  if constexpr (kQK) {
 #pragma unroll
-    for (int cb = 0; cb < Geo<D>::kCB; ++cb) {
-      st.accA[cb] *= alpha;
-      __builtin_amdgcn_sched_barrier(0);
-      st.accG[cb] *= alpha;
-      __builtin_amdgcn_sched_barrier(0);
+    for (int ks = 0; ks < 2; ++ks) {
+      ka[ks] = lds_load16(sK + rowoff + 32 * ks);
+      kda[ks] = lds_load16(sdK + rowoff + 32 * ks);
     }
   }
+  float lsum = 0.f, usum = 0.f;
+  const float m = st.m;
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) {
+    if constexpr (kQK) {
+      const int ks = i / 3, w = i % 3;
+      if (w == 0 && ks + 2 < G::kKS) {
+        ka[(ks + 2) % 3] = lds_load16(sK + rowoff + 32 * (ks + 2));
+        kda[(ks + 2) % 3] = lds_load16(sdK + rowoff + 32 * (ks + 2));
+      }
+      if (w == 0) snew.s = mma_bf16(ka[ks % 3], qf[ks], ks == 0 ? f32x16{} : snew.s);
+      if (w == 1) snew.ds = mma_bf16(ka[ks % 3], dqf[ks], ks == 0 ? f32x16{} : snew.ds);
+      if (w == 2) snew.ds = mma_bf16(kda[ks % 3], qf[ks], snew.ds);
+    }
+    if constexpr (kEW) {
+#pragma unroll
+      for (int q = i * 8 / kPairSlots; q < (i + 1) * 8 / kPairSlots && q < 8; ++q) {
+        float pp[2], pdd[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * q + e;
+          pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sold.s[r], c_log2, -m));
+          pdd[e] = pp[e] * sold.ds[r] * scale;
+          if (kMask && key0_old + slot_key(r, g) >= Nk) {
+            pp[e] = 0.f;
+            pdd[e] = 0.f;
+          }
+        }
+        const uint32_t hp = pack_f16x2(pp[0], pp[1]);
+        const uint32_t hd = pack_f16x2(pdd[0], pdd[1]);
+        pb.p[q >> 2][q & 3] = hp;
+        pb.pd[q >> 2][q & 3] = hd;
+        lsum = add_f16x2(hp, lsum);
+        usum = add_f16x2(hd, usum);
+      }
+      if (i == kSlots - 1) {
+        st.l = st.l * st.alpha + lsum;
+        st.u = st.u * st.alpha + usum;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
-// A^T += V^T P^T ; G^T += V^T (s P dS)^T + dV^T P^T for keys 32kb.. of the tile.
-template <int D>
-__device__ __attribute__((always_inline)) inline void pv_block(RowState<D>& st, const char* stage,
-                                                               int kb, const PBlock& pb, int l32,
-                                                               int g) {
+// R2.  kPV: A^T += V^T P^T, G^T += V^T (s P dS)^T + dV^T P^T for block `kb` of
+// `stage` with operands `pb`.  kMax: running-max update from block `snew`
+// (kMask: its keys >= Nk are left out), then the rescale.
+template <int D, bool kPV, bool kMax, bool kMask>
+__device__ __attribute__((always_inline)) inline void region2(
+    RowState<D>& st, const char* stage, int kb, const PBlock& pb, int l32, int g,
+    SBlock& snew, int key0_new, int Nk, float c_log2) {
   using G = Geo<D>;
+  constexpr int kSteps = 2 * G::kCB;  // (cb, t) pairs, three products each
+  constexpr int kSlots = 3 * kSteps;
   const char* sV = stage + 2 * G::kKTile;
   const char* sdV = sV + G::kVTile;
+  auto voff = [&](int step) {  // step = 2 cb + t
+    return ((32 * (step >> 1) + l32) * G::kVRow + 16 * g) + 16 * (4 * kb + 2 * (step & 1));
+  };
+  u32x4 va[3], vda[3];
+  if constexpr (kPV) {
 #pragma unroll
-  for (int cb = 0; cb < G::kCB; ++cb) {
-    const int vrow = (32 * cb + l32) * G::kVRow + 16 * g;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int off = vrow + 16 * (4 * kb + 2 * t);
-      const u32x4 a = lds_load16(sV + off);
-      const u32x4 da = lds_load16(sdV + off);
-      st.accA[cb] = mma_f16(a, pb.p[t], st.accA[cb]);
-      st.accG[cb] = mma_f16(a, pb.pd[t], st.accG[cb]);
-      st.accG[cb] = mma_f16(da, pb.p[t], st.accG[cb]);
+    for (int k = 0; k < 2; ++k) {
+      va[k] = lds_load16(sV + voff(k));
+      vda[k] = lds_load16(sdV + voff(k));
     }
   }
-}
-
-// Keeps the softmax outputs of a block in registers at this point, so the
-// compiler does not sink their computation past the rescale branch into the
-// next region.  Emits no instruction.
-__device__ __attribute__((always_inline)) inline void pin(PBlock& pb) {
-  asm volatile("" : "+v"(pb.p[0]), "+v"(pb.p[1]), "+v"(pb.pd[0]), "+v"(pb.pd[1]));
-}
-
-// One pipeline region for block j of the key sequence: S/dS of block j, then
-// the products P V of block j-1 (kPrev; operands `prev` from the previous
-// region), which are independent of block j's softmax, so the scheduler can
-// keep the matrix cores busy with them while the vector ALU runs the softmax.
-// kMask: block j lies in the last tile (keys >= Nk masked).  The accumulators
-// are rescaled by block j's alpha after P V of block j-1 has been added and
-// before that of block j is, as the online update requires.
-template <int D, bool kPrev, bool kMask>
-__device__ __attribute__((always_inline)) inline void region(
-    RowState<D>& st, const char* stage_cur, int kb_cur, const char* stage_prev, int kb_prev,
-    const u32x4* qf, const u32x4* dqf, int l32, int g, const PBlock& prev, PBlock& cur, int Nk,
-    int key0, float c_log2, float scale) {
-  f32x16 s, ds;
-  qk_block<D>(stage_cur, kb_cur, qf, dqf, l32, g, s, ds);
-  if constexpr (kPrev) pv_block<D>(st, stage_prev, kb_prev, prev, l32, g);
-  if constexpr (kMask) mask_block(s, ds, key0, Nk, g);
-  const float alpha = softmax_block<D, kMask>(st, s, ds, c_log2, scale, key0, Nk, g, cur);
-  pin(cur);
-  rescale<D>(st, alpha);
+  if constexpr (kMax && kMask) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (key0_new + slot_key(r, g) >= Nk) snew.s[r] = -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) {
+    if constexpr (kPV) {
+      const int step = i / 3, w = i % 3, cb = step >> 1, t = step & 1;
+      if (w == 0 && step + 2 < kSteps) {
+        va[(step + 2) % 3] = lds_load16(sV + voff(step + 2));
+        vda[(step + 2) % 3] = lds_load16(sdV + voff(step + 2));
+      }
+      if (w == 0) st.accA[cb] = mma_f16(va[step % 3], pb.p[t], st.accA[cb]);
+      if (w == 1) st.accG[cb] = mma_f16(va[step % 3], pb.pd[t], st.accG[cb]);
+      if (w == 2) st.accG[cb] = mma_f16(vda[step % 3], pb.p[t], st.accG[cb]);
+    }
+    if constexpr (kMax) {
+      // two elements per slot over the first eight slots, then the combine.
+      // NaN-propagating maximum: one v_maximum3 per slot, no canonicalisation.
+      if (i < 8)
+        mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, snew.s[2 * i]),
+                                           snew.s[2 * i + 1]);
+      if (i == 8) {
+        mx = halves_max(mx);
+        const float mt = mx * c_log2;
+        const float m_new = (mt > st.m + kTau) ? mt : st.m;
+        st.alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+        st.m = m_new;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (kMax) {
+    if (wave_any(st.alpha != 1.0f)) {
+      // One 16-register block at a time, so this rare path needs few
+      // temporaries and does not raise the main path's register pressure.
+#pragma unroll
+      for (int cb = 0; cb < G::kCB; ++cb) {
+        st.accA[cb] *= st.alpha;
+        __builtin_amdgcn_sched_barrier(0);
+        st.accG[cb] *= st.alpha;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
 }
 
 // Sizes of the whole tensors (bytes) the kernel may touch; each global access
@@ -311,6 +332,11 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
     qf[ks] = buf_load16(rq, off);
     dqf[ks] = buf_load16(rtq, off);
   }
+  // The Q/dQ fragments are only ever matrix-core operands, which may come
+  // from accumulation registers: keep them there and leave the vector
+  // registers to the softmax.  (Empty asm: a register-class constraint only.)
+#pragma unroll
+  for (int ks = 0; ks < G::kKS; ++ks) asm volatile("" : "+a"(qf[ks]), "+a"(dqf[ks]));
 
   // Staging through registers, one tensor pair at a time: each thread loads
   // kChunks 16-byte chunks of K|dK (or of the packed V^T|dV^T tile) into stg
@@ -364,21 +390,24 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
     st.accG[cb] = f32x16{};
   }
   st.m = -INFINITY;
+  st.alpha = 1.f;
   st.l = 0.f;
   st.u = 0.f;
 
-  // Software pipeline over 32-key blocks j = 0 .. 2*ntiles-1 (block j is half
-  // j % 2 of tile j / 2): region j forms S/dS and the softmax of block j and
-  // the products P V of block j-1.  K|dK(t) and V|dV(t) live in LDS buffer
-  // t % 2; K(t) is read in regions 2t, 2t+1 and V(t) in regions 2t+1, 2t+2.
-  // Per tile kt, with barrier B_j after region j:
-  //   K|dK(kt+1) -> LDS, V|dV(kt+1) loads issued   (K|dK(kt-1) last read in region 2kt-1)
-  //   region 2kt,   B_2kt
-  //   V|dV(kt+1) -> LDS, K|dK(kt+2) loads issued   (V|dV(kt-1) last read in region 2kt)
-  //   region 2kt+1, B_2kt+1
-  // so K|dK(kt+1) is visible from region 2kt+1 on and V|dV(kt+1) from 2kt+2 on.
-  PBlock pa, pb;  // softmax outputs of the even / odd block
+  // Blocks j = 0 .. 2*ntiles-1 (block j is half j % 2 of tile j / 2) run
+  // through region1 / region2 (R1(j), R2(j)) as described above.  K|dK(t) and
+  // V|dV(t) live in LDS buffer t % 2; K(t) is read in R1 of blocks 2t, 2t+1
+  // and V(t) in R2 of blocks 2t+1, 2t+2.  Per tile kt, with a barrier after
+  // each block:
+  //   K|dK(kt+1) -> LDS, V|dV(kt+1) loads issued   (K|dK(kt-1) last read in block 2kt-1)
+  //   block 2kt,   barrier
+  //   V|dV(kt+1) -> LDS, K|dK(kt+2) loads issued   (V|dV(kt-1) last read in block 2kt)
+  //   block 2kt+1, barrier
+  // so K|dK(kt+1) is visible from block 2kt+1 on and V|dV(kt+1) from 2kt+2 on.
+  SBlock sa, sb;  // S/dS of the even / odd block
+  PBlock pb;      // P, s*P*dS of the block whose P V is next
   const int kLast = ntiles - 1;
+  const int key_last = kLast * kBC;
   auto stage = [&](int t) { return smem + (t & 1) * G::kStageBytes; };
   load_k(0);
   store_k(smem);
@@ -387,44 +416,56 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
   load_k(1);  // past the last tile the descriptors read zeros or unused data
   __syncthreads();
   if (ntiles == 1) {
-    region<D, false, true>(st, smem, 0, nullptr, 0, qf, dqf, l32, g, pb, pa, Nk, 0, c_log2, scale);
-    region<D, true, true>(st, smem, 1, smem, 0, qf, dqf, l32, g, pa, pb, Nk, 32, c_log2, scale);
+    region1<D, true, false, false>(st, smem, 0, qf, dqf, l32, g, sa, sb, 0, Nk, c_log2, scale, pb);
+    region2<D, false, true, true>(st, smem, 0, pb, l32, g, sa, 0, Nk, c_log2);
+    region1<D, true, true, true>(st, smem, 1, qf, dqf, l32, g, sb, sa, 0, Nk, c_log2, scale, pb);
+    region2<D, true, true, true>(st, smem, 0, pb, l32, g, sb, 32, Nk, c_log2);
+    region1<D, false, true, true>(st, smem, 0, qf, dqf, l32, g, sa, sb, 32, Nk, c_log2, scale, pb);
+    region2<D, true, false, false>(st, smem, 1, pb, l32, g, sb, 0, Nk, c_log2);
   } else {
     // tile 0
     store_k(stage(1));
     load_v(1);
-    region<D, false, false>(st, smem, 0, nullptr, 0, qf, dqf, l32, g, pb, pa, Nk, 0, c_log2, scale);
+    region1<D, true, false, false>(st, smem, 0, qf, dqf, l32, g, sa, sb, 0, Nk, c_log2, scale, pb);
+    region2<D, false, true, false>(st, smem, 0, pb, l32, g, sa, 0, Nk, c_log2);
     __syncthreads();
     store_v(stage(1));
     load_k(2);
-    region<D, true, false>(st, smem, 1, smem, 0, qf, dqf, l32, g, pa, pb, Nk, 0, c_log2, scale);
+    region1<D, true, true, false>(st, smem, 1, qf, dqf, l32, g, sb, sa, 0, Nk, c_log2, scale, pb);
+    region2<D, true, true, false>(st, smem, 0, pb, l32, g, sb, 0, Nk, c_log2);
     __syncthreads();
     // tiles 1 .. ntiles-2
     for (int kt = 1; kt < kLast; ++kt) {
       store_k(stage(kt + 1));
       load_v(kt + 1);
-      region<D, true, false>(st, stage(kt), 0, stage(kt - 1), 1, qf, dqf, l32, g, pb, pa, Nk, 0,
-                             c_log2, scale);
+      region1<D, true, true, false>(st, stage(kt), 0, qf, dqf, l32, g, sa, sb, 0, Nk, c_log2,
+                                    scale, pb);
+      region2<D, true, true, false>(st, stage(kt - 1), 1, pb, l32, g, sa, 0, Nk, c_log2);
       __syncthreads();
       store_v(stage(kt + 1));
       load_k(kt + 2);
-      region<D, true, false>(st, stage(kt), 1, stage(kt), 0, qf, dqf, l32, g, pa, pb, Nk, 0,
-                             c_log2, scale);
+      region1<D, true, true, false>(st, stage(kt), 1, qf, dqf, l32, g, sb, sa, 0, Nk, c_log2,
+                                    scale, pb);
+      region2<D, true, true, false>(st, stage(kt), 0, pb, l32, g, sb, 0, Nk, c_log2);
       __syncthreads();
     }
-    // last tile: keys past Nk are masked
-    region<D, true, true>(st, stage(kLast), 0, stage(kLast - 1), 1, qf, dqf, l32, g, pb, pa, Nk,
-                          kLast * kBC, c_log2, scale);
-    region<D, true, true>(st, stage(kLast), 1, stage(kLast), 0, qf, dqf, l32, g, pa, pb, Nk,
-                          kLast * kBC + 32, c_log2, scale);
+    // last tile: keys past Nk are masked (the tile is complete in LDS already)
+    region1<D, true, true, false>(st, stage(kLast), 0, qf, dqf, l32, g, sa, sb, 0, Nk, c_log2,
+                                  scale, pb);
+    region2<D, true, true, true>(st, stage(kLast - 1), 1, pb, l32, g, sa, key_last, Nk, c_log2);
+    region1<D, true, true, true>(st, stage(kLast), 1, qf, dqf, l32, g, sb, sa, key_last, Nk,
+                                 c_log2, scale, pb);
+    region2<D, true, true, true>(st, stage(kLast), 0, pb, l32, g, sb, key_last + 32, Nk, c_log2);
+    region1<D, false, true, true>(st, stage(kLast), 0, qf, dqf, l32, g, sa, sb, key_last + 32, Nk,
+                                  c_log2, scale, pb);
+    region2<D, true, false, false>(st, stage(kLast), 1, pb, l32, g, sb, 0, Nk, c_log2);
   }
-  pv_block<D>(st, stage(kLast), 1, pb, l32, g);
 
-  // ---- epilogue: O = A / l, mu = s u / l, dO = G / l - mu O, lse ----
-  const float l = st.l + swap_halves(st.l);
-  const float u = st.u + swap_halves(st.u);
+  // ---- epilogue: O = A / l, mu = u / l, dO = G / l - mu O, lse ----
+  const float l = halves_sum(st.l);
+  const float u = halves_sum(st.u);
   const float inv_l = 1.0f / l;
-  const float mu = u * scale * inv_l;
+  const float mu = u * inv_l;
   if (row_ok) {
     const uint32_t orow = (bh * (uint32_t)Nq + row) * D * 4;
 #pragma unroll

@@ -69,8 +69,38 @@ __device__ inline u32x4 pack_f16x8(float a0, float a1, float a2, float a3,
   return __builtin_bit_cast(u32x4, h);
 }
 
+// Two fp32 values to one register of two fp16 (round to nearest even).
+__device__ inline uint32_t pack_f16x2(float a, float b) {
+  f16x2 h;
+  h[0] = (_Float16)a;
+  h[1] = (_Float16)b;
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// acc + h.x + h.y for a register of two fp16 (products with 1.0 are exact;
+// the sum is formed in fp32).
+__device__ inline float add_f16x2(uint32_t h, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), one, acc, false);
+}
+
 // Value held by lane (l ^ 32): the other half of a 64-wide wave.
 __device__ inline float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+// max / sum of x over lanes l and l ^ 32, in every lane.  v_permlane32_swap
+// exchanges the upper half of its first operand with the lower half of its
+// second; with both set to x the two results hold x of the lower and of the
+// upper half respectively, in every lane (a vector-ALU op, no LDS traffic).
+__device__ inline float halves_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ inline float halves_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
 
 __device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
