@@ -6,8 +6,8 @@ device memory and the current stream.  The names mirror the C entry points:
 
     attn_jvp_fwd(q, k, v, tq, tk, tv, scale=None, lse=True) -> (o, to, lse)
         bf16 inputs [B, H, Nq|Nk, d] on the GPU; fp32 outputs
-    attn_jvp_pack_v(v, tv, workspace=None) -> workspace
-    attn_jvp_fwd_packed(q, k, tq, tk, workspace, ...) -> (o, to, lse)
+    attn_jvp_pack_kv(k, v, tk, tv, workspace=None) -> workspace
+    attn_jvp_fwd_packed(q, tq, workspace, Nk, ...) -> (o, to, lse)
         the two phases of attn_jvp_fwd, callable separately
     attn_jvp_fwd_f32(...)  the same with fp32 inputs
     attn_jvp_workspace_bytes(B, H, Nk, d)
@@ -27,7 +27,7 @@ import os
 
 import torch
 
-__all__ = ["attn_jvp_fwd", "attn_jvp_pack_v", "attn_jvp_fwd_packed", "attn_jvp_fwd_f32", "attn_jvp_workspace_bytes",
+__all__ = ["attn_jvp_fwd", "attn_jvp_pack_kv", "attn_jvp_fwd_packed", "attn_jvp_fwd_f32", "attn_jvp_workspace_bytes",
            "attn_jvp_strerror", "AttnJvpError", "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_jvp.so")
@@ -53,9 +53,9 @@ def lib():
     L.attn_jvp_fwd.restype = _i
     L.attn_jvp_fwd_ws.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _vp, _sz, _vp]
     L.attn_jvp_fwd_ws.restype = _i
-    L.attn_jvp_pack_v.argtypes = [_vp, _vp] + [_i] * 4 + [_vp, _sz, _vp]
-    L.attn_jvp_pack_v.restype = _i
-    L.attn_jvp_fwd_packed.argtypes = [_vp] * 5 + [_sz] + [_vp] * 3 + [_i] * 5 + [_f, _vp]
+    L.attn_jvp_pack_kv.argtypes = [_vp] * 4 + [_i] * 4 + [_vp, _sz, _vp]
+    L.attn_jvp_pack_kv.restype = _i
+    L.attn_jvp_fwd_packed.argtypes = [_vp] * 3 + [_sz] + [_vp] * 3 + [_i] * 5 + [_f, _vp]
     L.attn_jvp_fwd_packed.restype = _i
     L.attn_jvp_fwd_f32.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _vp]
     L.attn_jvp_fwd_f32.restype = _i
@@ -144,42 +144,43 @@ def _nbytes(t):
     return t.numel() * t.element_size()
 
 
-def attn_jvp_pack_v(v, tv, workspace=None):
-    """Phase 1 of the bf16 path: pack V and dV ([B, H, Nk, d] bf16) into the
-    fp16 tile layout.  Returns the workspace (a new uint8 tensor unless one is
-    passed).  Launches on the current stream."""
-    for name, t in (("v", v), ("tv", tv)):
+def attn_jvp_pack_kv(k, v, tk, tv, workspace=None):
+    """Phase 1 of the bf16 path: pack K, V, dK, dV ([B, H, Nk, d] bf16) into
+    the tile images the fused kernel copies into LDS.  Returns the workspace (a
+    new uint8 tensor unless one is passed).  Launches on the current stream."""
+    for name, t in (("k", k), ("v", v), ("tk", tk), ("tv", tv)):
         if (not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda
                 or t.dim() != 4 or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous 4-D bf16 GPU tensor")
-    if tv.shape != v.shape or tv.device != v.device:
-        raise ValueError("tv must have v's shape and device")
-    B, H, Nk, d = v.shape
-    workspace = _workspace(workspace, B, H, Nk, d, v.device)
-    stream = ctypes.c_void_p(torch.cuda.current_stream(v.device).cuda_stream)
-    with torch.cuda.device(v.device):
-        rc = lib().attn_jvp_pack_v(_ptr(v), _ptr(tv), B, H, Nk, d, _ptr(workspace),
-                                   _nbytes(workspace), stream)
+    for name, t in (("v", v), ("tk", tk), ("tv", tv)):
+        if t.shape != k.shape or t.device != k.device:
+            raise ValueError(f"{name} must have k's shape and device")
+    B, H, Nk, d = k.shape
+    workspace = _workspace(workspace, B, H, Nk, d, k.device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(k.device).cuda_stream)
+    with torch.cuda.device(k.device):
+        rc = lib().attn_jvp_pack_kv(_ptr(k), _ptr(v), _ptr(tk), _ptr(tv), B, H, Nk, d,
+                                    _ptr(workspace), _nbytes(workspace), stream)
     if rc != OK:
         raise AttnJvpError(rc)
     return workspace
 
 
-def attn_jvp_fwd_packed(q, k, tq, tk, workspace, scale=None, lse=True, out=None):
-    """Phase 2 of the bf16 path: attention + JVP from q, k, tq, tk and a
-    workspace filled by ``attn_jvp_pack_v`` for the same V, dV.  Returns
+def attn_jvp_fwd_packed(q, tq, workspace, Nk, scale=None, lse=True, out=None):
+    """Phase 2 of the bf16 path: attention + JVP from q, tq and a workspace
+    filled by ``attn_jvp_pack_kv`` for Nk keys of the same B, H, d.  Returns
     (o, to, lse) like ``attn_jvp_fwd``."""
-    B, H, Nq, Nk, d = _check(q, k, k, tq, tk, tk, torch.bfloat16)
+    B, H, Nq, _, d = _check(q, q, q, tq, q, q, torch.bfloat16)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if workspace is None:
-        raise ValueError("workspace must come from attn_jvp_pack_v")
+        raise ValueError("workspace must come from attn_jvp_pack_kv")
     workspace = _workspace(workspace, B, H, Nk, d, q.device)
     o, to, lse_t = _outputs(q, B, H, Nq, d, lse, out)
     stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
     with torch.cuda.device(q.device):
-        rc = lib().attn_jvp_fwd_packed(_ptr(q), _ptr(k), _ptr(tq), _ptr(tk), _ptr(workspace),
-                                       _nbytes(workspace), _ptr(o), _ptr(to), _ptr(lse_t), B, H,
-                                       Nq, Nk, d, s, stream)
+        rc = lib().attn_jvp_fwd_packed(_ptr(q), _ptr(tq), _ptr(workspace), _nbytes(workspace),
+                                       _ptr(o), _ptr(to), _ptr(lse_t), B, H, Nq, int(Nk), d, s,
+                                       stream)
     if rc != OK:
         raise AttnJvpError(rc)
     return o, to, lse_t

@@ -21,18 +21,18 @@ constexpr int64_t kMaxSlices = 65535;
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
-// Sizes shared by every entry point: counts >= 1, d in {64, 128}, and every
-// tensor (including the bf16 path's padded fp16 V/dV workspace, 2*Nk_pad*d*2
-// bytes per slice) under 2^31 bytes.  Grid: (ceil(Nq/128), B*H) workgroups;
-// pack: (ceil(Nk/64), B*H).  esize is the input element size.
+// Sizes shared by every entry point: counts >= 1, d in {64, 128}, every
+// tensor under 2^31 bytes, and one (b, h) slice of the bf16 path's tile-image
+// workspace under 2^31 bytes (the kernels address it per slice).
+// Grid: (ceil(Nq/256), B*H) workgroups; pack: (ceil(Nk/64), B*H).  esize is
+// the input element size.
 int check_sizes(int B, int H, int Nq, int Nk, int d, int esize) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_JVP_EINVAL;
   if (d != 64 && d != 128) return ATTN_JVP_EUNSUPPORTED;
   const int64_t bh = int64_t(B) * H;
-  const int64_t kpad = (int64_t(Nk) + 63) / 64 * 64;
   if (bh > kMaxSlices) return ATTN_JVP_EUNSUPPORTED;
-  const int64_t qb = bh * Nq * d * esize, kb = bh * kpad * d * esize, ob = bh * Nq * d * 4;
-  const int64_t wsb = bh * kpad * d * 2 * 2;
+  const int64_t qb = bh * Nq * d * esize, kb = bh * Nk * d * esize, ob = bh * Nq * d * 4;
+  const int64_t wsb = int64_t(ajvp::bf16_workspace_bytes(1, 1, Nk, d));  // one slice
   if (qb >= kMaxTensorBytes || kb >= kMaxTensorBytes || ob >= kMaxTensorBytes ||
       wsb >= kMaxTensorBytes)
     return ATTN_JVP_EUNSUPPORTED;
@@ -127,30 +127,31 @@ int attn_jvp_fwd_ws(const void* q, const void* k, const void* v, const void* tq,
   return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
 }
 
-int attn_jvp_pack_v(const void* v, const void* tv, int B, int H, int Nk, int d, void* workspace,
-                    size_t workspace_bytes, attn_jvp_stream_t stream) {
-  if (v == nullptr || tv == nullptr) return ATTN_JVP_EINVAL;
+int attn_jvp_pack_kv(const void* k, const void* v, const void* tk, const void* tv, int B, int H,
+                     int Nk, int d, void* workspace, size_t workspace_bytes,
+                     attn_jvp_stream_t stream) {
+  if (k == nullptr || v == nullptr || tk == nullptr || tv == nullptr) return ATTN_JVP_EINVAL;
   int rc = check_sizes(B, H, 1, Nk, d, 2);
   if (rc != ATTN_JVP_OK) return rc;
   rc = check_workspace(workspace, workspace_bytes, B, H, Nk, d);
   if (rc != ATTN_JVP_OK) return rc;
-  if (misaligned(v, 16) || misaligned(tv, 16)) return ATTN_JVP_EALIGN;
-  hipError_t e = ajvp::launch_pack_v(v, tv, B, H, Nk, d, workspace,
-                                     reinterpret_cast<hipStream_t>(stream));
+  if (misaligned(k, 16) || misaligned(v, 16) || misaligned(tk, 16) || misaligned(tv, 16))
+    return ATTN_JVP_EALIGN;
+  hipError_t e = ajvp::launch_pack_kv(k, v, tk, tv, B, H, Nk, d, workspace,
+                                      reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
 }
 
-int attn_jvp_fwd_packed(const void* q, const void* k, const void* tq, const void* tk,
-                        const void* workspace, size_t workspace_bytes, float* o, float* to,
-                        float* lse, int B, int H, int Nq, int Nk, int d, float scale,
-                        attn_jvp_stream_t stream) {
-  const void* in[4] = {q, k, tq, tk};
-  int rc = validate(in, 4, o, to, lse, B, H, Nq, Nk, d, scale, 2);
+int attn_jvp_fwd_packed(const void* q, const void* tq, const void* workspace,
+                        size_t workspace_bytes, float* o, float* to, float* lse, int B, int H,
+                        int Nq, int Nk, int d, float scale, attn_jvp_stream_t stream) {
+  const void* in[2] = {q, tq};
+  int rc = validate(in, 2, o, to, lse, B, H, Nq, Nk, d, scale, 2);
   if (rc != ATTN_JVP_OK) return rc;
   rc = check_workspace(workspace, workspace_bytes, B, H, Nk, d);
   if (rc != ATTN_JVP_OK) return rc;
-  hipError_t e = ajvp::launch_bf16_packed(q, k, tq, tk, workspace, o, to, lse, B, H, Nq, Nk, d,
-                                          scale, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = ajvp::launch_bf16_packed(q, tq, workspace, o, to, lse, B, H, Nq, Nk, d, scale,
+                                          reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
 }
 

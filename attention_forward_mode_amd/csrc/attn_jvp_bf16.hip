@@ -7,14 +7,17 @@
 //   dS = s (dQ K^T + Q dK^T),  mu = rowsum(P * dS),  lse = ln rowsum exp(s Q K^T).
 //
 // Two kernels per call:
-//  1. pack_v: V and dV -> fp16, transposed to [d][64 keys] tiles in matrix-core
-//     operand order, zero-padded past Nk.  HBM
-//     bound, ~1% of the fused kernel's time at N = 32760.  fp16 instead of bf16
-//     for the second contraction keeps P and P*dS at 11 significant bits.
-//  2. attn_jvp_bf16: one workgroup = 4 waves x 32 query rows of one (b, h).
-//     Per 64-key tile: stage K, dK (bf16) and the packed V^T, dV^T (fp16) in
-//     LDS through registers (double buffered, loads one tile ahead), then
-//     per wave and 32-key block
+//  1. pack_kv: K, dK, V, dV -> one "tile image" per 64 keys in the workspace,
+//     byte for byte the LDS layout the fused kernel computes from: K and dK
+//     rows (bf16, padded), then V^T and dV^T (fp16, [d][64 keys] in
+//     matrix-core operand order, padded), zero past Nk.  HBM bound, under 1%
+//     of the fused kernel's time at N = 32760.  fp16 instead of bf16 for the
+//     second contraction keeps P and P*dS at 11 significant bits.
+//  2. attn_jvp_bf16: one workgroup = 8 waves x 32 query rows of one (b, h),
+//     two waves per SIMD.  Per 64-key tile the waves copy the next tile image
+//     from the workspace straight into LDS (buffer loads with the LDS-direct
+//     bit, 1 KiB per instruction, no registers in between; double buffered),
+//     then per wave and 32-key block
 //        S^T  = K Q^T            (bf16 MFMA 32x32x16, Q held in registers)
 //        dS^T = dK Q^T + K dQ^T  (same K fragments reused)
 //     online softmax in the accumulator layout (each lane owns one query row,
@@ -22,9 +25,12 @@
 //        A^T += V^T P^T,  G^T += V^T (s P dS)^T + dV^T P^T  (fp16 MFMA)
 //     with P, s*P*dS rounded to fp16.  The epilogue forms O = A / l,
 //     mu = u / l (u = rowsum s P dS), dO = G / l - mu O and lse.
-//  The running max is only raised when a tile's max exceeds it by more than
+//  While one wave of a SIMD runs its softmax on the vector ALU, the other
+//  keeps the matrix core busy; every wave fits in 256 registers (128
+//  accumulators, 64 for the Q and dQ operands, 64 for the rest).
+//  The running max is only raised when a block's max exceeds it by more than
 //  kTau (log2 units): results are exact either way, p stays <= 2^kTau, and the
-//  accumulator rescale is skipped on most tiles.
+//  accumulator rescale is skipped on most blocks.
 #include "cdna4.hpp"
 #include "launch.hpp"
 
@@ -32,16 +38,17 @@ namespace ajvp {
 namespace bf16_path {
 
 constexpr int kBC = 64;             // keys per tile
-constexpr int kThreads = 256;       // 4 waves
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
-constexpr int kBR = 128;            // query rows per workgroup
+constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
+constexpr int kPackThreads = 256;
 constexpr float kTau = 4.0f;        // lazy-rescale headroom, log2 units
+constexpr int kDmaBytes = 1024;     // one LDS-direct load: 64 lanes x 16 bytes
 
 template <int D>
 struct Geo {
-  static constexpr int kTileBytes = kBC * D * 2;          // one tile of K (bf16) or V^T (fp16)
-  static constexpr int kPackTileBytes = 2 * kTileBytes;   // V^T | dV^T in the workspace
-  // LDS rows are padded by 16 bytes: the 8 rows that one phase of a 16-byte
+  // LDS rows are padded by 16 bytes: the 16 rows that one phase of a 16-byte
   // matrix-operand read touches then start 16 bytes apart modulo the bank
   // width, so the reads are conflict-free, and every address is a per-lane
   // base plus a constant.
@@ -49,10 +56,15 @@ struct Geo {
   static constexpr int kVRow = kBC * 2 + 16;              // V^T, dV^T: D rows of 64 keys
   static constexpr int kKTile = kBC * kKRow;
   static constexpr int kVTile = D * kVRow;
-  static constexpr int kStageBytes = 2 * kKTile + 2 * kVTile;  // K | dK | V^T | dV^T
+  static constexpr int kImgUsed = 2 * kKTile + 2 * kVTile;  // K | dK | V^T | dV^T
+  // The image is a whole number of workgroup-wide copy rounds (8 KiB each).
+  static constexpr int kRound = kThreads * 16;
+  static constexpr int kImgBytes = (kImgUsed + kRound - 1) / kRound * kRound;
+  static constexpr int kDmaPerWave = kImgBytes / (kWaves * kDmaBytes);
   static constexpr int kKS = D / 16;                      // contraction steps over d
   static constexpr int kCB = D / 32;                      // 32-column output blocks
 };
+static_assert(Geo<128>::kImgBytes == 73728 && Geo<64>::kImgBytes == 40960, "tile image size");
 
 // Key held at position `pos` (0..63) of a packed V^T row.  Positions
 // 16G + 8g + e hold the keys that the S^T accumulator of lane half g puts in
@@ -63,31 +75,48 @@ __device__ inline int packed_key(int pos) {
   return 16 * G + (e < 4 ? 4 * g + e : 8 + 4 * g + (e - 4));
 }
 
+// One tile image: blockIdx.x = 64-key tile, blockIdx.y = (b, h) slice.
 template <int D>
-__device__ __attribute__((always_inline)) inline void pack_v_body(const uint16_t* __restrict__ v,
-                                                                  const uint16_t* __restrict__ dv,
-                                                                  char* __restrict__ ws, int Nk,
-                                                                  int ntiles, uint32_t v_bytes,
-                                                                  uint32_t ws_bytes) {
+__device__ __attribute__((always_inline)) inline void pack_kv_body(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dk, const uint16_t* __restrict__ dv, char* __restrict__ ws,
+    int Nk, int ntiles, uint32_t kv_bytes) {
   using G = Geo<D>;
   __shared__ _Float16 sv[2][kBC][D + 2];
-  const int tile = blockIdx.x;                 // 64-key tile
-  const uint32_t bh = blockIdx.y;              // (b, h) slice
+  const int tile = blockIdx.x;
+  const uint32_t bh = blockIdx.y;
   // Every global access goes through a buffer descriptor spanning the whole
   // tensor: an offset outside it is dropped (stores) or reads zero (loads).
-  const auto rv = make_rsrc(v, v_bytes);
-  const auto rdv = make_rsrc(dv, v_bytes);
-  const auto rws = make_rsrc(ws, ws_bytes);
+  const auto rk = make_rsrc(k, kv_bytes);
+  const auto rdk = make_rsrc(dk, kv_bytes);
+  const auto rv = make_rsrc(v, kv_bytes);
+  const auto rdv = make_rsrc(dv, kv_bytes);
+  // the workspace descriptor spans this (b, h) slice's images only
+  const uint32_t slice_bytes = (uint32_t)ntiles * G::kImgBytes;
+  const auto rws = make_rsrc(ws + (size_t)bh * slice_bytes, slice_bytes);
   const int key0 = tile * kBC;
-  constexpr int kIn = kBC * D / 8;  // 16-byte input chunks per tensor
-  for (int c = threadIdx.x; c < 2 * kIn; c += kThreads) {
-    const int t = c / kIn, rem = c % kIn, r = rem / (D / 8), col = (rem % (D / 8)) * 8;
+  const uint32_t img = (uint32_t)tile * G::kImgBytes;
+  constexpr int kChunksPerRow = D / 8;  // 16-byte chunks of one input row
+  constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
+  // K, dK: rows copied with a zero pad chunk after each; keys >= Nk are zero.
+  constexpr int kKChunks = kBC * (kChunksPerRow + 1);
+  for (int c = threadIdx.x; c < 2 * kKChunks; c += kPackThreads) {
+    const int t = c / kKChunks, rem = c % kKChunks;
+    const int r = rem / (kChunksPerRow + 1), col = rem % (kChunksPerRow + 1);
     const int key = key0 + r;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < Nk) {
-      const uint32_t off = ((bh * (uint32_t)Nk + key) * D + col) * 2;
-      x = buf_load16(t == 0 ? rv : rdv, off);
-    }
+    u32x4 x = kZero;
+    if (col < kChunksPerRow && key < Nk)
+      x = buf_load16(t == 0 ? rk : rdk, ((bh * (uint32_t)Nk + key) * D + 8 * col) * 2);
+    buf_store16(rws, img + t * G::kKTile + r * G::kKRow + col * 16, x);
+  }
+  // V, dV: to fp16 in LDS, then written transposed ([d][64 keys], keys in
+  // packed_key order) with a zero pad chunk after each row.
+  constexpr int kIn = kBC * kChunksPerRow;
+  for (int c = threadIdx.x; c < 2 * kIn; c += kPackThreads) {
+    const int t = c / kIn, rem = c % kIn, r = rem / kChunksPerRow, col = (rem % kChunksPerRow) * 8;
+    const int key = key0 + r;
+    u32x4 x = kZero;
+    if (key < Nk) x = buf_load16(t == 0 ? rv : rdv, ((bh * (uint32_t)Nk + key) * D + col) * 2);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t bits = (x[e >> 1] >> (16 * (e & 1))) & 0xffffu;
@@ -95,14 +124,20 @@ __device__ __attribute__((always_inline)) inline void pack_v_body(const uint16_t
     }
   }
   __syncthreads();
-  const uint32_t out = (bh * (uint32_t)ntiles + tile) * G::kPackTileBytes;
-  for (int c = threadIdx.x; c < 2 * D * 8; c += kThreads) {
-    const int t = c / (D * 8), rem = c % (D * 8), col = rem / 8, p = rem % 8;
-    f16x8 h;
+  for (int c = threadIdx.x; c < 2 * D * 9; c += kPackThreads) {
+    const int t = c / (D * 9), rem = c % (D * 9), col = rem / 9, p = rem % 9;
+    u32x4 x = kZero;
+    if (p < 8) {
+      f16x8 h;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = sv[t][packed_key(8 * p + e)][col];
-    buf_store16(rws, out + t * G::kTileBytes + col * 128 + p * 16, __builtin_bit_cast(u32x4, h));
+      for (int e = 0; e < 8; ++e) h[e] = sv[t][packed_key(8 * p + e)][col];
+      x = __builtin_bit_cast(u32x4, h);
+    }
+    buf_store16(rws, img + 2 * G::kKTile + t * G::kVTile + col * G::kVRow + p * 16, x);
   }
+  // the image's tail beyond the four tiles
+  for (int o = G::kImgUsed + threadIdx.x * 16; o < G::kImgBytes; o += kPackThreads * 16)
+    buf_store16(rws, img + o, kZero);
 }
 
 template <int D>
@@ -110,19 +145,8 @@ struct RowState {
   f32x16 accA[Geo<D>::kCB];  // A^T = sum p v      (rows: output column, cols: query)
   f32x16 accG[Geo<D>::kCB];  // G^T = sum p (s dS v + dv)
   float m;                   // running max of s*log2e*S (log2 units), per query row
-  float alpha;               // 2^(m_prev - m) of the latest max update
   float l;                   // this lane's half of sum p         (of the fp16-rounded p)
   float u;                   // this lane's half of sum s p dS    (of the fp16-rounded values)
-};
-
-// S^T and dS^T of one 32-key block (rows: key, columns: this wave's queries).
-struct SBlock {
-  f32x16 s, ds;
-};
-
-// Operands of the second contraction for one block: P and s*P*dS in fp16.
-struct PBlock {
-  u32x4 p[2], pd[2];
 };
 
 // Slot r of lane half g holds key 8(r/4) + 4g + r%4 of its 32-key block.
@@ -130,185 +154,148 @@ __device__ __attribute__((always_inline)) inline int slot_key(int r, int g) {
   return 8 * (r >> 2) + 4 * g + (r & 3);
 }
 
-// ---- the per-block pipeline ----
-// Block j of the key sequence passes through two scheduling regions:
-//   R1(j): S/dS of block j on the matrix cores, while the vector ALU turns
-//          block j-1 into P, s*P*dS (fp16) and its row sums;
-//   R2(j): P V of block j-1 on the matrix cores, while the vector ALU finds
-//          the max of block j's S and the new running max / rescale factor;
-//   then the accumulators are rescaled (rare, see kTau).
-// Both regions are written as slots of one matrix-core instruction plus a
-// share of vector work, separated by scheduling barriers, so the two units
-// run side by side within one wave.  Operand fragments are read from LDS two
-// slots-of-three ahead of their use.
-// Online-softmax order: P V of block j-1 (normalised to m_{j-1}) is added
-// before the rescale by alpha_j = 2^(m_{j-1} - m_j), and P of block j is
-// formed with m_j, so the accumulators always hold sums normalised to the
-// current m.
-
-// R1.  kQK: form S/dS of block `kb` of `stage` into `snew`.  kEW: finish block
-// `sold` (max already applied to st.m): P, s*P*dS -> `pb`, and l, u updated
-// with the rescale factor of that block.  kMask: `sold` lies in the last tile
-// (keys >= Nk get p = 0 and contribute nothing to u).  Each pair of results is
-// rounded to fp16 as soon as it exists, and l, u sum exactly those rounded
-// values (one dot instruction per pair): the weights that the normalisation
-// uses are the ones the matrix cores multiply, so O is an exact convex
-// combination of V's rows and sum_j (p_j dS_j - mu p_j) cancels as it must.
-template <int D, bool kQK, bool kEW, bool kMask>
-__device__ __attribute__((always_inline)) inline void region1(
+// One 32-key block (block `kb` of the tile in `stage`) for this wave's 32
+// query rows.  kMask: the block lies in the last tile, whose keys >= Nk get
+// p = 0 and contribute nothing to u.
+// Online-softmax order: the accumulators hold sums normalised to the running
+// max m; a raised max rescales them by alpha = 2^(m_old - m_new) before this
+// block's P V is added.
+template <int D, bool kMask>
+__device__ __attribute__((always_inline)) inline void jvp_block(
     RowState<D>& st, const char* stage, int kb, const u32x4* qf, const u32x4* dqf, int l32,
-    int g, SBlock& snew, const SBlock& sold, int key0_old, int Nk, float c_log2, float scale,
-    PBlock& pb) {
+    int g, int key0, int Nk, float c_log2, float scale) {
   using G = Geo<D>;
-  constexpr int kSlots = 3 * G::kKS;
-  constexpr int kPairSlots = kSlots - 1;  // element pairs spread over these slots
   const char* sK = stage;
   const char* sdK = stage + G::kKTile;
-  const int rowoff = (32 * kb + l32) * G::kKRow + 16 * g;
-  u32x4 ka[3], kda[3];
-  if constexpr (kQK) {
+  const char* sV = stage + 2 * G::kKTile;
+  const char* sdV = sV + G::kVTile;
+
+  // S^T and dS^T (rows: key, columns: this wave's queries)
+  // Scheduling barriers keep the compiler from hoisting operand reads (and
+  // their registers) across steps; the other wave on the SIMD covers the LDS
+  // latency.
+  const int krow = (32 * kb + l32) * G::kKRow + 16 * g;
+  f32x16 s, ds;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      ka[ks] = lds_load16(sK + rowoff + 32 * ks);
-      kda[ks] = lds_load16(sdK + rowoff + 32 * ks);
+  for (int ks = 0; ks < G::kKS; ++ks) {
+    const u32x4 kf = lds_load16(sK + krow + 32 * ks);
+    const u32x4 dkf = lds_load16(sdK + krow + 32 * ks);
+    s = mma_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s);
+    ds = mma_bf16(kf, dqf[ks], ks == 0 ? f32x16{} : ds);
+    ds = mma_bf16(dkf, qf[ks], ds);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // running max (NaN-propagating maximum, combined across the half-waves)
+  if constexpr (kMask) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (key0 + slot_key(r, g) >= Nk) s[r] = -INFINITY;
+  }
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, s[r]);
+  mx = halves_max(mx);
+  const float mt = mx * c_log2;
+  const float m_new = (mt > st.m + kTau) ? mt : st.m;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  st.m = m_new;
+
+  // P and s*P*dS, rounded to fp16 in pairs straight into the B operands of the
+  // second contraction; l and u sum exactly those rounded values (one dot
+  // instruction per pair), so the weights of the normalisation are the ones
+  // the matrix cores multiply: O is an exact convex combination of V's rows
+  // and sum_j (p_j s dS_j - mu p_j) cancels as it must.
+  u32x4 p[2], pd[2];
+  float lsum = 0.f, usum = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    float pp[2], pdd[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 2 * q + e;
+      pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -m_new));
+      pdd[e] = pp[e] * ds[r] * scale;
+      if (kMask && key0 + slot_key(r, g) >= Nk) {
+        pp[e] = 0.f;
+        pdd[e] = 0.f;
+      }
+    }
+    const uint32_t hp = pack_f16x2(pp[0], pp[1]);
+    const uint32_t hd = pack_f16x2(pdd[0], pdd[1]);
+    p[q >> 2][q & 3] = hp;
+    pd[q >> 2][q & 3] = hd;
+    lsum = add_f16x2(hp, lsum);
+    usum = add_f16x2(hd, usum);
+  }
+  st.l = st.l * alpha + lsum;
+  st.u = st.u * alpha + usum;
+  // Pin the sums here (empty asm: a register constraint only); left alone, the
+  // compiler sinks them into the next block and keeps P alive until then.
+  asm volatile("" : "+v"(st.l), "+v"(st.u));
+  if (wave_any(alpha != 1.0f)) {
+#pragma unroll
+    for (int cb = 0; cb < G::kCB; ++cb) {
+      st.accA[cb] *= alpha;
+      st.accG[cb] *= alpha;
     }
   }
-  float lsum = 0.f, usum = 0.f;
-  const float m = st.m;
+
+  __builtin_amdgcn_sched_barrier(0);
+
+  // A^T += V^T P^T, G^T += V^T (s P dS)^T + dV^T P^T; step = (t, cb)
+  constexpr int kSteps = 2 * G::kCB;
+  auto voff = [&](int step) {
+    const int t = step / G::kCB, cb = step % G::kCB;
+    return (32 * cb + l32) * G::kVRow + 16 * g + 16 * (4 * kb + 2 * t);
+  };
 #pragma unroll
-  for (int i = 0; i < kSlots; ++i) {
-    if constexpr (kQK) {
-      const int ks = i / 3, w = i % 3;
-      if (w == 0 && ks + 2 < G::kKS) {
-        ka[(ks + 2) % 3] = lds_load16(sK + rowoff + 32 * (ks + 2));
-        kda[(ks + 2) % 3] = lds_load16(sdK + rowoff + 32 * (ks + 2));
-      }
-      if (w == 0) snew.s = mma_bf16(ka[ks % 3], qf[ks], ks == 0 ? f32x16{} : snew.s);
-      if (w == 1) snew.ds = mma_bf16(ka[ks % 3], dqf[ks], ks == 0 ? f32x16{} : snew.ds);
-      if (w == 2) snew.ds = mma_bf16(kda[ks % 3], qf[ks], snew.ds);
-    }
-    if constexpr (kEW) {
-#pragma unroll
-      for (int q = i * 8 / kPairSlots; q < (i + 1) * 8 / kPairSlots && q < 8; ++q) {
-        float pp[2], pdd[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = 2 * q + e;
-          pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sold.s[r], c_log2, -m));
-          pdd[e] = pp[e] * sold.ds[r] * scale;
-          if (kMask && key0_old + slot_key(r, g) >= Nk) {
-            pp[e] = 0.f;
-            pdd[e] = 0.f;
-          }
-        }
-        const uint32_t hp = pack_f16x2(pp[0], pp[1]);
-        const uint32_t hd = pack_f16x2(pdd[0], pdd[1]);
-        pb.p[q >> 2][q & 3] = hp;
-        pb.pd[q >> 2][q & 3] = hd;
-        lsum = add_f16x2(hp, lsum);
-        usum = add_f16x2(hd, usum);
-      }
-      if (i == kSlots - 1) {
-        st.l = st.l * st.alpha + lsum;
-        st.u = st.u * st.alpha + usum;
-      }
-    }
+  for (int step = 0; step < kSteps; ++step) {
+    const int t = step / G::kCB, cb = step % G::kCB;
+    const u32x4 vf = lds_load16(sV + voff(step));
+    const u32x4 dvf = lds_load16(sdV + voff(step));
+    st.accA[cb] = mma_f16(vf, p[t], st.accA[cb]);
+    st.accG[cb] = mma_f16(vf, pd[t], st.accG[cb]);
+    st.accG[cb] = mma_f16(dvf, p[t], st.accG[cb]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// R2.  kPV: A^T += V^T P^T, G^T += V^T (s P dS)^T + dV^T P^T for block `kb` of
-// `stage` with operands `pb`.  kMax: running-max update from block `snew`
-// (kMask: its keys >= Nk are left out), then the rescale.
-template <int D, bool kPV, bool kMax, bool kMask>
-__device__ __attribute__((always_inline)) inline void region2(
-    RowState<D>& st, const char* stage, int kb, const PBlock& pb, int l32, int g,
-    SBlock& snew, int key0_new, int Nk, float c_log2) {
-  using G = Geo<D>;
-  constexpr int kSteps = 2 * G::kCB;  // (cb, t) pairs, three products each
-  constexpr int kSlots = 3 * kSteps;
-  const char* sV = stage + 2 * G::kKTile;
-  const char* sdV = sV + G::kVTile;
-  auto voff = [&](int step) {  // step = 2 cb + t
-    return ((32 * (step >> 1) + l32) * G::kVRow + 16 * g) + 16 * (4 * kb + 2 * (step & 1));
-  };
-  u32x4 va[3], vda[3];
-  if constexpr (kPV) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      va[k] = lds_load16(sV + voff(k));
-      vda[k] = lds_load16(sdV + voff(k));
-    }
-  }
-  if constexpr (kMax && kMask) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (key0_new + slot_key(r, g) >= Nk) snew.s[r] = -INFINITY;
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kSlots; ++i) {
-    if constexpr (kPV) {
-      const int step = i / 3, w = i % 3, cb = step >> 1, t = step & 1;
-      if (w == 0 && step + 2 < kSteps) {
-        va[(step + 2) % 3] = lds_load16(sV + voff(step + 2));
-        vda[(step + 2) % 3] = lds_load16(sdV + voff(step + 2));
-      }
-      if (w == 0) st.accA[cb] = mma_f16(va[step % 3], pb.p[t], st.accA[cb]);
-      if (w == 1) st.accG[cb] = mma_f16(va[step % 3], pb.pd[t], st.accG[cb]);
-      if (w == 2) st.accG[cb] = mma_f16(vda[step % 3], pb.p[t], st.accG[cb]);
-    }
-    if constexpr (kMax) {
-      // two elements per slot over the first eight slots, then the combine.
-      // NaN-propagating maximum: one v_maximum3 per slot, no canonicalisation.
-      if (i < 8)
-        mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, snew.s[2 * i]),
-                                           snew.s[2 * i + 1]);
-      if (i == 8) {
-        mx = halves_max(mx);
-        const float mt = mx * c_log2;
-        const float m_new = (mt > st.m + kTau) ? mt : st.m;
-        st.alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-        st.m = m_new;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if constexpr (kMax) {
-    if (wave_any(st.alpha != 1.0f)) {
-      // One 16-register block at a time, so this rare path needs few
-      // temporaries and does not raise the main path's register pressure.
-#pragma unroll
-      for (int cb = 0; cb < G::kCB; ++cb) {
-        st.accA[cb] *= st.alpha;
-        __builtin_amdgcn_sched_barrier(0);
-        st.accG[cb] *= st.alpha;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
+// One full tile: the copy of the next tile image into `next` is issued first,
+// then both 32-key blocks are computed from `cur`.  The two stage pointers are
+// restrict-qualified (they name disjoint halves of the LDS), which tells the
+// compiler that reads of `cur` need not wait for the copy into `next`.
+template <int D, typename Copy>
+__device__ __attribute__((always_inline)) inline void tile_step(
+    char* __restrict__ next, const char* __restrict__ cur, Copy copy, RowState<D>& st,
+    const u32x4* qf, const u32x4* dqf, int l32, int g, int Nk, float c_log2, float scale) {
+  copy(next);
+  jvp_block<D, false>(st, cur, 0, qf, dqf, l32, g, 0, Nk, c_log2, scale);
+  jvp_block<D, false>(st, cur, 1, qf, dqf, l32, g, 0, Nk, c_log2, scale);
 }
 
 // Sizes of the whole tensors (bytes) the kernel may touch; each global access
 // is checked against them by the buffer descriptor.
 struct Extents {
-  uint32_t q_bytes, k_bytes, ws_bytes, o_bytes, lse_bytes;
+  uint32_t q_bytes, o_bytes, lse_bytes;
 };
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int D>
 __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ tq, const uint16_t* __restrict__ tk,
-    const char* __restrict__ vpack, float* __restrict__ o, float* __restrict__ to,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ tq,
+    const char* __restrict__ img, float* __restrict__ o, float* __restrict__ to,
     float* __restrict__ lse, int Nq, int Nk, int ntiles, Extents ext, float scale,
     float c_log2) {
   using G = Geo<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * G::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::kImgBytes];
 
-  // Work item: blockIdx.x = 128-row query tile, blockIdx.y = (b, h) slice.
+  // Work item: blockIdx.x = query tile of kBR rows, blockIdx.y = (b, h) slice.
   const int qt = blockIdx.x;
   const uint32_t bh = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int row = qt * kBR + wave * kRowsPerWave + l32;
   const bool row_ok = row < Nq;
@@ -316,11 +303,25 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
   // Buffer descriptors over whole tensors (see Extents).
   const auto rq = make_rsrc(q, ext.q_bytes);
   const auto rtq = make_rsrc(tq, ext.q_bytes);
-  const auto rk = make_rsrc(k, ext.k_bytes);
-  const auto rtk = make_rsrc(tk, ext.k_bytes);
-  const auto rv = make_rsrc(vpack, ext.ws_bytes);
+  // the workspace descriptor spans this (b, h) slice's tile images only
+  const uint32_t slice_bytes = (uint32_t)ntiles * G::kImgBytes;
+  const auto rimg = make_rsrc(img + (size_t)bh * slice_bytes, slice_bytes);
   const auto ro = make_rsrc(o, ext.o_bytes);
   const auto rto = make_rsrc(to, ext.o_bytes);
+
+  // Copy of tile image kt into a stage: this wave's kDmaPerWave consecutive
+  // KiB, lane l moving bytes 16 l .. 16 l + 15 of each (LDS address = the
+  // wave-uniform stage pointer + 16 l; global = image offset + 16 l).
+  const uint32_t wave_part = (uint32_t)wave * G::kDmaPerWave * kDmaBytes;
+  auto copy_tile = [&](int kt, char* stage) {
+    const uint32_t src = (uint32_t)kt * G::kImgBytes + wave_part;
+#pragma unroll
+    for (int j = 0; j < G::kDmaPerWave; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rimg, (lds_ptr_t)(stage + wave_part + j * kDmaBytes),
+                                               16, lane * 16, src + j * kDmaBytes, 0, 0);
+  };
+
+  copy_tile(0, smem);
 
   // Q and dQ fragments: the B operand of S^T = K Q^T (lane: row l32, d-slice g).
   // Rows past Nq get an offset past the tensor, which the descriptor reads as 0.
@@ -332,56 +333,6 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
     qf[ks] = buf_load16(rq, off);
     dqf[ks] = buf_load16(rtq, off);
   }
-  // The Q/dQ fragments are only ever matrix-core operands, which may come
-  // from accumulation registers: keep them there and leave the vector
-  // registers to the softmax.  (Empty asm: a register-class constraint only.)
-#pragma unroll
-  for (int ks = 0; ks < G::kKS; ++ks) asm volatile("" : "+a"(qf[ks]), "+a"(dqf[ks]));
-
-  // Staging through registers, one tensor pair at a time: each thread loads
-  // kChunks 16-byte chunks of K|dK (or of the packed V^T|dV^T tile) into stg
-  // and later writes them to LDS.  Chunk n of thread tid is chunk tid + 256 n
-  // of the tile pair: its row advances by a constant per n, so the per-lane
-  // part of every offset is fixed and the rest is a constant or wave-uniform.
-  // Key rows past Nk in the last tile hold whatever the descriptor returns;
-  // they are masked in the compute.
-  constexpr int kChunks = G::kTileBytes * 2 / 16 / kThreads;  // per pair of tensors
-  constexpr int kChunksPerTensor = kChunks / 2;
-  constexpr int kKRowsPerN = kThreads / (D / 8);   // K rows advanced per chunk step
-  constexpr int kVRowsPerN = kThreads / 8;         // V^T rows advanced per chunk step
-  const uint32_t kslice = bh * (uint32_t)Nk * D * 2;
-  const uint32_t vslice = bh * (uint32_t)ntiles * G::kPackTileBytes;
-  const uint32_t k_lane = (uint32_t)tid * 16;  // global: row tid/(D/8), chunk tid%(D/8)
-  const int k_lds = (tid / (D / 8)) * G::kKRow + (tid % (D / 8)) * 16;
-  const int v_lds = (tid / 8) * G::kVRow + (tid % 8) * 16;
-  u32x4 stg[kChunks];
-  auto load_k = [&](int kt) {
-    const uint32_t kbase = kslice + (uint32_t)kt * kBC * D * 2;
-#pragma unroll
-    for (int n = 0; n < kChunks; ++n)
-      stg[n] = buf_load16(n < kChunksPerTensor ? rk : rtk, k_lane,
-                          kbase + (uint32_t)(n % kChunksPerTensor) * kThreads * 16);
-  };
-  auto load_v = [&](int kt) {
-    const uint32_t vbase = vslice + (uint32_t)kt * G::kPackTileBytes;
-#pragma unroll
-    for (int n = 0; n < kChunks; ++n)
-      stg[n] = buf_load16(rv, k_lane, vbase + (uint32_t)n * kThreads * 16);
-  };
-  auto store_k = [&](char* sb) {
-#pragma unroll
-    for (int n = 0; n < kChunks; ++n)
-      lds_store16(sb + k_lds + (n / kChunksPerTensor) * G::kKTile +
-                      (n % kChunksPerTensor) * kKRowsPerN * G::kKRow,
-                  stg[n]);
-  };
-  // The V^T and dV^T tiles are D rows each, so row r >= D of the pair is row
-  // r - D of dV^T, which starts kVTile bytes after V^T: one formula covers both.
-  auto store_v = [&](char* sb) {
-#pragma unroll
-    for (int n = 0; n < kChunks; ++n)
-      lds_store16(sb + 2 * G::kKTile + v_lds + n * kVRowsPerN * G::kVRow, stg[n]);
-  };
 
   RowState<D> st;
 #pragma unroll
@@ -390,75 +341,31 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
     st.accG[cb] = f32x16{};
   }
   st.m = -INFINITY;
-  st.alpha = 1.f;
   st.l = 0.f;
   st.u = 0.f;
 
-  // Blocks j = 0 .. 2*ntiles-1 (block j is half j % 2 of tile j / 2) run
-  // through region1 / region2 (R1(j), R2(j)) as described above.  K|dK(t) and
-  // V|dV(t) live in LDS buffer t % 2; K(t) is read in R1 of blocks 2t, 2t+1
-  // and V(t) in R2 of blocks 2t+1, 2t+2.  Per tile kt, with a barrier after
-  // each block:
-  //   K|dK(kt+1) -> LDS, V|dV(kt+1) loads issued   (K|dK(kt-1) last read in block 2kt-1)
-  //   block 2kt,   barrier
-  //   V|dV(kt+1) -> LDS, K|dK(kt+2) loads issued   (V|dV(kt-1) last read in block 2kt)
-  //   block 2kt+1, barrier
-  // so K|dK(kt+1) is visible from block 2kt+1 on and V|dV(kt+1) from 2kt+2 on.
-  SBlock sa, sb;  // S/dS of the even / odd block
-  PBlock pb;      // P, s*P*dS of the block whose P V is next
+  // Tile kt is computed from stage kt % 2 while tile kt + 1 is copied into
+  // the other stage; the wait for the copies and the barrier at the end of
+  // each tile make tile kt + 1 visible to every wave and retire every read of
+  // stage kt % 2 before the next copy into it starts.
   const int kLast = ntiles - 1;
-  const int key_last = kLast * kBC;
-  auto stage = [&](int t) { return smem + (t & 1) * G::kStageBytes; };
-  load_k(0);
-  store_k(smem);
-  load_v(0);
-  store_v(smem);
-  load_k(1);  // past the last tile the descriptors read zeros or unused data
-  __syncthreads();
-  if (ntiles == 1) {
-    region1<D, true, false, false>(st, smem, 0, qf, dqf, l32, g, sa, sb, 0, Nk, c_log2, scale, pb);
-    region2<D, false, true, true>(st, smem, 0, pb, l32, g, sa, 0, Nk, c_log2);
-    region1<D, true, true, true>(st, smem, 1, qf, dqf, l32, g, sb, sa, 0, Nk, c_log2, scale, pb);
-    region2<D, true, true, true>(st, smem, 0, pb, l32, g, sb, 32, Nk, c_log2);
-    region1<D, false, true, true>(st, smem, 0, qf, dqf, l32, g, sa, sb, 32, Nk, c_log2, scale, pb);
-    region2<D, true, false, false>(st, smem, 1, pb, l32, g, sb, 0, Nk, c_log2);
-  } else {
-    // tile 0
-    store_k(stage(1));
-    load_v(1);
-    region1<D, true, false, false>(st, smem, 0, qf, dqf, l32, g, sa, sb, 0, Nk, c_log2, scale, pb);
-    region2<D, false, true, false>(st, smem, 0, pb, l32, g, sa, 0, Nk, c_log2);
+  auto finish_tile = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    store_v(stage(1));
-    load_k(2);
-    region1<D, true, true, false>(st, smem, 1, qf, dqf, l32, g, sb, sa, 0, Nk, c_log2, scale, pb);
-    region2<D, true, true, false>(st, smem, 0, pb, l32, g, sb, 0, Nk, c_log2);
-    __syncthreads();
-    // tiles 1 .. ntiles-2
-    for (int kt = 1; kt < kLast; ++kt) {
-      store_k(stage(kt + 1));
-      load_v(kt + 1);
-      region1<D, true, true, false>(st, stage(kt), 0, qf, dqf, l32, g, sa, sb, 0, Nk, c_log2,
-                                    scale, pb);
-      region2<D, true, true, false>(st, stage(kt - 1), 1, pb, l32, g, sa, 0, Nk, c_log2);
-      __syncthreads();
-      store_v(stage(kt + 1));
-      load_k(kt + 2);
-      region1<D, true, true, false>(st, stage(kt), 1, qf, dqf, l32, g, sb, sa, 0, Nk, c_log2,
-                                    scale, pb);
-      region2<D, true, true, false>(st, stage(kt), 0, pb, l32, g, sb, 0, Nk, c_log2);
-      __syncthreads();
-    }
-    // last tile: keys past Nk are masked (the tile is complete in LDS already)
-    region1<D, true, true, false>(st, stage(kLast), 0, qf, dqf, l32, g, sa, sb, 0, Nk, c_log2,
-                                  scale, pb);
-    region2<D, true, true, true>(st, stage(kLast - 1), 1, pb, l32, g, sa, key_last, Nk, c_log2);
-    region1<D, true, true, true>(st, stage(kLast), 1, qf, dqf, l32, g, sb, sa, key_last, Nk,
-                                 c_log2, scale, pb);
-    region2<D, true, true, true>(st, stage(kLast), 0, pb, l32, g, sb, key_last + 32, Nk, c_log2);
-    region1<D, false, true, true>(st, stage(kLast), 0, qf, dqf, l32, g, sa, sb, key_last + 32, Nk,
-                                  c_log2, scale, pb);
-    region2<D, true, false, false>(st, stage(kLast), 1, pb, l32, g, sb, 0, Nk, c_log2);
+  };
+  finish_tile();
+  for (int kt = 0; kt < kLast; ++kt) {
+    tile_step<D>(smem + ((kt + 1) & 1) * G::kImgBytes, smem + (kt & 1) * G::kImgBytes,
+                 [&](char* next) { copy_tile(kt + 1, next); }, st, qf, dqf, l32, g, Nk,
+                 c_log2, scale);
+    finish_tile();
+  }
+  // last tile: keys past Nk are masked (the tile image holds zeros there)
+  {
+    const char* cur = smem + (kLast & 1) * G::kImgBytes;
+    const int kl = kLast * kBC;
+    jvp_block<D, true>(st, cur, 0, qf, dqf, l32, g, kl, Nk, c_log2, scale);
+    jvp_block<D, true>(st, cur, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, scale);
   }
 
   // ---- epilogue: O = A / l, mu = u / l, dO = G / l - mu O, lse ----
@@ -491,18 +398,18 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
 }
 
 #define AJVP_BF16_KERNEL(D)                                                                 \
-  __global__ __launch_bounds__(kThreads, 1) void attn_jvp_bf16_d##D(                         \
-      const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,                        \
-      const uint16_t* __restrict__ tq, const uint16_t* __restrict__ tk,                      \
-      const char* __restrict__ vpack, float* __restrict__ o, float* __restrict__ to,         \
+  __global__ __launch_bounds__(kThreads) void attn_jvp_bf16_d##D(                            \
+      const uint16_t* __restrict__ q, const uint16_t* __restrict__ tq,                       \
+      const char* __restrict__ img, float* __restrict__ o, float* __restrict__ to,           \
       float* __restrict__ lse, int Nq, int Nk, int ntiles, Extents ext, float scale,         \
       float c_log2) {                                                                         \
-    attn_jvp_bf16_body<D>(q, k, tq, tk, vpack, o, to, lse, Nq, Nk, ntiles, ext, scale, c_log2); \
+    attn_jvp_bf16_body<D>(q, tq, img, o, to, lse, Nq, Nk, ntiles, ext, scale, c_log2);       \
   }                                                                                           \
-  __global__ __launch_bounds__(kThreads) void pack_v_d##D(                                   \
-      const uint16_t* __restrict__ v, const uint16_t* __restrict__ dv, char* __restrict__ ws, \
-      int Nk, int ntiles, uint32_t v_bytes, uint32_t ws_bytes) {                              \
-    pack_v_body<D>(v, dv, ws, Nk, ntiles, v_bytes, ws_bytes);                                 \
+  __global__ __launch_bounds__(kPackThreads) void pack_kv_d##D(                              \
+      const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,                        \
+      const uint16_t* __restrict__ dk, const uint16_t* __restrict__ dv, char* __restrict__ ws, \
+      int Nk, int ntiles, uint32_t kv_bytes) {                                                \
+    pack_kv_body<D>(k, v, dk, dv, ws, Nk, ntiles, kv_bytes);                                  \
   }
 AJVP_BF16_KERNEL(64)
 AJVP_BF16_KERNEL(128)
@@ -513,43 +420,40 @@ struct Kernels;
 template <>
 struct Kernels<64> {
   static constexpr auto main = attn_jvp_bf16_d64;
-  static constexpr auto pack = pack_v_d64;
+  static constexpr auto pack = pack_kv_d64;
 };
 template <>
 struct Kernels<128> {
   static constexpr auto main = attn_jvp_bf16_d128;
-  static constexpr auto pack = pack_v_d128;
+  static constexpr auto pack = pack_kv_d128;
 };
 
 template <int D>
-hipError_t launch_pack_d(const void* v, const void* tv, int B, int H, int Nk, void* ws,
-                         hipStream_t stream) {
+hipError_t launch_pack_d(const void* k, const void* v, const void* tk, const void* tv, int B,
+                         int H, int Nk, void* ws, hipStream_t stream) {
   const int ntiles = (Nk + kBC - 1) / kBC;
   const int bh = B * H;
-  const uint32_t v_bytes = (uint32_t)((size_t)bh * Nk * D * 2);
-  const uint32_t ws_bytes = (uint32_t)bf16_workspace_bytes(B, H, Nk, D);
-  hipLaunchKernelGGL(Kernels<D>::pack, dim3(ntiles, bh), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(tv),
-                     static_cast<char*>(ws), Nk, ntiles, v_bytes, ws_bytes);
+  const uint32_t kv_bytes = (uint32_t)((size_t)bh * Nk * D * 2);
+  hipLaunchKernelGGL(Kernels<D>::pack, dim3(ntiles, bh), dim3(kPackThreads), 0, stream,
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                     static_cast<const uint16_t*>(tk), static_cast<const uint16_t*>(tv),
+                     static_cast<char*>(ws), Nk, ntiles, kv_bytes);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_main_d(const void* q, const void* k, const void* tq, const void* tk,
-                         const void* ws, float* o, float* to, float* lse, int B, int H, int Nq,
-                         int Nk, float scale, hipStream_t stream) {
+hipError_t launch_main_d(const void* q, const void* tq, const void* ws, float* o, float* to,
+                         float* lse, int B, int H, int Nq, int Nk, float scale,
+                         hipStream_t stream) {
   const int ntiles = (Nk + kBC - 1) / kBC;
   const int nqt = (Nq + kBR - 1) / kBR;
   const int bh = B * H;
   Extents ext;
   ext.q_bytes = (uint32_t)((size_t)bh * Nq * D * 2);
-  ext.k_bytes = (uint32_t)((size_t)bh * Nk * D * 2);
-  ext.ws_bytes = (uint32_t)bf16_workspace_bytes(B, H, Nk, D);
   ext.o_bytes = (uint32_t)((size_t)bh * Nq * D * 4);
   ext.lse_bytes = (uint32_t)((size_t)bh * Nq * 4);
   hipLaunchKernelGGL(Kernels<D>::main, dim3(nqt, bh), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(tq), static_cast<const uint16_t*>(tk),
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(tq),
                      static_cast<const char*>(ws), o, to, lse, Nq, Nk, ntiles, ext, scale,
                      scale * kLog2e);
   return hipGetLastError();
@@ -560,28 +464,29 @@ using namespace bf16_path;
 
 size_t bf16_workspace_bytes(int B, int H, int Nk, int d) {
   const size_t ntiles = ((size_t)Nk + kBC - 1) / kBC;
-  return (size_t)B * H * ntiles * 2 * kBC * (size_t)d * 2;
+  const size_t img = d == 128 ? Geo<128>::kImgBytes : Geo<64>::kImgBytes;
+  return (size_t)B * H * ntiles * img;
 }
 
-hipError_t launch_pack_v(const void* v, const void* tv, int B, int H, int Nk, int d, void* ws,
-                         hipStream_t stream) {
-  return d == 128 ? launch_pack_d<128>(v, tv, B, H, Nk, ws, stream)
-                  : launch_pack_d<64>(v, tv, B, H, Nk, ws, stream);
+hipError_t launch_pack_kv(const void* k, const void* v, const void* tk, const void* tv, int B,
+                          int H, int Nk, int d, void* ws, hipStream_t stream) {
+  return d == 128 ? launch_pack_d<128>(k, v, tk, tv, B, H, Nk, ws, stream)
+                  : launch_pack_d<64>(k, v, tk, tv, B, H, Nk, ws, stream);
 }
 
-hipError_t launch_bf16_packed(const void* q, const void* k, const void* tq, const void* tk,
-                              const void* ws, float* o, float* to, float* lse, int B, int H,
-                              int Nq, int Nk, int d, float scale, hipStream_t stream) {
-  return d == 128 ? launch_main_d<128>(q, k, tq, tk, ws, o, to, lse, B, H, Nq, Nk, scale, stream)
-                  : launch_main_d<64>(q, k, tq, tk, ws, o, to, lse, B, H, Nq, Nk, scale, stream);
+hipError_t launch_bf16_packed(const void* q, const void* tq, const void* ws, float* o,
+                              float* to, float* lse, int B, int H, int Nq, int Nk, int d,
+                              float scale, hipStream_t stream) {
+  return d == 128 ? launch_main_d<128>(q, tq, ws, o, to, lse, B, H, Nq, Nk, scale, stream)
+                  : launch_main_d<64>(q, tq, ws, o, to, lse, B, H, Nq, Nk, scale, stream);
 }
 
 hipError_t launch_bf16(const void* q, const void* k, const void* v, const void* tq,
                        const void* tk, const void* tv, float* o, float* to, float* lse, int B,
                        int H, int Nq, int Nk, int d, float scale, void* ws, hipStream_t stream) {
-  const hipError_t e = launch_pack_v(v, tv, B, H, Nk, d, ws, stream);
+  const hipError_t e = launch_pack_kv(k, v, tk, tv, B, H, Nk, d, ws, stream);
   if (e != hipSuccess) return e;
-  return launch_bf16_packed(q, k, tq, tk, ws, o, to, lse, B, H, Nq, Nk, d, scale, stream);
+  return launch_bf16_packed(q, tq, ws, o, to, lse, B, H, Nq, Nk, d, scale, stream);
 }
 
 }  // namespace ajvp

@@ -8,7 +8,8 @@
 
 namespace ajvp {
 
-// Workspace bytes of the bf16 path: fp16 V^T and dV^T tiles, 64 keys each.
+// Workspace bytes of the bf16 path: one LDS tile image (K, dK, V^T, dV^T) per
+// (b, h) and 64-key tile.
 size_t bf16_workspace_bytes(int B, int H, int Nk, int d);
 
 hipError_t launch_bf16(const void* q, const void* k, const void* v, const void* tq,
@@ -16,13 +17,13 @@ hipError_t launch_bf16(const void* q, const void* k, const void* v, const void* 
                        int B, int H, int Nq, int Nk, int d, float scale, void* workspace,
                        hipStream_t stream);
 
-// The two phases of launch_bf16: V/dV -> packed fp16 workspace, then the
-// fused kernel reading that workspace.
-hipError_t launch_pack_v(const void* v, const void* tv, int B, int H, int Nk, int d,
-                         void* workspace, hipStream_t stream);
-hipError_t launch_bf16_packed(const void* q, const void* k, const void* tq, const void* tk,
-                              const void* workspace, float* o, float* to, float* lse, int B,
-                              int H, int Nq, int Nk, int d, float scale, hipStream_t stream);
+// The two phases of launch_bf16: K, V, dK, dV -> tile images in the
+// workspace, then the fused kernel reading them.
+hipError_t launch_pack_kv(const void* k, const void* v, const void* tk, const void* tv, int B,
+                          int H, int Nk, int d, void* workspace, hipStream_t stream);
+hipError_t launch_bf16_packed(const void* q, const void* tq, const void* workspace, float* o,
+                              float* to, float* lse, int B, int H, int Nq, int Nk, int d,
+                              float scale, hipStream_t stream);
 
 hipError_t launch_f32(const float* q, const float* k, const float* v, const float* tq,
                       const float* tk, const float* tv, float* o, float* to, float* lse,

@@ -3,8 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step is one pass of the whole hot path over one batch of resident
-synthetic inputs: the V/dV pack kernel and the fused attention+JVP kernel,
-launched through the C ABI (attn_jvp_pack_v, attn_jvp_fwd_packed: the two
+synthetic inputs: the K/V/dK/dV pack kernel and the fused attention+JVP
+kernel, launched through the C ABI (attn_jvp_pack_kv, attn_jvp_fwd_packed: the two
 phases of attn_jvp_fwd) into preallocated outputs and workspace.  The
 default workload is the 1.3B-video-DiT shape (B=1, H=12, Nq=Nk=32760, d=128,
 bf16 inputs, fp32 outputs).  Prints ONE JSON line:
@@ -164,11 +164,10 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev_mid=None):
-        ajvp.attn_jvp_pack_v(g["v"], g["dv"], workspace=ws)
+        ajvp.attn_jvp_pack_kv(g["k"], g["v"], g["dk"], g["dv"], workspace=ws)
         if ev_mid is not None:
             ev_mid.record(stream)
-        ajvp.attn_jvp_fwd_packed(g["q"], g["k"], g["dq"], g["dk"], ws, scale=scale,
-                                 out=(o, to, lse))
+        ajvp.attn_jvp_fwd_packed(g["q"], g["dq"], ws, Nk, scale=scale, out=(o, to, lse))
 
     for _ in range(args.warmup):
         step()
@@ -222,7 +221,7 @@ def main():
             "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(),
             "kernel_ms_avg": round(kern_ms, 4),
-            "pack_v_ms_avg": round(sum(pack_ms) / len(pack_ms), 4),
+            "pack_kv_ms_avg": round(sum(pack_ms) / len(pack_ms), 4),
         },
         "kernel_source_sha256": kernel_source_hash(),
     }

@@ -47,8 +47,9 @@
  *   ATTN_JVP_EINVAL       a required pointer is NULL; B, H, Nq or Nk < 1;
  *                         `scale` is negative, NaN or infinite; the workspace
  *                         is NULL or too small
- *   ATTN_JVP_EUNSUPPORTED d is not 64 or 128, B*H exceeds 65535, or a tensor
- *                         (or the bf16 path's workspace) reaches 2^31 bytes
+ *   ATTN_JVP_EUNSUPPORTED d is not 64 or 128, B*H exceeds 65535, a tensor
+ *                         reaches 2^31 bytes, or one (b, h) slice of the bf16
+ *                         path's workspace does (Nk beyond about 1.9 million)
  *   ATTN_JVP_EALIGN       a tensor pointer is not 16-byte aligned (workspace:
  *                         256-byte aligned)
  *   ATTN_JVP_ELAUNCH      the HIP runtime rejected a launch or an allocation
@@ -101,9 +102,11 @@ ATTN_JVP_API int attn_jvp_fwd(const void *q, const void *k, const void *v,
                  attn_jvp_stream_t stream);
 
 /*
- * Bytes of workspace the bf16 path needs for these sizes (fp16 transposed
- * copies of V and dV in matrix-core tile order, padded to 64 keys); 0 if a size
- * is invalid.  Same operation as attn_jvp_fwd.
+ * Bytes of workspace the bf16 path needs for these sizes: one 64-key tile
+ * image per (b, h) and key tile, holding K and dK (bf16) and V^T and dV^T
+ * (fp16, in matrix-core operand order), each row padded, laid out byte for
+ * byte as the fused kernel holds them in LDS (72 KiB per tile at d = 128,
+ * 40 KiB at d = 64); 0 if a size is invalid.  Same operation as attn_jvp_fwd.
  */
 ATTN_JVP_API size_t attn_jvp_workspace_bytes(int B, int H, int Nk, int d);
 
@@ -122,27 +125,27 @@ ATTN_JVP_API int attn_jvp_fwd_ws(const void *q, const void *k, const void *v,
 
 /*
  * The two phases of attn_jvp_fwd_ws, for callers that schedule, time or reuse
- * them separately (one packed V/dV serves every call with the same V, dV, B,
- * H, Nk and d, e.g. several query batches against one set of keys).
+ * them separately (one packed workspace serves every call with the same K, V,
+ * dK, dV, B, H, Nk and d, e.g. several query batches against one set of keys).
  *
- * attn_jvp_pack_v converts v and tv (bf16, [B, H, Nk, d]) to the fp16 tile
- * layout of the second contraction and writes it to `workspace` (256-byte
- * aligned, at least attn_jvp_workspace_bytes(B, H, Nk, d) bytes), overwriting
- * all of it.  Errors as above (EINVAL for NULL v, tv or workspace, or a short
- * workspace).
+ * attn_jvp_pack_kv converts k, v, tk, tv (bf16, [B, H, Nk, d]) to the tile
+ * images described at attn_jvp_workspace_bytes and writes them to `workspace`
+ * (256-byte aligned, at least attn_jvp_workspace_bytes(B, H, Nk, d) bytes),
+ * overwriting all of it.  Errors as above (EINVAL for a NULL input or
+ * workspace, or a short workspace).
  *
- * attn_jvp_fwd_packed computes O, dO and lse from q, k, tq, tk and a workspace
- * that attn_jvp_pack_v filled for the same B, H, Nk, d, ordered before this
- * call (same stream, or synchronised).  The workspace is only read.  Other
+ * attn_jvp_fwd_packed computes O, dO and lse from q, tq and a workspace that
+ * attn_jvp_pack_kv filled for the same B, H, Nk, d, ordered before this call
+ * (same stream, or synchronised).  The workspace is only read.  Other
  * arguments and errors as attn_jvp_fwd.  Allocates nothing.
  */
-ATTN_JVP_API int attn_jvp_pack_v(const void *v, const void *tv,
-                    int B, int H, int Nk, int d,
-                    void *workspace, size_t workspace_bytes,
-                    attn_jvp_stream_t stream);
+ATTN_JVP_API int attn_jvp_pack_kv(const void *k, const void *v,
+                     const void *tk, const void *tv,
+                     int B, int H, int Nk, int d,
+                     void *workspace, size_t workspace_bytes,
+                     attn_jvp_stream_t stream);
 
-ATTN_JVP_API int attn_jvp_fwd_packed(const void *q, const void *k,
-                        const void *tq, const void *tk,
+ATTN_JVP_API int attn_jvp_fwd_packed(const void *q, const void *tq,
                         const void *workspace, size_t workspace_bytes,
                         float *o, float *to, float *lse,
                         int B, int H, int Nq, int Nk, int d, float scale,

@@ -51,10 +51,15 @@ def test_strerror():
 
 
 def test_workspace_bytes():
-    # fp16 V^T and dV^T, padded to 64 keys: 2 * 64 * d * 2 bytes per key tile
-    assert ajvp.attn_jvp_workspace_bytes(1, 1, 1, 128) == 2 * 64 * 128 * 2
-    assert ajvp.attn_jvp_workspace_bytes(1, 12, 32760, 128) == 12 * 512 * 2 * 64 * 128 * 2
-    assert ajvp.attn_jvp_workspace_bytes(2, 3, 65, 64) == 6 * 2 * 2 * 64 * 64 * 2
+    # one tile image per (b, h) and 64-key tile: K, dK rows of 2d + 16 bytes,
+    # V^T, dV^T rows of 64 * 2 + 16 bytes, rounded up to 8 KiB
+    def img(d):
+        used = 2 * 64 * (2 * d + 16) + 2 * d * (2 * 64 + 16)
+        return -(-used // 8192) * 8192
+    assert img(128) == 72 * 1024 and img(64) == 40 * 1024
+    assert ajvp.attn_jvp_workspace_bytes(1, 1, 1, 128) == img(128)
+    assert ajvp.attn_jvp_workspace_bytes(1, 12, 32760, 128) == 12 * 512 * img(128)
+    assert ajvp.attn_jvp_workspace_bytes(2, 3, 65, 64) == 6 * 2 * img(64)
     assert ajvp.attn_jvp_workspace_bytes(0, 1, 1, 128) == 0
     assert ajvp.attn_jvp_workspace_bytes(1, 1, 1, 96) == 0
 
@@ -140,48 +145,52 @@ def test_workspace_checks():
     assert _call("attn_jvp_fwd_ws", ws=A + 0x1000000 + 16) == EALIGN
 
 
-def _pack(v=A, tv=A + 0x100000, B=1, H=1, Nk=4, d=128, ws=A + 0x1000000, ws_bytes=None):
+def _pack(k=A, v=A + 0x100000, tk=A + 0x200000, tv=A + 0x300000, B=1, H=1, Nk=4, d=128,
+          ws=A + 0x1000000, ws_bytes=None):
     nb = ajvp.attn_jvp_workspace_bytes(max(B, 1), max(H, 1), max(Nk, 1), d)
-    return ajvp.lib().attn_jvp_pack_v(
-        ctypes.c_void_p(v), ctypes.c_void_p(tv), B, H, Nk, d, ctypes.c_void_p(ws),
-        ctypes.c_size_t(nb if ws_bytes is None else ws_bytes), ctypes.c_void_p(0))
+    return ajvp.lib().attn_jvp_pack_kv(
+        ctypes.c_void_p(k), ctypes.c_void_p(v), ctypes.c_void_p(tk), ctypes.c_void_p(tv), B, H,
+        Nk, d, ctypes.c_void_p(ws), ctypes.c_size_t(nb if ws_bytes is None else ws_bytes),
+        ctypes.c_void_p(0))
 
 
 def _packed(ptrs=None, B=1, H=1, Nq=4, Nk=4, d=128, scale=0.1, ws=A + 0x1000000,
             ws_bytes=None):
-    p = [A + i * 0x100000 for i in range(7)] if ptrs is None else ptrs  # q k tq tk o to lse
+    p = [A + i * 0x100000 for i in range(5)] if ptrs is None else ptrs  # q tq o to lse
     nb = ajvp.attn_jvp_workspace_bytes(max(B, 1), max(H, 1), max(Nk, 1), d)
     return ajvp.lib().attn_jvp_fwd_packed(
-        *[ctypes.c_void_p(x) for x in p[:4]], ctypes.c_void_p(ws),
+        *[ctypes.c_void_p(x) for x in p[:2]], ctypes.c_void_p(ws),
         ctypes.c_size_t(nb if ws_bytes is None else ws_bytes),
-        *[ctypes.c_void_p(x) for x in p[4:]], B, H, Nq, Nk, d, ctypes.c_float(scale),
+        *[ctypes.c_void_p(x) for x in p[2:]], B, H, Nq, Nk, d, ctypes.c_float(scale),
         ctypes.c_void_p(0))
 
 
-def test_pack_v_rejects_bad_arguments():
-    assert _pack(v=0) == EINVAL and _pack(tv=0) == EINVAL and _pack(ws=0) == EINVAL
+def test_pack_kv_rejects_bad_arguments():
+    assert _pack(k=0) == EINVAL and _pack(v=0) == EINVAL and _pack(tk=0) == EINVAL
+    assert _pack(tv=0) == EINVAL and _pack(ws=0) == EINVAL
     assert _pack(ws_bytes=100) == EINVAL
     assert _pack(B=0) == EINVAL and _pack(Nk=0) == EINVAL
     assert _pack(d=96) == EUNSUPPORTED and _pack(Nk=1 << 24) == EUNSUPPORTED
     assert _pack(B=1 << 16) == EUNSUPPORTED
-    assert _pack(v=A + 4) == EALIGN and _pack(tv=A + 8) == EALIGN
+    assert _pack(k=A + 4) == EALIGN and _pack(v=A + 0x100000 + 8) == EALIGN
+    assert _pack(tk=A + 0x200000 + 2) == EALIGN and _pack(tv=A + 0x300000 + 8) == EALIGN
     assert _pack(ws=A + 0x1000000 + 16) == EALIGN
 
 
 def test_fwd_packed_rejects_bad_arguments():
-    for i in range(6):  # q k tq tk o to (lse may be NULL)
-        p = [A + j * 0x100000 for j in range(7)]
+    for i in range(4):  # q tq o to (lse may be NULL)
+        p = [A + j * 0x100000 for j in range(5)]
         p[i] = 0
         assert _packed(p) == EINVAL, i
     assert _packed(ws=0) == EINVAL and _packed(ws_bytes=100) == EINVAL
     assert _packed(scale=-1.0) == EINVAL and _packed(scale=float("nan")) == EINVAL
     assert _packed(Nq=0) == EINVAL
     assert _packed(d=64 + 1) == EUNSUPPORTED and _packed(Nk=1 << 24) == EUNSUPPORTED
-    for i in range(6):
-        p = [A + j * 0x100000 for j in range(7)]
+    for i in range(4):
+        p = [A + j * 0x100000 for j in range(5)]
         p[i] += 4
         assert _packed(p) == EALIGN, i
-    p = [A + j * 0x100000 for j in range(7)]
-    p[6] += 2
+    p = [A + j * 0x100000 for j in range(5)]
+    p[4] += 2
     assert _packed(p) == EALIGN
     assert _packed(ws=A + 0x1000000 + 64) == EALIGN

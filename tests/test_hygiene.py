@@ -106,18 +106,20 @@ def test_python_binding_validation():
     with pytest.raises(ValueError):
         ajvp.attn_jvp_fwd(*[g[n] for n in NAMES], workspace=torch.empty(1 << 20, dtype=torch.uint8))
     with pytest.raises(ValueError):
-        ajvp.attn_jvp_pack_v(g["v"], g["dv"], workspace=torch.empty(1 << 20, dtype=torch.uint8))
+        ajvp.attn_jvp_pack_kv(g["k"], g["v"], g["dk"], g["dv"],
+                              workspace=torch.empty(1 << 20, dtype=torch.uint8))
 
 
 def test_two_phases_match_fused_and_packed_workspace_is_reusable():
-    """attn_jvp_pack_v + attn_jvp_fwd_packed == attn_jvp_fwd bit for bit; one
-    packed V/dV serves two query batches of different lengths."""
+    """attn_jvp_pack_kv + attn_jvp_fwd_packed == attn_jvp_fwd bit for bit; one
+    packed K/V/dK/dV serves two query batches of different lengths."""
     g, s = _inputs()
     ref = ajvp.attn_jvp_fwd(*[g[n] for n in NAMES], scale=s)
-    ws = ajvp.attn_jvp_pack_v(g["v"], g["dv"])
-    got = ajvp.attn_jvp_fwd_packed(g["q"], g["k"], g["dq"], g["dk"], ws, scale=s)
+    ws = ajvp.attn_jvp_pack_kv(g["k"], g["v"], g["dk"], g["dv"])
+    Nk = g["k"].shape[2]
+    got = ajvp.attn_jvp_fwd_packed(g["q"], g["dq"], ws, Nk, scale=s)
     q2, dq2 = g["q"][:, :, :97].contiguous(), g["dq"][:, :, :97].contiguous()
-    got2 = ajvp.attn_jvp_fwd_packed(q2, g["k"], dq2, g["dk"], ws, scale=s)
+    got2 = ajvp.attn_jvp_fwd_packed(q2, dq2, ws, Nk, scale=s)
     torch.cuda.synchronize()
     for a, b in zip(ref, got):
         assert torch.equal(a, b)
