@@ -160,24 +160,25 @@ __device__ __attribute__((always_inline)) inline int slot_key(int r, int g) {
 // Online-softmax order: the accumulators hold sums normalised to the running
 // max m; a raised max rescales them by alpha = 2^(m_old - m_new) before this
 // block's P V is added.
-template <int D, bool kMask>
+template <int D, bool kMask, typename Issue>
 __device__ __attribute__((always_inline)) inline void jvp_block(
     RowState<D>& st, const char* stage, int kb, const u32x4* qf, const u32x4* dqf, int l32,
-    int g, int key0, int Nk, float c_log2, float scale) {
+    int g, int key0, int Nk, float c_log2, float scale, Issue issue) {
   using G = Geo<D>;
   const char* sK = stage;
   const char* sdK = stage + G::kKTile;
   const char* sV = stage + 2 * G::kKTile;
   const char* sdV = sV + G::kVTile;
 
-  // S^T and dS^T (rows: key, columns: this wave's queries)
-  // Scheduling barriers keep the compiler from hoisting operand reads (and
-  // their registers) across steps; the other wave on the SIMD covers the LDS
-  // latency.
+  // S^T and dS^T (rows: key, columns: this wave's queries).  The K and dK
+  // fragments are read at their own step (the other wave on the SIMD covers
+  // the LDS latency); scheduling barriers keep the compiler from hoisting
+  // reads, and their registers, across steps.
   const int krow = (32 * kb + l32) * G::kKRow + 16 * g;
   f32x16 s, ds;
 #pragma unroll
   for (int ks = 0; ks < G::kKS; ++ks) {
+    issue(ks);
     const u32x4 kf = lds_load16(sK + krow + 32 * ks);
     const u32x4 dkf = lds_load16(sdK + krow + 32 * ks);
     s = mma_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s);
@@ -243,35 +244,49 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
 
   __builtin_amdgcn_sched_barrier(0);
 
-  // A^T += V^T P^T, G^T += V^T (s P dS)^T + dV^T P^T; step = (t, cb)
+  // A^T += V^T P^T, G^T += V^T (s P dS)^T + dV^T P^T; step = (t, cb), its
+  // V^T and dV^T fragments read one step ahead (S and dS are dead by now, so
+  // the prefetch registers come free)
   constexpr int kSteps = 2 * G::kCB;
   auto voff = [&](int step) {
     const int t = step / G::kCB, cb = step % G::kCB;
     return (32 * cb + l32) * G::kVRow + 16 * g + 16 * (4 * kb + 2 * t);
   };
+  u32x4 vf[2], dvf[2];
+  vf[0] = lds_load16(sV + voff(0));
+  dvf[0] = lds_load16(sdV + voff(0));
 #pragma unroll
   for (int step = 0; step < kSteps; ++step) {
     const int t = step / G::kCB, cb = step % G::kCB;
-    const u32x4 vf = lds_load16(sV + voff(step));
-    const u32x4 dvf = lds_load16(sdV + voff(step));
-    st.accA[cb] = mma_f16(vf, p[t], st.accA[cb]);
-    st.accG[cb] = mma_f16(vf, pd[t], st.accG[cb]);
-    st.accG[cb] = mma_f16(dvf, p[t], st.accG[cb]);
+    issue(G::kKS + step);
+    if (step + 1 < kSteps) {
+      vf[(step + 1) & 1] = lds_load16(sV + voff(step + 1));
+      dvf[(step + 1) & 1] = lds_load16(sdV + voff(step + 1));
+    }
+    st.accA[cb] = mma_f16(vf[step & 1], p[t], st.accA[cb]);
+    st.accG[cb] = mma_f16(vf[step & 1], pd[t], st.accG[cb]);
+    st.accG[cb] = mma_f16(dvf[step & 1], p[t], st.accG[cb]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// One full tile: the copy of the next tile image into `next` is issued first,
-// then both 32-key blocks are computed from `cur`.  The two stage pointers are
-// restrict-qualified (they name disjoint halves of the LDS), which tells the
-// compiler that reads of `cur` need not wait for the copy into `next`.
+// One full tile: the copy of the next tile image into `next` is spread over
+// the first steps of the first block (copy instruction j at step j, so the
+// copy queue holds one load per wave at a time), while both 32-key blocks are
+// computed from `cur`.  The two stage pointers are restrict-qualified (they
+// name disjoint halves of the LDS), which tells the compiler that reads of
+// `cur` need not wait for the copy into `next`.
 template <int D, typename Copy>
 __device__ __attribute__((always_inline)) inline void tile_step(
     char* __restrict__ next, const char* __restrict__ cur, Copy copy, RowState<D>& st,
     const u32x4* qf, const u32x4* dqf, int l32, int g, int Nk, float c_log2, float scale) {
-  copy(next);
-  jvp_block<D, false>(st, cur, 0, qf, dqf, l32, g, 0, Nk, c_log2, scale);
-  jvp_block<D, false>(st, cur, 1, qf, dqf, l32, g, 0, Nk, c_log2, scale);
+  using G = Geo<D>;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+    jvp_block<D, false>(st, cur, kb, qf, dqf, l32, g, 0, Nk, c_log2, scale,
+                        [&](int slot) {
+                          if (kb == 0 && slot < G::kDmaPerWave) copy(next, slot);
+                        });
 }
 
 // Sizes of the whole tensors (bytes) the kernel may touch; each global access
@@ -313,14 +328,15 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
   // KiB, lane l moving bytes 16 l .. 16 l + 15 of each (LDS address = the
   // wave-uniform stage pointer + 16 l; global = image offset + 16 l).
   const uint32_t wave_part = (uint32_t)wave * G::kDmaPerWave * kDmaBytes;
-  auto copy_tile = [&](int kt, char* stage) {
-    const uint32_t src = (uint32_t)kt * G::kImgBytes + wave_part;
-#pragma unroll
-    for (int j = 0; j < G::kDmaPerWave; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rimg, (lds_ptr_t)(stage + wave_part + j * kDmaBytes),
-                                               16, lane * 16, src + j * kDmaBytes, 0, 0);
+  auto copy_one = [&](int kt, char* stage, int j) {
+    const uint32_t src = (uint32_t)kt * G::kImgBytes + wave_part + j * kDmaBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rimg, (lds_ptr_t)(stage + wave_part + j * kDmaBytes),
+                                             16, lane * 16, src, 0, 0);
   };
-
+  auto copy_tile = [&](int kt, char* stage) {
+#pragma unroll
+    for (int j = 0; j < G::kDmaPerWave; ++j) copy_one(kt, stage, j);
+  };
   copy_tile(0, smem);
 
   // Q and dQ fragments: the B operand of S^T = K Q^T (lane: row l32, d-slice g).
@@ -356,7 +372,7 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
   finish_tile();
   for (int kt = 0; kt < kLast; ++kt) {
     tile_step<D>(smem + ((kt + 1) & 1) * G::kImgBytes, smem + (kt & 1) * G::kImgBytes,
-                 [&](char* next) { copy_tile(kt + 1, next); }, st, qf, dqf, l32, g, Nk,
+                 [&](char* next, int j) { copy_one(kt + 1, next, j); }, st, qf, dqf, l32, g, Nk,
                  c_log2, scale);
     finish_tile();
   }
@@ -364,8 +380,9 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
   {
     const char* cur = smem + (kLast & 1) * G::kImgBytes;
     const int kl = kLast * kBC;
-    jvp_block<D, true>(st, cur, 0, qf, dqf, l32, g, kl, Nk, c_log2, scale);
-    jvp_block<D, true>(st, cur, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, scale);
+    auto none = [](int) {};
+    jvp_block<D, true>(st, cur, 0, qf, dqf, l32, g, kl, Nk, c_log2, scale, none);
+    jvp_block<D, true>(st, cur, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, scale, none);
   }
 
   // ---- epilogue: O = A / l, mu = u / l, dO = G / l - mu O, lse ----

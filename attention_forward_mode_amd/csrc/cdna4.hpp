@@ -87,14 +87,16 @@ __device__ inline float add_f16x2(uint32_t h, float acc) {
 // Value held by lane (l ^ 32): the other half of a 64-wide wave.
 __device__ inline float swap_halves(float x) { return __shfl_xor(x, 32); }
 
-// max / sum of x over lanes l and l ^ 32, in every lane.  v_permlane32_swap
-// exchanges the upper half of its first operand with the lower half of its
-// second; with both set to x the two results hold x of the lower and of the
-// upper half respectively, in every lane (a vector-ALU op, no LDS traffic).
+// max / sum of x over lanes l and l ^ 32, in every lane (the max propagates
+// NaN).  v_permlane32_swap exchanges the upper half of its first operand with
+// the lower half of its second; with both set to x the two results hold x of
+// the lower and of the upper half respectively, in every lane (a vector-ALU
+// op, no LDS traffic).
 __device__ inline float halves_max(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  return __builtin_elementwise_maximum(__builtin_bit_cast(float, (unsigned)r[0]),
+                                       __builtin_bit_cast(float, (unsigned)r[1]));
 }
 __device__ inline float halves_sum(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
