@@ -9,6 +9,11 @@ device memory and the current stream.  The names mirror the C entry points:
     attn_jvp_pack_kv(k, v, tk, tv, workspace=None) -> workspace
     attn_jvp_fwd_packed(q, tq, workspace, Nk, ...) -> (o, to, lse)
         the two phases of attn_jvp_fwd, callable separately
+    attn_jvp_fwd_ex(q, k, v, tq=None, tk=None, tv=None, ...) -> (o, to, lse, tlse)
+        NULL (None) tangents, the tangent of lse, fp32 or bf16 outputs
+    attn_fwd(q, k, v, ...) -> (o, lse)    forward attention alone
+    attn_jvp_merge(lse_parts, o_parts, to_parts=None, tlse_parts=None)
+        -> (lse, o, to, tlse): combine results over disjoint key subsets
     attn_jvp_fwd_f32(...)  the same with fp32 inputs
     attn_jvp_workspace_bytes(B, H, Nk, d)
     attn_jvp_strerror(status)
@@ -27,7 +32,8 @@ import os
 
 import torch
 
-__all__ = ["attn_jvp_fwd", "attn_jvp_pack_kv", "attn_jvp_fwd_packed", "attn_jvp_fwd_f32", "attn_jvp_workspace_bytes",
+__all__ = ["attn_jvp_fwd", "attn_jvp_pack_kv", "attn_jvp_fwd_packed", "attn_jvp_fwd_ex", "attn_fwd",
+           "attn_jvp_merge", "attn_jvp_fwd_f32", "attn_jvp_workspace_bytes",
            "attn_jvp_strerror", "AttnJvpError", "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_jvp.so")
@@ -57,6 +63,12 @@ def lib():
     L.attn_jvp_pack_kv.restype = _i
     L.attn_jvp_fwd_packed.argtypes = [_vp] * 3 + [_sz] + [_vp] * 3 + [_i] * 5 + [_f, _vp]
     L.attn_jvp_fwd_packed.restype = _i
+    L.attn_jvp_fwd_ex.argtypes = [_vp] * 10 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
+    L.attn_jvp_fwd_ex.restype = _i
+    L.attn_fwd.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
+    L.attn_fwd.restype = _i
+    L.attn_jvp_merge.argtypes = [_vp] * 4 + [_i] * 3 + [_vp] * 5
+    L.attn_jvp_merge.restype = _i
     L.attn_jvp_fwd_f32.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _vp]
     L.attn_jvp_fwd_f32.restype = _i
     L.attn_jvp_workspace_bytes.argtypes = [_i, _i, _i, _i]
@@ -68,6 +80,7 @@ def lib():
 
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, ELAUNCH = 0, -1, -2, -3, -4
+OUT_F32, OUT_BF16 = 0, 1
 
 
 class AttnJvpError(RuntimeError):
@@ -206,6 +219,111 @@ def attn_jvp_fwd(q, k, v, tq, tk, tv, scale=None, lse=True, out=None, workspace=
     if rc != OK:
         raise AttnJvpError(rc)
     return o, to, lse_t
+
+
+def _out_code(out_dtype):
+    if out_dtype == torch.float32:
+        return OUT_F32
+    if out_dtype == torch.bfloat16:
+        return OUT_BF16
+    raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+
+
+def _check_opt(t, like, name):
+    """An optional tangent: None, or a tensor exactly like its primal."""
+    if t is None:
+        return
+    if (not isinstance(t, torch.Tensor) or t.dtype != like.dtype or t.shape != like.shape
+            or t.device != like.device or not t.is_contiguous()):
+        raise ValueError(f"{name} must be None or a contiguous tensor like its primal")
+
+
+def _ws_arg(workspace, device):
+    if workspace is None:
+        return None, 0
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return _ptr(workspace), _nbytes(workspace)
+
+
+def attn_jvp_fwd_ex(q, k, v, tq=None, tk=None, tv=None, scale=None, lse=True, tlse=True,
+                    out_dtype=torch.float32, workspace=None):
+    """bf16 attention + JVP with optional tangents (None = zero; tk = tv = None
+    runs the frozen-key kernel), the tangent of lse, and fp32 or bf16 outputs.
+    Returns (o, to, lse, tlse); lse / tlse are None when not requested.  With
+    workspace=None the library's stream-ordered pool provides it."""
+    B, H, Nq, Nk, d = _check(q, k, v, q, k, v, torch.bfloat16)
+    _check_opt(tq, q, "tq")
+    _check_opt(tk, k, "tk")
+    _check_opt(tv, v, "tv")
+    code = _out_code(out_dtype)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    to = torch.empty_like(o)
+    lse_t = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse else None
+    tlse_t = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if tlse else None
+    wp, wb = _ws_arg(workspace, q.device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_jvp_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                                   _ptr(o), _ptr(to), _ptr(lse_t), _ptr(tlse_t), B, H, Nq, Nk, d,
+                                   s, code, wp, wb, stream)
+    if rc != OK:
+        raise AttnJvpError(rc)
+    return o, to, lse_t, tlse_t
+
+
+def attn_fwd(q, k, v, scale=None, lse=True, out_dtype=torch.float32, workspace=None):
+    """Forward attention alone (bf16 inputs): returns (o, lse)."""
+    B, H, Nq, Nk, d = _check(q, k, v, q, k, v, torch.bfloat16)
+    code = _out_code(out_dtype)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    lse_t = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse else None
+    wp, wb = _ws_arg(workspace, q.device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Nq, Nk, d, s,
+                            code, wp, wb, stream)
+    if rc != OK:
+        raise AttnJvpError(rc)
+    return o, lse_t
+
+
+def attn_jvp_merge(lse_parts, o_parts, to_parts=None, tlse_parts=None):
+    """Merge P partial results over disjoint key subsets.  lse_parts [P, *rows],
+    o_parts [P, *rows, d] (fp32, contiguous, on the GPU), to_parts / tlse_parts
+    like them or both None.  Returns (lse, o, to, tlse) with the part axis
+    removed (to, tlse None for a forward-only merge)."""
+    for name, t in (("lse_parts", lse_parts), ("o_parts", o_parts), ("to_parts", to_parts),
+                    ("tlse_parts", tlse_parts)):
+        if t is None and name in ("to_parts", "tlse_parts"):
+            continue
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 GPU tensor")
+    if (to_parts is None) != (tlse_parts is None):
+        raise ValueError("to_parts and tlse_parts go together")
+    P = lse_parts.shape[0]
+    rows = tuple(lse_parts.shape[1:])
+    d = o_parts.shape[-1]
+    if tuple(o_parts.shape) != (P, *rows, d):
+        raise ValueError("o_parts must be [P, *rows, d] matching lse_parts")
+    if to_parts is not None and (to_parts.shape != o_parts.shape or tlse_parts.shape != lse_parts.shape):
+        raise ValueError("to_parts / tlse_parts must match o_parts / lse_parts")
+    R = int(math.prod(rows))
+    dev = lse_parts.device
+    lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    o = torch.empty((*rows, d), dtype=torch.float32, device=dev)
+    to = torch.empty_like(o) if to_parts is not None else None
+    tlse = torch.empty_like(lse) if to_parts is not None else None
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    with torch.cuda.device(dev):
+        rc = lib().attn_jvp_merge(_ptr(lse_parts), _ptr(o_parts), _ptr(to_parts), _ptr(tlse_parts),
+                                  P, R, d, _ptr(lse), _ptr(o), _ptr(to), _ptr(tlse), stream)
+    if rc != OK:
+        raise AttnJvpError(rc)
+    return lse, o, to, tlse
 
 
 def attn_jvp_fwd_f32(q, k, v, tq, tk, tv, scale=None, lse=True, out=None):

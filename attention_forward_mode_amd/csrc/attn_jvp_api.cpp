@@ -18,6 +18,7 @@ namespace {
 // descriptors spanning the whole tensor), and B*H is the grid's y extent.
 constexpr int64_t kMaxTensorBytes = int64_t(1) << 31;
 constexpr int64_t kMaxSlices = 65535;
+constexpr int kMaxMergeParts = 1024;
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -92,6 +93,29 @@ hipError_t device_pool(hipMemPool_t* out) {
   *out = g_pool[dev];
   return hipSuccess;
 }
+
+// Runs `launch(ws)` with the caller's workspace (checked) or, when it is NULL,
+// with one taken from the device pool and returned stream-ordered.
+template <typename Launch>
+int with_workspace(void* workspace, size_t workspace_bytes, int B, int H, int Nk, int d,
+                   hipStream_t st, Launch launch) {
+  if (workspace != nullptr) {
+    const int rc = check_workspace(workspace, workspace_bytes, B, H, Nk, d);
+    if (rc != ATTN_JVP_OK) return rc;
+    return launch(workspace) == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+  }
+  hipMemPool_t pool = nullptr;
+  if (device_pool(&pool) != hipSuccess) return ATTN_JVP_ELAUNCH;
+  void* ws = nullptr;
+  if (hipMallocFromPoolAsync(&ws, ajvp::bf16_workspace_bytes(B, H, Nk, d), pool, st) !=
+      hipSuccess)
+    return ATTN_JVP_ELAUNCH;
+  const hipError_t e = launch(ws);
+  const hipError_t f = hipFreeAsync(ws, st);
+  return (e == hipSuccess && f == hipSuccess) ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+}
+
+bool bad_out_dtype(int t) { return t != ATTN_JVP_OUT_F32 && t != ATTN_JVP_OUT_BF16; }
 
 }  // namespace
 
@@ -170,6 +194,65 @@ int attn_jvp_fwd(const void* q, const void* k, const void* v, const void* tq, co
   hipError_t e = ajvp::launch_bf16(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, d, scale, ws, st);
   hipError_t f = hipFreeAsync(ws, st);
   return (e == hipSuccess && f == hipSuccess) ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+}
+
+int attn_jvp_fwd_ex(const void* q, const void* k, const void* v, const void* tq, const void* tk,
+                    const void* tv, void* o, void* to, float* lse, float* tlse, int B, int H,
+                    int Nq, int Nk, int d, float scale, int out_dtype, void* workspace,
+                    size_t workspace_bytes, attn_jvp_stream_t stream) {
+  const void* in[3] = {q, k, v};
+  int rc = validate(in, 3, static_cast<float*>(o), static_cast<float*>(to), lse, B, H, Nq, Nk, d,
+                    scale, 2);
+  if (rc != ATTN_JVP_OK) return rc;
+  if (bad_out_dtype(out_dtype)) return ATTN_JVP_EINVAL;
+  const void* tan[3] = {tq, tk, tv};
+  for (const void* t : tan)
+    if (t != nullptr && misaligned(t, 16)) return ATTN_JVP_EALIGN;
+  if (tlse != nullptr && misaligned(tlse, 4)) return ATTN_JVP_EALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return with_workspace(workspace, workspace_bytes, B, H, Nk, d, st, [&](void* ws) {
+    return ajvp::launch_bf16_ex(q, k, v, tq, tk, tv, o, to, lse, tlse, B, H, Nq, Nk, d, scale,
+                                out_dtype == ATTN_JVP_OUT_BF16, ws, st);
+  });
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int Nq, int Nk, int d, float scale, int out_dtype, void* workspace,
+             size_t workspace_bytes, attn_jvp_stream_t stream) {
+  const void* in[3] = {q, k, v};
+  if (o == nullptr) return ATTN_JVP_EINVAL;
+  // validate() also wants a tangent output; o stands in for it here
+  int rc = validate(in, 3, static_cast<float*>(o), static_cast<float*>(o), lse, B, H, Nq, Nk, d,
+                    scale, 2);
+  if (rc != ATTN_JVP_OK) return rc;
+  if (bad_out_dtype(out_dtype)) return ATTN_JVP_EINVAL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return with_workspace(workspace, workspace_bytes, B, H, Nk, d, st, [&](void* ws) {
+    return ajvp::launch_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale,
+                            out_dtype == ATTN_JVP_OUT_BF16, ws, st);
+  });
+}
+
+int attn_jvp_merge(const float* lse_parts, const float* o_parts, const float* to_parts,
+                   const float* tlse_parts, int P, int R, int d, float* lse, float* o, float* to,
+                   float* tlse, attn_jvp_stream_t stream) {
+  if (lse_parts == nullptr || o_parts == nullptr || o == nullptr) return ATTN_JVP_EINVAL;
+  const bool tan = to_parts != nullptr;
+  if (tan != (tlse_parts != nullptr) || tan != (to != nullptr)) return ATTN_JVP_EINVAL;
+  if (!tan && tlse != nullptr) return ATTN_JVP_EINVAL;
+  if (P < 1 || R < 1) return ATTN_JVP_EINVAL;
+  if (d != 64 && d != 128) return ATTN_JVP_EUNSUPPORTED;
+  if (P > kMaxMergeParts || int64_t(P) * R * d * 4 >= kMaxTensorBytes)
+    return ATTN_JVP_EUNSUPPORTED;
+  const void* al16[4] = {o_parts, to_parts, o, to};
+  for (const void* p : al16)
+    if (p != nullptr && misaligned(p, 16)) return ATTN_JVP_EALIGN;
+  const void* al4[4] = {lse_parts, tlse_parts, lse, tlse};
+  for (const void* p : al4)
+    if (p != nullptr && misaligned(p, 4)) return ATTN_JVP_EALIGN;
+  const hipError_t e = ajvp::launch_merge(lse_parts, o_parts, to_parts, tlse_parts, P, R, d, lse,
+                                          o, to, tlse, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
 }
 
 int attn_jvp_fwd_f32(const float* q, const float* k, const float* v, const float* tq,

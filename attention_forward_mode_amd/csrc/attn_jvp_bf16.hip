@@ -4,7 +4,8 @@
 // takeaways", "JVP at production scale", paper §3.2 / App. C: FlashAttention-2
 // and its Jacobian-vector product in one tiled pass):
 //   O = softmax(s Q K^T) V,  dO = (P * (dS - mu)) V + P dV,
-//   dS = s (dQ K^T + Q dK^T),  mu = rowsum(P * dS),  lse = ln rowsum exp(s Q K^T).
+//   dS = s (dQ K^T + Q dK^T),  mu = rowsum(P * dS),  lse = ln rowsum exp(s Q K^T),
+//   and mu is also the tangent of lse.
 //
 // Two kernels per call:
 //  1. pack_kv: K, dK, V, dV -> one "tile image" per 64 keys in the workspace,
@@ -31,6 +32,14 @@
 //  The running max is only raised when a block's max exceeds it by more than
 //  kTau (log2 units): results are exact either way, p stays <= 2^kTau, and the
 //  accumulator rescale is skipped on most blocks.
+//
+// Three modes share that body:
+//  kFull    the JVP along (dQ, dK, dV); a NULL tangent reads as zeros;
+//  kFrozen  the JVP with dK = dV = 0 (e.g. frozen text keys of cross-attention):
+//           the products with dK and dV and their tiles are left out (4 of the
+//           6 contractions remain);
+//  kFwd     the forward pass alone (O, lse: 2 contractions).
+// Outputs O and dO are written in fp32 or bf16 (round to nearest even).
 #include "cdna4.hpp"
 #include "launch.hpp"
 
@@ -45,8 +54,18 @@ constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
 constexpr int kPackThreads = 256;
 constexpr float kTau = 4.0f;        // lazy-rescale headroom, log2 units
 constexpr int kDmaBytes = 1024;     // one LDS-direct load: 64 lanes x 16 bytes
+constexpr uint32_t kXcds = 8;       // accelerator dies (each with its own L2) on MI355X
 
-template <int D>
+enum : int { kFull = 0, kFrozen = 1, kFwd = 2 };
+template <int kMode>
+struct Mode {
+  static constexpr bool kTan = kMode != kFwd;  // the tangent is computed
+  static constexpr bool kKV = kMode == kFull;  // dK and dV take part
+};
+
+// Tile image of 64 keys: K | dK | V^T | dV^T (without dK and dV when kKV is
+// false), rounded up to a whole number of workgroup-wide copy rounds.
+template <int D, bool kKV>
 struct Geo {
   // LDS rows are padded by 16 bytes: the 16 rows that one phase of a 16-byte
   // matrix-operand read touches then start 16 bytes apart modulo the bank
@@ -56,15 +75,20 @@ struct Geo {
   static constexpr int kVRow = kBC * 2 + 16;              // V^T, dV^T: D rows of 64 keys
   static constexpr int kKTile = kBC * kKRow;
   static constexpr int kVTile = D * kVRow;
-  static constexpr int kImgUsed = 2 * kKTile + 2 * kVTile;  // K | dK | V^T | dV^T
-  // The image is a whole number of workgroup-wide copy rounds (8 KiB each).
-  static constexpr int kRound = kThreads * 16;
+  static constexpr int kNT = kKV ? 2 : 1;                 // tiles per kind
+  static constexpr int kOffdK = kKTile;
+  static constexpr int kOffV = kNT * kKTile;
+  static constexpr int kOffdV = kOffV + kVTile;
+  static constexpr int kImgUsed = kNT * (kKTile + kVTile);
+  static constexpr int kRound = kThreads * 16;            // 8 KiB
   static constexpr int kImgBytes = (kImgUsed + kRound - 1) / kRound * kRound;
   static constexpr int kDmaPerWave = kImgBytes / (kWaves * kDmaBytes);
   static constexpr int kKS = D / 16;                      // contraction steps over d
   static constexpr int kCB = D / 32;                      // 32-column output blocks
 };
-static_assert(Geo<128>::kImgBytes == 73728 && Geo<64>::kImgBytes == 40960, "tile image size");
+static_assert(Geo<128, true>::kImgBytes == 73728 && Geo<64, true>::kImgBytes == 40960 &&
+                  Geo<128, false>::kImgBytes == 40960 && Geo<64, false>::kImgBytes == 24576,
+              "tile image sizes");
 
 // Key held at position `pos` (0..63) of a packed V^T row.  Positions
 // 16G + 8g + e hold the keys that the S^T accumulator of lane half g puts in
@@ -75,22 +99,24 @@ __device__ inline int packed_key(int pos) {
   return 16 * G + (e < 4 ? 4 * g + e : 8 + 4 * g + (e - 4));
 }
 
-// One tile image: blockIdx.x = 64-key tile, blockIdx.y = (b, h) slice.
-template <int D>
+// One tile image: blockIdx.x = 64-key tile, blockIdx.y = (b, h) slice.  A NULL
+// dk or dv gets an empty descriptor, so its part of the image is zero.
+template <int D, bool kKV>
 __device__ __attribute__((always_inline)) inline void pack_kv_body(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dk, const uint16_t* __restrict__ dv, char* __restrict__ ws,
     int Nk, int ntiles, uint32_t kv_bytes) {
-  using G = Geo<D>;
-  __shared__ _Float16 sv[2][kBC][D + 2];
+  using G = Geo<D, kKV>;
+  constexpr int kT = G::kNT;
+  __shared__ _Float16 sv[kT][kBC][D + 2];
   const int tile = blockIdx.x;
   const uint32_t bh = blockIdx.y;
   // Every global access goes through a buffer descriptor spanning the whole
   // tensor: an offset outside it is dropped (stores) or reads zero (loads).
   const auto rk = make_rsrc(k, kv_bytes);
-  const auto rdk = make_rsrc(dk, kv_bytes);
+  const auto rdk = make_rsrc(dk, dk != nullptr ? kv_bytes : 0u);
   const auto rv = make_rsrc(v, kv_bytes);
-  const auto rdv = make_rsrc(dv, kv_bytes);
+  const auto rdv = make_rsrc(dv, dv != nullptr ? kv_bytes : 0u);
   // the workspace descriptor spans this (b, h) slice's images only
   const uint32_t slice_bytes = (uint32_t)ntiles * G::kImgBytes;
   const auto rws = make_rsrc(ws + (size_t)bh * slice_bytes, slice_bytes);
@@ -100,19 +126,19 @@ __device__ __attribute__((always_inline)) inline void pack_kv_body(
   constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
   // K, dK: rows copied with a zero pad chunk after each; keys >= Nk are zero.
   constexpr int kKChunks = kBC * (kChunksPerRow + 1);
-  for (int c = threadIdx.x; c < 2 * kKChunks; c += kPackThreads) {
+  for (int c = threadIdx.x; c < kT * kKChunks; c += kPackThreads) {
     const int t = c / kKChunks, rem = c % kKChunks;
     const int r = rem / (kChunksPerRow + 1), col = rem % (kChunksPerRow + 1);
     const int key = key0 + r;
     u32x4 x = kZero;
     if (col < kChunksPerRow && key < Nk)
       x = buf_load16(t == 0 ? rk : rdk, ((bh * (uint32_t)Nk + key) * D + 8 * col) * 2);
-    buf_store16(rws, img + t * G::kKTile + r * G::kKRow + col * 16, x);
+    buf_store16(rws, img + t * G::kOffdK + r * G::kKRow + col * 16, x);
   }
   // V, dV: to fp16 in LDS, then written transposed ([d][64 keys], keys in
   // packed_key order) with a zero pad chunk after each row.
   constexpr int kIn = kBC * kChunksPerRow;
-  for (int c = threadIdx.x; c < 2 * kIn; c += kPackThreads) {
+  for (int c = threadIdx.x; c < kT * kIn; c += kPackThreads) {
     const int t = c / kIn, rem = c % kIn, r = rem / kChunksPerRow, col = (rem % kChunksPerRow) * 8;
     const int key = key0 + r;
     u32x4 x = kZero;
@@ -124,7 +150,7 @@ __device__ __attribute__((always_inline)) inline void pack_kv_body(
     }
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < 2 * D * 9; c += kPackThreads) {
+  for (int c = threadIdx.x; c < kT * D * 9; c += kPackThreads) {
     const int t = c / (D * 9), rem = c % (D * 9), col = rem / 9, p = rem % 9;
     u32x4 x = kZero;
     if (p < 8) {
@@ -133,20 +159,20 @@ __device__ __attribute__((always_inline)) inline void pack_kv_body(
       for (int e = 0; e < 8; ++e) h[e] = sv[t][packed_key(8 * p + e)][col];
       x = __builtin_bit_cast(u32x4, h);
     }
-    buf_store16(rws, img + 2 * G::kKTile + t * G::kVTile + col * G::kVRow + p * 16, x);
+    buf_store16(rws, img + G::kOffV + t * G::kVTile + col * G::kVRow + p * 16, x);
   }
-  // the image's tail beyond the four tiles
+  // the image's tail beyond its tiles
   for (int o = G::kImgUsed + threadIdx.x * 16; o < G::kImgBytes; o += kPackThreads * 16)
     buf_store16(rws, img + o, kZero);
 }
 
 template <int D>
 struct RowState {
-  f32x16 accA[Geo<D>::kCB];  // A^T = sum p v      (rows: output column, cols: query)
-  f32x16 accG[Geo<D>::kCB];  // G^T = sum p (s dS v + dv)
-  float m;                   // running max of s*log2e*S (log2 units), per query row
-  float l;                   // this lane's half of sum p         (of the fp16-rounded p)
-  float u;                   // this lane's half of sum s p dS    (of the fp16-rounded values)
+  f32x16 accA[D / 32];  // A^T = sum p v      (rows: output column, cols: query)
+  f32x16 accG[D / 32];  // G^T = sum p (s dS v + dv)
+  float m;              // running max of s*log2e*S (log2 units), per query row
+  float l;              // this lane's half of sum p         (of the fp16-rounded p)
+  float u;              // this lane's half of sum s p dS    (of the fp16-rounded values)
 };
 
 // Slot r of lane half g holds key 8(r/4) + 4g + r%4 of its 32-key block.
@@ -156,19 +182,21 @@ __device__ __attribute__((always_inline)) inline int slot_key(int r, int g) {
 
 // One 32-key block (block `kb` of the tile in `stage`) for this wave's 32
 // query rows.  kMask: the block lies in the last tile, whose keys >= Nk get
-// p = 0 and contribute nothing to u.
+// p = 0 and contribute nothing to u.  issue(slot) is called at the start of
+// each step (slots 0..kKS-1: the S/dS steps, then the P V steps).
 // Online-softmax order: the accumulators hold sums normalised to the running
 // max m; a raised max rescales them by alpha = 2^(m_old - m_new) before this
 // block's P V is added.
-template <int D, bool kMask, typename Issue>
+template <int D, int kMode, bool kMask, typename Issue>
 __device__ __attribute__((always_inline)) inline void jvp_block(
     RowState<D>& st, const char* stage, int kb, const u32x4* qf, const u32x4* dqf, int l32,
     int g, int key0, int Nk, float c_log2, float scale, Issue issue) {
-  using G = Geo<D>;
+  using M = Mode<kMode>;
+  using G = Geo<D, M::kKV>;
   const char* sK = stage;
-  const char* sdK = stage + G::kKTile;
-  const char* sV = stage + 2 * G::kKTile;
-  const char* sdV = sV + G::kVTile;
+  const char* sdK = stage + G::kOffdK;
+  const char* sV = stage + G::kOffV;
+  const char* sdV = stage + G::kOffdV;
 
   // S^T and dS^T (rows: key, columns: this wave's queries).  The K and dK
   // fragments are read at their own step (the other wave on the SIMD covers
@@ -176,14 +204,16 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
   // reads, and their registers, across steps.
   const int krow = (32 * kb + l32) * G::kKRow + 16 * g;
   f32x16 s, ds;
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < G::kKS; ++ks) {
     issue(ks);
     const u32x4 kf = lds_load16(sK + krow + 32 * ks);
-    const u32x4 dkf = lds_load16(sdK + krow + 32 * ks);
+    u32x4 dkf;
+    if constexpr (M::kKV) dkf = lds_load16(sdK + krow + 32 * ks);
     s = mma_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s);
-    ds = mma_bf16(kf, dqf[ks], ks == 0 ? f32x16{} : ds);
-    ds = mma_bf16(dkf, qf[ks], ds);
+    if constexpr (M::kTan) ds = mma_bf16(kf, dqf[ks], ks == 0 ? f32x16{} : ds);
+    if constexpr (M::kKV) ds = mma_bf16(dkf, qf[ks], ds);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -216,21 +246,22 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
     for (int e = 0; e < 2; ++e) {
       const int r = 2 * q + e;
       pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -m_new));
-      pdd[e] = pp[e] * ds[r] * scale;
-      if (kMask && key0 + slot_key(r, g) >= Nk) {
-        pp[e] = 0.f;
-        pdd[e] = 0.f;
-      }
+      // keys past Nk: p = 0 (their K and dK rows are zero, so dS is 0 there
+      // unless the row's own Q or dQ is not finite)
+      if (kMask && key0 + slot_key(r, g) >= Nk) pp[e] = 0.f;
+      if constexpr (M::kTan) pdd[e] = pp[e] * ds[r] * scale;
     }
     const uint32_t hp = pack_f16x2(pp[0], pp[1]);
-    const uint32_t hd = pack_f16x2(pdd[0], pdd[1]);
     p[q >> 2][q & 3] = hp;
-    pd[q >> 2][q & 3] = hd;
     lsum = add_f16x2(hp, lsum);
-    usum = add_f16x2(hd, usum);
+    if constexpr (M::kTan) {
+      const uint32_t hd = pack_f16x2(pdd[0], pdd[1]);
+      pd[q >> 2][q & 3] = hd;
+      usum = add_f16x2(hd, usum);
+    }
   }
   st.l = st.l * alpha + lsum;
-  st.u = st.u * alpha + usum;
+  if constexpr (M::kTan) st.u = st.u * alpha + usum;
   // Pin the sums here (empty asm: a register constraint only); left alone, the
   // compiler sinks them into the next block and keeps P alive until then.
   asm volatile("" : "+v"(st.l), "+v"(st.u));
@@ -238,7 +269,7 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
 #pragma unroll
     for (int cb = 0; cb < G::kCB; ++cb) {
       st.accA[cb] *= alpha;
-      st.accG[cb] *= alpha;
+      if constexpr (M::kTan) st.accG[cb] *= alpha;
     }
   }
 
@@ -254,18 +285,18 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
   };
   u32x4 vf[2], dvf[2];
   vf[0] = lds_load16(sV + voff(0));
-  dvf[0] = lds_load16(sdV + voff(0));
+  if constexpr (M::kKV) dvf[0] = lds_load16(sdV + voff(0));
 #pragma unroll
   for (int step = 0; step < kSteps; ++step) {
     const int t = step / G::kCB, cb = step % G::kCB;
     issue(G::kKS + step);
     if (step + 1 < kSteps) {
       vf[(step + 1) & 1] = lds_load16(sV + voff(step + 1));
-      dvf[(step + 1) & 1] = lds_load16(sdV + voff(step + 1));
+      if constexpr (M::kKV) dvf[(step + 1) & 1] = lds_load16(sdV + voff(step + 1));
     }
     st.accA[cb] = mma_f16(vf[step & 1], p[t], st.accA[cb]);
-    st.accG[cb] = mma_f16(vf[step & 1], pd[t], st.accG[cb]);
-    st.accG[cb] = mma_f16(dvf[step & 1], p[t], st.accG[cb]);
+    if constexpr (M::kTan) st.accG[cb] = mma_f16(vf[step & 1], pd[t], st.accG[cb]);
+    if constexpr (M::kKV) st.accG[cb] = mma_f16(dvf[step & 1], p[t], st.accG[cb]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -276,17 +307,17 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
 // computed from `cur`.  The two stage pointers are restrict-qualified (they
 // name disjoint halves of the LDS), which tells the compiler that reads of
 // `cur` need not wait for the copy into `next`.
-template <int D, typename Copy>
+template <int D, int kMode, typename Copy>
 __device__ __attribute__((always_inline)) inline void tile_step(
     char* __restrict__ next, const char* __restrict__ cur, Copy copy, RowState<D>& st,
     const u32x4* qf, const u32x4* dqf, int l32, int g, int Nk, float c_log2, float scale) {
-  using G = Geo<D>;
+  using G = Geo<D, Mode<kMode>::kKV>;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
-    jvp_block<D, false>(st, cur, kb, qf, dqf, l32, g, 0, Nk, c_log2, scale,
-                        [&](int slot) {
-                          if (kb == 0 && slot < G::kDmaPerWave) copy(next, slot);
-                        });
+    jvp_block<D, kMode, false>(st, cur, kb, qf, dqf, l32, g, 0, Nk, c_log2, scale,
+                               [&](int slot) {
+                                 if (kb == 0 && slot < G::kDmaPerWave) copy(next, slot);
+                               });
 }
 
 // Sizes of the whole tensors (bytes) the kernel may touch; each global access
@@ -297,32 +328,56 @@ struct Extents {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int D>
-__device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
+// Four consecutive outputs of one row: 16 bytes of fp32, or 8 bytes of bf16.
+template <bool kBf16>
+__device__ __attribute__((always_inline)) inline void store4(__amdgpu_buffer_rsrc_t r,
+                                                             uint32_t elem, f32x4 x) {
+  if constexpr (kBf16) {
+    bf16x4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (__bf16)x[e];
+    buf_store8(r, elem * 2, __builtin_bit_cast(u32x2, h));
+  } else {
+    buf_store16(r, elem * 4, __builtin_bit_cast(u32x4, x));
+  }
+}
+
+// o, to: [B, H, Nq, D] in fp32 (kOutBf16 false) or bf16; lse, tlse: [B, H, Nq]
+// fp32, each may be NULL.  kFwd reads no tq and writes no to, tlse.
+template <int D, int kMode, bool kOutBf16>
+__global__ __launch_bounds__(kThreads) void attn_jvp_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ tq,
-    const char* __restrict__ img, float* __restrict__ o, float* __restrict__ to,
-    float* __restrict__ lse, int Nq, int Nk, int ntiles, Extents ext, float scale,
-    float c_log2) {
-  using G = Geo<D>;
+    const char* __restrict__ img, void* __restrict__ o, void* __restrict__ to,
+    float* __restrict__ lse, float* __restrict__ tlse, int Nq, int Nk, int ntiles, int nqt,
+    Extents ext, float scale, float c_log2) {
+  using M = Mode<kMode>;
+  using G = Geo<D, M::kKV>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * G::kImgBytes];
 
-  // Work item: blockIdx.x = query tile of kBR rows, blockIdx.y = (b, h) slice.
-  const int qt = blockIdx.x;
-  const uint32_t bh = blockIdx.y;
+  // Work item (query tile qt of kBR rows, (b, h) slice bh) from the linear
+  // workgroup id: the dispatcher deals workgroups to the 8 XCDs in turn
+  // (id % 8), so XCD x is given the x-th contiguous range of the work list
+  // ordered by (bh, qt).  The row tiles of one head then run on one XCD and
+  // share its L2, which holds the head's tile images once instead of once per
+  // XCD.  Any XCD count still gives a bijection (only locality changes).
+  const uint32_t wg = blockIdx.x, nwg = gridDim.x;
+  const uint32_t xcd = wg % kXcds, slot = wg / kXcds, per = nwg / kXcds, extra = nwg % kXcds;
+  const uint32_t work = xcd < extra ? xcd * (per + 1) + slot
+                                    : extra * (per + 1) + (xcd - extra) * per + slot;
+  const int qt = (int)(work % (uint32_t)nqt);
+  const uint32_t bh = work / (uint32_t)nqt;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int row = qt * kBR + wave * kRowsPerWave + l32;
   const bool row_ok = row < Nq;
 
-  // Buffer descriptors over whole tensors (see Extents).
+  // Buffer descriptors over whole tensors (see Extents); a NULL tq reads zeros.
   const auto rq = make_rsrc(q, ext.q_bytes);
-  const auto rtq = make_rsrc(tq, ext.q_bytes);
+  const auto rtq = make_rsrc(tq, tq != nullptr ? ext.q_bytes : 0u);
   // the workspace descriptor spans this (b, h) slice's tile images only
   const uint32_t slice_bytes = (uint32_t)ntiles * G::kImgBytes;
   const auto rimg = make_rsrc(img + (size_t)bh * slice_bytes, slice_bytes);
-  const auto ro = make_rsrc(o, ext.o_bytes);
-  const auto rto = make_rsrc(to, ext.o_bytes);
 
   // Copy of tile image kt into a stage: this wave's kDmaPerWave consecutive
   // KiB, lane l moving bytes 16 l .. 16 l + 15 of each (LDS address = the
@@ -333,11 +388,8 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rimg, (lds_ptr_t)(stage + wave_part + j * kDmaBytes),
                                              16, lane * 16, src, 0, 0);
   };
-  auto copy_tile = [&](int kt, char* stage) {
 #pragma unroll
-    for (int j = 0; j < G::kDmaPerWave; ++j) copy_one(kt, stage, j);
-  };
-  copy_tile(0, smem);
+  for (int j = 0; j < G::kDmaPerWave; ++j) copy_one(0, smem, j);
 
   // Q and dQ fragments: the B operand of S^T = K Q^T (lane: row l32, d-slice g).
   // Rows past Nq get an offset past the tensor, which the descriptor reads as 0.
@@ -347,7 +399,7 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
   for (int ks = 0; ks < G::kKS; ++ks) {
     const uint32_t off = qrow + (16 * ks + 8 * g) * 2;
     qf[ks] = buf_load16(rq, off);
-    dqf[ks] = buf_load16(rtq, off);
+    if constexpr (M::kTan) dqf[ks] = buf_load16(rtq, off);
   }
 
   RowState<D> st;
@@ -371,9 +423,9 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
   };
   finish_tile();
   for (int kt = 0; kt < kLast; ++kt) {
-    tile_step<D>(smem + ((kt + 1) & 1) * G::kImgBytes, smem + (kt & 1) * G::kImgBytes,
-                 [&](char* next, int j) { copy_one(kt + 1, next, j); }, st, qf, dqf, l32, g, Nk,
-                 c_log2, scale);
+    tile_step<D, kMode>(smem + ((kt + 1) & 1) * G::kImgBytes, smem + (kt & 1) * G::kImgBytes,
+                        [&](char* next, int j) { copy_one(kt + 1, next, j); }, st, qf, dqf, l32,
+                        g, Nk, c_log2, scale);
     finish_tile();
   }
   // last tile: keys past Nk are masked (the tile image holds zeros there)
@@ -381,17 +433,18 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
     const char* cur = smem + (kLast & 1) * G::kImgBytes;
     const int kl = kLast * kBC;
     auto none = [](int) {};
-    jvp_block<D, true>(st, cur, 0, qf, dqf, l32, g, kl, Nk, c_log2, scale, none);
-    jvp_block<D, true>(st, cur, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, scale, none);
+    jvp_block<D, kMode, true>(st, cur, 0, qf, dqf, l32, g, kl, Nk, c_log2, scale, none);
+    jvp_block<D, kMode, true>(st, cur, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, scale, none);
   }
 
-  // ---- epilogue: O = A / l, mu = u / l, dO = G / l - mu O, lse ----
+  // ---- epilogue: O = A / l, mu = u / l, dO = G / l - mu O, lse, tlse = mu ----
   const float l = halves_sum(st.l);
-  const float u = halves_sum(st.u);
   const float inv_l = 1.0f / l;
-  const float mu = u * inv_l;
+  const float mu = M::kTan ? halves_sum(st.u) * inv_l : 0.f;
   if (row_ok) {
-    const uint32_t orow = (bh * (uint32_t)Nq + row) * D * 4;
+    const uint32_t orow = (bh * (uint32_t)Nq + row) * D;  // first element of the row
+    const auto ro = make_rsrc(o, ext.o_bytes);
+    const auto rto = make_rsrc(to, M::kTan ? ext.o_bytes : 0u);
 #pragma unroll
     for (int cb = 0; cb < G::kCB; ++cb)
 #pragma unroll
@@ -402,78 +455,81 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_bf16_body(
         for (int e = 0; e < 4; ++e) {
           const float a = st.accA[cb][4 * qq + e] * inv_l;
           ov[e] = a;
-          tv[e] = st.accG[cb][4 * qq + e] * inv_l - mu * a;
+          if constexpr (M::kTan) tv[e] = st.accG[cb][4 * qq + e] * inv_l - mu * a;
         }
-        buf_store16(ro, orow + c0 * 4, __builtin_bit_cast(u32x4, ov));
-        buf_store16(rto, orow + c0 * 4, __builtin_bit_cast(u32x4, tv));
+        store4<kOutBf16>(ro, orow + c0, ov);
+        if constexpr (M::kTan) store4<kOutBf16>(rto, orow + c0, tv);
       }
-    if (lse != nullptr && g == 0) {
-      const auto rl = make_rsrc(lse, ext.lse_bytes);
-      buf_store4(rl, (bh * (uint32_t)Nq + row) * 4, (st.m + __log2f(l)) * kLn2);
+    if (g == 0) {
+      const uint32_t off = (bh * (uint32_t)Nq + row) * 4;
+      if (lse != nullptr) buf_store4(make_rsrc(lse, ext.lse_bytes), off, (st.m + __log2f(l)) * kLn2);
+      if (M::kTan && tlse != nullptr) buf_store4(make_rsrc(tlse, ext.lse_bytes), off, mu);
     }
   }
 }
 
-#define AJVP_BF16_KERNEL(D)                                                                 \
-  __global__ __launch_bounds__(kThreads) void attn_jvp_bf16_d##D(                            \
-      const uint16_t* __restrict__ q, const uint16_t* __restrict__ tq,                       \
-      const char* __restrict__ img, float* __restrict__ o, float* __restrict__ to,           \
-      float* __restrict__ lse, int Nq, int Nk, int ntiles, Extents ext, float scale,         \
-      float c_log2) {                                                                         \
-    attn_jvp_bf16_body<D>(q, tq, img, o, to, lse, Nq, Nk, ntiles, ext, scale, c_log2);       \
-  }                                                                                           \
-  __global__ __launch_bounds__(kPackThreads) void pack_kv_d##D(                              \
-      const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,                        \
-      const uint16_t* __restrict__ dk, const uint16_t* __restrict__ dv, char* __restrict__ ws, \
-      int Nk, int ntiles, uint32_t kv_bytes) {                                                \
-    pack_kv_body<D>(k, v, dk, dv, ws, Nk, ntiles, kv_bytes);                                  \
-  }
-AJVP_BF16_KERNEL(64)
-AJVP_BF16_KERNEL(128)
-#undef AJVP_BF16_KERNEL
+template <int D, bool kKV>
+__global__ __launch_bounds__(kPackThreads) void pack_kv_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dk, const uint16_t* __restrict__ dv, char* __restrict__ ws,
+    int Nk, int ntiles, uint32_t kv_bytes) {
+  pack_kv_body<D, kKV>(k, v, dk, dv, ws, Nk, ntiles, kv_bytes);
+}
 
-template <int D>
-struct Kernels;
-template <>
-struct Kernels<64> {
-  static constexpr auto main = attn_jvp_bf16_d64;
-  static constexpr auto pack = pack_kv_d64;
-};
-template <>
-struct Kernels<128> {
-  static constexpr auto main = attn_jvp_bf16_d128;
-  static constexpr auto pack = pack_kv_d128;
-};
-
-template <int D>
+template <int D, bool kKV>
 hipError_t launch_pack_d(const void* k, const void* v, const void* tk, const void* tv, int B,
                          int H, int Nk, void* ws, hipStream_t stream) {
   const int ntiles = (Nk + kBC - 1) / kBC;
   const int bh = B * H;
   const uint32_t kv_bytes = (uint32_t)((size_t)bh * Nk * D * 2);
-  hipLaunchKernelGGL(Kernels<D>::pack, dim3(ntiles, bh), dim3(kPackThreads), 0, stream,
+  hipLaunchKernelGGL((pack_kv_kernel<D, kKV>), dim3(ntiles, bh), dim3(kPackThreads), 0, stream,
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      static_cast<const uint16_t*>(tk), static_cast<const uint16_t*>(tv),
                      static_cast<char*>(ws), Nk, ntiles, kv_bytes);
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_main_d(const void* q, const void* tq, const void* ws, float* o, float* to,
-                         float* lse, int B, int H, int Nq, int Nk, float scale,
+template <int D, int kMode, bool kOutBf16>
+hipError_t launch_main_d(const void* q, const void* tq, const void* ws, void* o, void* to,
+                         float* lse, float* tlse, int B, int H, int Nq, int Nk, float scale,
                          hipStream_t stream) {
   const int ntiles = (Nk + kBC - 1) / kBC;
   const int nqt = (Nq + kBR - 1) / kBR;
   const int bh = B * H;
   Extents ext;
   ext.q_bytes = (uint32_t)((size_t)bh * Nq * D * 2);
-  ext.o_bytes = (uint32_t)((size_t)bh * Nq * D * 4);
+  ext.o_bytes = (uint32_t)((size_t)bh * Nq * D * (kOutBf16 ? 2 : 4));
   ext.lse_bytes = (uint32_t)((size_t)bh * Nq * 4);
-  hipLaunchKernelGGL(Kernels<D>::main, dim3(nqt, bh), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(tq),
-                     static_cast<const char*>(ws), o, to, lse, Nq, Nk, ntiles, ext, scale,
-                     scale * kLog2e);
+  hipLaunchKernelGGL((attn_jvp_bf16_kernel<D, kMode, kOutBf16>), dim3(nqt * bh),
+                     dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(tq), static_cast<const char*>(ws), o, to, lse,
+                     tlse, Nq, Nk, ntiles, nqt, ext, scale, scale * kLog2e);
   return hipGetLastError();
+}
+
+template <int kMode>
+hipError_t launch_main(const void* q, const void* tq, const void* ws, void* o, void* to,
+                       float* lse, float* tlse, int B, int H, int Nq, int Nk, int d, float scale,
+                       bool out_bf16, hipStream_t stream) {
+  if (d == 128)
+    return out_bf16 ? launch_main_d<128, kMode, true>(q, tq, ws, o, to, lse, tlse, B, H, Nq, Nk,
+                                                      scale, stream)
+                    : launch_main_d<128, kMode, false>(q, tq, ws, o, to, lse, tlse, B, H, Nq, Nk,
+                                                       scale, stream);
+  return out_bf16 ? launch_main_d<64, kMode, true>(q, tq, ws, o, to, lse, tlse, B, H, Nq, Nk,
+                                                   scale, stream)
+                  : launch_main_d<64, kMode, false>(q, tq, ws, o, to, lse, tlse, B, H, Nq, Nk,
+                                                    scale, stream);
+}
+
+hipError_t launch_pack(bool kv_tangents, const void* k, const void* v, const void* tk,
+                       const void* tv, int B, int H, int Nk, int d, void* ws,
+                       hipStream_t stream) {
+  if (kv_tangents)
+    return d == 128 ? launch_pack_d<128, true>(k, v, tk, tv, B, H, Nk, ws, stream)
+                    : launch_pack_d<64, true>(k, v, tk, tv, B, H, Nk, ws, stream);
+  return d == 128 ? launch_pack_d<128, false>(k, v, nullptr, nullptr, B, H, Nk, ws, stream)
+                  : launch_pack_d<64, false>(k, v, nullptr, nullptr, B, H, Nk, ws, stream);
 }
 
 }  // namespace bf16_path
@@ -481,21 +537,20 @@ using namespace bf16_path;
 
 size_t bf16_workspace_bytes(int B, int H, int Nk, int d) {
   const size_t ntiles = ((size_t)Nk + kBC - 1) / kBC;
-  const size_t img = d == 128 ? Geo<128>::kImgBytes : Geo<64>::kImgBytes;
+  const size_t img = d == 128 ? Geo<128, true>::kImgBytes : Geo<64, true>::kImgBytes;
   return (size_t)B * H * ntiles * img;
 }
 
 hipError_t launch_pack_kv(const void* k, const void* v, const void* tk, const void* tv, int B,
                           int H, int Nk, int d, void* ws, hipStream_t stream) {
-  return d == 128 ? launch_pack_d<128>(k, v, tk, tv, B, H, Nk, ws, stream)
-                  : launch_pack_d<64>(k, v, tk, tv, B, H, Nk, ws, stream);
+  return launch_pack(true, k, v, tk, tv, B, H, Nk, d, ws, stream);
 }
 
 hipError_t launch_bf16_packed(const void* q, const void* tq, const void* ws, float* o,
                               float* to, float* lse, int B, int H, int Nq, int Nk, int d,
                               float scale, hipStream_t stream) {
-  return d == 128 ? launch_main_d<128>(q, tq, ws, o, to, lse, B, H, Nq, Nk, scale, stream)
-                  : launch_main_d<64>(q, tq, ws, o, to, lse, B, H, Nq, Nk, scale, stream);
+  return launch_main<kFull>(q, tq, ws, o, to, lse, nullptr, B, H, Nq, Nk, d, scale, false,
+                            stream);
 }
 
 hipError_t launch_bf16(const void* q, const void* k, const void* v, const void* tq,
@@ -504,6 +559,29 @@ hipError_t launch_bf16(const void* q, const void* k, const void* v, const void* 
   const hipError_t e = launch_pack_kv(k, v, tk, tv, B, H, Nk, d, ws, stream);
   if (e != hipSuccess) return e;
   return launch_bf16_packed(q, tq, ws, o, to, lse, B, H, Nq, Nk, d, scale, stream);
+}
+
+hipError_t launch_bf16_ex(const void* q, const void* k, const void* v, const void* tq,
+                          const void* tk, const void* tv, void* o, void* to, float* lse,
+                          float* tlse, int B, int H, int Nq, int Nk, int d, float scale,
+                          bool out_bf16, void* ws, hipStream_t stream) {
+  // dK = dV = 0: the frozen-key mode leaves their products and tiles out
+  const bool kv = tk != nullptr || tv != nullptr;
+  hipError_t e = launch_pack(kv, k, v, tk, tv, B, H, Nk, d, ws, stream);
+  if (e != hipSuccess) return e;
+  return kv ? launch_main<kFull>(q, tq, ws, o, to, lse, tlse, B, H, Nq, Nk, d, scale, out_bf16,
+                                 stream)
+            : launch_main<kFrozen>(q, tq, ws, o, to, lse, tlse, B, H, Nq, Nk, d, scale, out_bf16,
+                                   stream);
+}
+
+hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int Nq, int Nk, int d, float scale, bool out_bf16, void* ws,
+                      hipStream_t stream) {
+  hipError_t e = launch_pack(false, k, v, nullptr, nullptr, B, H, Nk, d, ws, stream);
+  if (e != hipSuccess) return e;
+  return launch_main<kFwd>(q, nullptr, ws, o, nullptr, lse, nullptr, B, H, Nq, Nk, d, scale,
+                           out_bf16, stream);
 }
 
 }  // namespace ajvp

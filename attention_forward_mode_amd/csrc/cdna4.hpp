@@ -14,6 +14,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -36,9 +38,16 @@ __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, 
       u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, (int)uniform_off, 0));
 }
 
+__device__ inline float buf_load4f(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
+}
+
 // Stores at or past the descriptor's size are dropped by the hardware.
 __device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, 0);
+}
+__device__ inline void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)byte_off, 0, 0);
 }
 __device__ inline void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)byte_off, 0, 0);

@@ -25,6 +25,24 @@ hipError_t launch_bf16_packed(const void* q, const void* tq, const void* workspa
                               float* to, float* lse, int B, int H, int Nq, int Nk, int d,
                               float scale, hipStream_t stream);
 
+// Extended JVP: tq, tk, tv may be NULL (zero tangents; with tk = tv = NULL the
+// frozen-key mode skips their products), tlse (the tangent of lse) and lse may
+// be NULL, o and to are fp32 or (out_bf16) bf16.
+hipError_t launch_bf16_ex(const void* q, const void* k, const void* v, const void* tq,
+                          const void* tk, const void* tv, void* o, void* to, float* lse,
+                          float* tlse, int B, int H, int Nq, int Nk, int d, float scale,
+                          bool out_bf16, void* workspace, hipStream_t stream);
+
+// Forward attention alone (O, lse).
+hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int Nq, int Nk, int d, float scale, bool out_bf16, void* workspace,
+                      hipStream_t stream);
+
+// Merge of P partial results over disjoint key subsets (rows R, head dim d).
+hipError_t launch_merge(const float* lse_p, const float* o_p, const float* to_p,
+                        const float* tlse_p, int P, int R, int d, float* lse, float* o,
+                        float* to, float* tlse, hipStream_t stream);
+
 hipError_t launch_f32(const float* q, const float* k, const float* v, const float* tq,
                       const float* tk, const float* tv, float* o, float* to, float* lse,
                       int B, int H, int Nq, int Nk, int d, float scale, hipStream_t stream);

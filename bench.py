@@ -118,12 +118,79 @@ def calib_copy(nbytes=1 << 30, reps=5):
     print(json.dumps({"calib_copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
+# flops per (b, h) and Nq Nk d of each mode: the contractions it performs
+MODE_FLOPS = {"jvp": 12.0, "frozen": 8.0, "fwd": 4.0}
+
+
+def bench_variant(args, ajvp, w, g, x, scale):
+    """Time one call of attn_jvp_fwd_ex (frozen keys: tk = tv = NULL) or attn_fwd
+    per step, pack included, with a preallocated workspace."""
+    import torch
+
+    B, H, Nq, d = g["q"].shape
+    Nk = g["k"].shape[2]
+    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    ws = torch.empty(ajvp.attn_jvp_workspace_bytes(B, H, Nk, d), dtype=torch.uint8, device="cuda")
+
+    def step():
+        if args.mode == "fwd":
+            return ajvp.attn_fwd(g["q"], g["k"], g["v"], scale=scale, out_dtype=out_dtype,
+                                 workspace=ws)
+        if args.mode == "frozen":
+            return ajvp.attn_jvp_fwd_ex(g["q"], g["k"], g["v"], g["dq"], None, None, scale=scale,
+                                        out_dtype=out_dtype, workspace=ws)
+        return ajvp.attn_jvp_fwd_ex(g["q"], g["k"], g["v"], g["dq"], g["dk"], g["dv"],
+                                    scale=scale, out_dtype=out_dtype, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t_wall = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        out = step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = sum(per) / len(per)
+    assert all(torch.isfinite(t).all() for t in out if t is not None), "non-finite output"
+    fl = MODE_FLOPS[args.mode] * B * H * Nq * Nk * d
+    tflops = fl / (ms / 1e3) / 1e12
+    names = {"jvp": "attn+JVP", "frozen": "attn+JVP with frozen keys (dK = dV = 0)",
+             "fwd": "forward attention"}
+    res = {
+        "metric": f"{names[args.mode]} TFLOP/s at 1 GPU ({args.workload})",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "ms_per_step_min": round(min(per), 4),
+        "wall_ms_timed_region": round(wall_ms, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded Gaussians)",
+        "config": {"workload": f"{w.name}: {w.description}", "B": B, "H": H, "Nq": Nq, "Nk": Nk,
+                   "d": d, "scale": scale, "mode": args.mode,
+                   "outputs": f"{args.out_dtype} O" + ("" if args.mode == "fwd" else ", dO") +
+                              ", fp32 lse"},
+        "flops_per_step": fl,
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"kernel": "pack_kv + attn_jvp_bf16 (one call, pack included)",
+                     "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video_1p3b")
+    ap.add_argument("--mode", choices=["jvp", "frozen", "fwd"], default="jvp",
+                    help="jvp: the full attention+JVP (the headline); frozen: dK = dV = 0 passed "
+                         "as NULL (8 Nq Nk d flops); fwd: forward attention alone (4 Nq Nk d)")
+    ap.add_argument("--out-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
@@ -154,6 +221,8 @@ def main():
 
     B, H, Nq, d = g["q"].shape
     Nk = g["k"].shape[2]
+    if args.mode != "jvp" or args.out_dtype != "f32":
+        return bench_variant(args, ajvp, w, g, x, scale)
     o = torch.empty((B, H, Nq, d), dtype=torch.float32, device=dev)
     to = torch.empty_like(o)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)

@@ -78,6 +78,10 @@ extern "C" {
 #define ATTN_JVP_EALIGN (-3)
 #define ATTN_JVP_ELAUNCH (-4)
 
+/* Output element types of attn_jvp_fwd_ex and attn_fwd. */
+#define ATTN_JVP_OUT_F32 0
+#define ATTN_JVP_OUT_BF16 1
+
 /* Opaque HIP stream handle (hipStream_t). */
 typedef struct ihipStream_t *attn_jvp_stream_t;
 
@@ -150,6 +154,64 @@ ATTN_JVP_API int attn_jvp_fwd_packed(const void *q, const void *tq,
                         float *o, float *to, float *lse,
                         int B, int H, int Nq, int Nk, int d, float scale,
                         attn_jvp_stream_t stream);
+
+/*
+ * Extended form of attn_jvp_fwd (same operation, same input layouts):
+ *   tq, tk, tv   each may be NULL, meaning a zero tangent.  With tk = tv = NULL
+ *                (frozen keys, e.g. the text keys of cross-attention) the
+ *                products with dK and dV are left out: 4 of the 6 contractions.
+ *   o, to        O and dO, [B, H, Nq, d], in fp32 (out_dtype ATTN_JVP_OUT_F32)
+ *                or bf16 rounded to nearest even (ATTN_JVP_OUT_BF16); required
+ *   lse          fp32 [B, H, Nq] or NULL
+ *   tlse         the tangent of lse, mu_i = sum_j P_ij dS_ij, fp32 [B, H, Nq], or
+ *                NULL.  With lse, O and dO it is the state that attn_jvp_merge
+ *                combines across key subsets.
+ *   workspace    NULL (a library-owned stream-ordered pool provides it) or a
+ *                device buffer of at least attn_jvp_workspace_bytes(B, H, Nk, d)
+ *                bytes, 256-byte aligned (then nothing is allocated)
+ * Errors as attn_jvp_fwd; EINVAL also for an unknown out_dtype; EALIGN for a
+ * non-NULL tangent not 16-byte aligned or tlse not 4-byte aligned.
+ */
+ATTN_JVP_API int attn_jvp_fwd_ex(const void *q, const void *k, const void *v,
+                    const void *tq, const void *tk, const void *tv,
+                    void *o, void *to, float *lse, float *tlse,
+                    int B, int H, int Nq, int Nk, int d, float scale, int out_dtype,
+                    void *workspace, size_t workspace_bytes,
+                    attn_jvp_stream_t stream);
+
+/*
+ * Forward attention alone (FlashAttention-2's output, without a tangent):
+ * O = softmax(scale Q K^T) V and lse, bf16 inputs as in attn_jvp_fwd, O in fp32
+ * or bf16 (out_dtype), lse fp32 or NULL.  The same kernel as attn_jvp_fwd with
+ * the tangent left out (2 of the 6 contractions); its O and lse equal
+ * attn_jvp_fwd's bit for bit.  Workspace and errors as attn_jvp_fwd_ex.
+ */
+ATTN_JVP_API int attn_fwd(const void *q, const void *k, const void *v,
+             void *o, float *lse,
+             int B, int H, int Nq, int Nk, int d, float scale, int out_dtype,
+             void *workspace, size_t workspace_bytes,
+             attn_jvp_stream_t stream);
+
+/*
+ * Merge of P partial results of the same R query rows, each computed against
+ * a disjoint subset of the keys (a key-split of one call, or the key shards
+ * of a context-parallel layout).  fp32 device arrays, part-major:
+ *   lse_parts [P][R], o_parts [P][R][d], to_parts [P][R][d], tlse_parts [P][R]
+ *   lse [R], o [R][d], to [R][d], tlse [R]
+ * with a_p = exp(lse_p - lse):  lse = log sum_p exp(lse_p),  O = sum_p a_p O_p,
+ * tlse = sum_p a_p tlse_p,  dO = sum_p a_p (dO_p + tlse_p O_p) - tlse O.
+ * to_parts, tlse_parts and to are either all given (the JVP state) or all NULL
+ * (forward only; tlse must then be NULL too); lse may be NULL.  d = 64 or 128,
+ * 1 <= P <= 1024, each array under 2^31 bytes.  A row whose parts all have
+ * lse = -inf yields NaN.  Errors: EINVAL (NULL inputs, inconsistent tangent
+ * arguments, P or R < 1), EUNSUPPORTED (d, P or sizes), EALIGN (16-byte for
+ * o/to arrays, 4-byte for lse/tlse arrays), ELAUNCH.  Allocates nothing.
+ */
+ATTN_JVP_API int attn_jvp_merge(const float *lse_parts, const float *o_parts,
+                   const float *to_parts, const float *tlse_parts,
+                   int P, int R, int d,
+                   float *lse, float *o, float *to, float *tlse,
+                   attn_jvp_stream_t stream);
 
 /*
  * The same operation with fp32 inputs and fp32 arithmetic throughout (the

@@ -37,6 +37,8 @@ def test_library_loads_and_exports_every_declared_symbol():
 def test_error_codes_match_header():
     text = open(os.path.join(ROOT, "include", "attn_jvp.h")).read()
     codes = dict(re.findall(r"#define (ATTN_JVP_\w+) \(?(-?\d+)\)?", text))
+    outs = {k: int(codes.pop(k)) for k in list(codes) if k.startswith("ATTN_JVP_OUT_")}
+    assert outs == {"ATTN_JVP_OUT_F32": ajvp.OUT_F32, "ATTN_JVP_OUT_BF16": ajvp.OUT_BF16}
     assert {k: int(v) for k, v in codes.items()} == {
         "ATTN_JVP_OK": OK, "ATTN_JVP_EINVAL": EINVAL, "ATTN_JVP_EUNSUPPORTED": EUNSUPPORTED,
         "ATTN_JVP_EALIGN": EALIGN, "ATTN_JVP_ELAUNCH": ELAUNCH}
@@ -194,3 +196,97 @@ def test_fwd_packed_rejects_bad_arguments():
     p[4] += 2
     assert _packed(p) == EALIGN
     assert _packed(ws=A + 0x1000000 + 64) == EALIGN
+
+
+# ---- extended entry points ----
+
+def _ex(ptrs=None, B=1, H=1, Nq=4, Nk=4, d=128, scale=0.1, out_dtype=0, ws=0, ws_bytes=0):
+    # q k v tq tk tv o to lse tlse
+    p = [A + i * 0x100000 for i in range(10)] if ptrs is None else ptrs
+    return ajvp.lib().attn_jvp_fwd_ex(
+        *[ctypes.c_void_p(x) for x in p], B, H, Nq, Nk, d, ctypes.c_float(scale), out_dtype,
+        ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(0))
+
+
+def _fwd(ptrs=None, B=1, H=1, Nq=4, Nk=4, d=128, scale=0.1, out_dtype=0, ws=0, ws_bytes=0):
+    p = [A + i * 0x100000 for i in range(5)] if ptrs is None else ptrs  # q k v o lse
+    return ajvp.lib().attn_fwd(
+        *[ctypes.c_void_p(x) for x in p], B, H, Nq, Nk, d, ctypes.c_float(scale), out_dtype,
+        ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(0))
+
+
+def _merge(ptrs=None, P=2, R=8, d=128):
+    p = [A + i * 0x100000 for i in range(8)] if ptrs is None else ptrs
+    # lse_parts o_parts to_parts tlse_parts | lse o to tlse
+    return ajvp.lib().attn_jvp_merge(*[ctypes.c_void_p(x) for x in p[:4]], P, R, d,
+                                     *[ctypes.c_void_p(x) for x in p[4:]], ctypes.c_void_p(0))
+
+
+def test_fwd_ex_rejects_bad_arguments():
+    for i in (0, 1, 2, 6, 7):  # q k v o to are required; tangents, lse, tlse optional
+        p = [A + j * 0x100000 for j in range(10)]
+        p[i] = 0
+        assert _ex(p) == EINVAL, i
+    assert _ex(out_dtype=2) == EINVAL and _ex(out_dtype=-1) == EINVAL
+    assert _ex(scale=float("nan")) == EINVAL and _ex(Nq=0) == EINVAL
+    assert _ex(d=96) == EUNSUPPORTED
+    for i in range(8):  # 16-byte alignment of every tensor
+        p = [A + j * 0x100000 for j in range(10)]
+        p[i] += 8
+        assert _ex(p) == EALIGN, i
+    p = [A + j * 0x100000 for j in range(10)]
+    p[9] += 2  # tlse: 4-byte alignment
+    assert _ex(p) == EALIGN
+    # a caller workspace is checked like attn_jvp_fwd_ws's
+    assert _ex(ws=A + 0x3000000, ws_bytes=100) == EINVAL
+    nb = ajvp.attn_jvp_workspace_bytes(1, 1, 4, 128)
+    assert _ex(ws=A + 0x3000000 + 64, ws_bytes=nb) == EALIGN
+
+
+def test_fwd_ex_accepts_null_tangents_up_to_launch():
+    # every combination of NULL tangents passes validation; a misaligned o stops
+    # the call before anything is launched
+    for mask in range(8):
+        p = [A + j * 0x100000 for j in range(10)]
+        for i in range(3):
+            if mask >> i & 1:
+                p[3 + i] = 0
+        p[6] += 4
+        assert _ex(p) == EALIGN, mask
+
+
+def test_attn_fwd_rejects_bad_arguments():
+    for i in range(4):  # q k v o (lse optional)
+        p = [A + j * 0x100000 for j in range(5)]
+        p[i] = 0
+        assert _fwd(p) == EINVAL, i
+    assert _fwd(out_dtype=3) == EINVAL and _fwd(scale=-1.0) == EINVAL
+    assert _fwd(d=32) == EUNSUPPORTED and _fwd(B=1 << 16) == EUNSUPPORTED
+    p = [A + j * 0x100000 for j in range(5)]
+    p[3] += 4
+    assert _fwd(p) == EALIGN
+
+
+def test_merge_rejects_bad_arguments():
+    for i in (0, 1, 5):  # lse_parts, o_parts, o
+        p = [A + j * 0x100000 for j in range(8)]
+        p[i] = 0
+        assert _merge(p) == EINVAL, i
+    for i in (2, 3, 6):  # the tangent arrays go together
+        p = [A + j * 0x100000 for j in range(8)]
+        p[i] = 0
+        assert _merge(p) == EINVAL, i
+    p = [A + j * 0x100000 for j in range(8)]
+    p[2] = p[3] = p[6] = 0  # forward-only merge with a tlse output
+    assert _merge(p) == EINVAL
+    assert _merge(P=0) == EINVAL and _merge(R=0) == EINVAL
+    assert _merge(d=96) == EUNSUPPORTED and _merge(P=2048) == EUNSUPPORTED
+    assert _merge(P=1024, R=1 << 20) == EUNSUPPORTED  # o_parts past 2^31 bytes
+    for i in (1, 2, 5, 6):
+        p = [A + j * 0x100000 for j in range(8)]
+        p[i] += 8
+        assert _merge(p) == EALIGN, i
+    for i in (0, 3, 4, 7):
+        p = [A + j * 0x100000 for j in range(8)]
+        p[i] += 2
+        assert _merge(p) == EALIGN, i
