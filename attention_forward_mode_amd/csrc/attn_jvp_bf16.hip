@@ -264,7 +264,10 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
   if constexpr (M::kTan) st.u = st.u * alpha + usum;
   // Pin the sums here (empty asm: a register constraint only); left alone, the
   // compiler sinks them into the next block and keeps P alive until then.
-  asm volatile("" : "+v"(st.l), "+v"(st.u));
+  if constexpr (M::kTan)
+    asm volatile("" : "+v"(st.l), "+v"(st.u));
+  else
+    asm volatile("" : "+v"(st.l));
   if (wave_any(alpha != 1.0f)) {
 #pragma unroll
     for (int cb = 0; cb < G::kCB; ++cb) {
@@ -283,14 +286,17 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
     const int t = step / G::kCB, cb = step % G::kCB;
     return (32 * cb + l32) * G::kVRow + 16 * g + 16 * (4 * kb + 2 * t);
   };
+  // (the forward mode, held to 128 registers, reads each fragment at its step)
+  constexpr bool kPf = M::kTan;
   u32x4 vf[2], dvf[2];
-  vf[0] = lds_load16(sV + voff(0));
+  if constexpr (kPf) vf[0] = lds_load16(sV + voff(0));
   if constexpr (M::kKV) dvf[0] = lds_load16(sdV + voff(0));
 #pragma unroll
   for (int step = 0; step < kSteps; ++step) {
     const int t = step / G::kCB, cb = step % G::kCB;
     issue(G::kKS + step);
-    if (step + 1 < kSteps) {
+    if constexpr (!kPf) vf[step & 1] = lds_load16(sV + voff(step));
+    if (kPf && step + 1 < kSteps) {
       vf[(step + 1) & 1] = lds_load16(sV + voff(step + 1));
       if constexpr (M::kKV) dvf[(step + 1) & 1] = lds_load16(sdV + voff(step + 1));
     }
@@ -344,8 +350,10 @@ __device__ __attribute__((always_inline)) inline void store4(__amdgpu_buffer_rsr
 
 // o, to: [B, H, Nq, D] in fp32 (kOutBf16 false) or bf16; lse, tlse: [B, H, Nq]
 // fp32, each may be NULL.  kFwd reads no tq and writes no to, tlse.
+// Waves per SIMD: 2 for the JVP modes (256 registers each); 4 for the forward
+// mode, whose 128 registers and 80 KiB of LDS let two workgroups share a CU.
 template <int D, int kMode, bool kOutBf16>
-__global__ __launch_bounds__(kThreads) void attn_jvp_bf16_kernel(
+__global__ __launch_bounds__(kThreads, kMode == kFwd ? 4 : 2) void attn_jvp_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ tq,
     const char* __restrict__ img, void* __restrict__ o, void* __restrict__ to,
     float* __restrict__ lse, float* __restrict__ tlse, int Nq, int Nk, int ntiles, int nqt,
