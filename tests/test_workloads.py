@@ -77,3 +77,20 @@ def test_outliers():
     for t in TENSORS:
         assert f[t].dtype == torch.float32
         assert torch.equal(f[t].to(torch.bfloat16), g[t])
+
+
+def test_unrounded_draws_round_to_the_bf16_draws():
+    """dtype="fp32" gives the draws before their bf16 rounding: rounding them
+    reproduces the bf16 workload exactly (no row-max step), or to within one
+    bf16 rounding of the row scale (row-max step)."""
+    for name in ("image_dit", "video_14b"):
+        x, _ = make_inputs(name, Nq=40, Nk=50, heads=[1], device="cpu")
+        y, _ = make_inputs(name, Nq=40, Nk=50, heads=[1], device="cpu", dtype="fp32")
+        assert all(y[n].dtype == torch.float32 for n in y)
+        for n in x:
+            assert torch.equal(y[n].to(torch.bfloat16), x[n]), (name, n)
+        assert any(not torch.equal(y[n], x[n].float()) for n in x)
+    x, _ = make_inputs("video_1p3b", Nq=40, Nk=50, heads=[0], device="cpu")
+    y, _ = make_inputs("video_1p3b", Nq=40, Nk=50, heads=[0], device="cpu", dtype="fp32")
+    rel = ((y["q"] - x["q"].float()).abs() / x["q"].float().abs().clamp_min(1e-3)).max()
+    assert rel < 2 ** -6  # two bf16 roundings and a row scale from rounded values

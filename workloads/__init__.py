@@ -105,13 +105,16 @@ def _max_dot(q, k, device):
     return out
 
 
-def make_inputs(name, seed=0, heads=None, Nq=None, Nk=None, device=None):
+def make_inputs(name, seed=0, heads=None, Nq=None, Nk=None, device=None, dtype=None):
     """Draw the six input tensors of a workload on the CPU.
 
     ``heads`` restricts to a subset of head indices (same values as in the full
     draw); ``Nq``/``Nk`` override the sequence lengths with the same recipe
     (for reduced-size checks).  ``device`` is where the float64 max-dot-product
     of the ``row_max`` step runs (default: the GPU if one is visible).
+    ``dtype="fp32"`` returns a bf16 workload's draws before they are rounded to
+    bf16 (the row_max step then works on the fp32 values), for precision
+    comparisons against unrounded inputs.
     Returns (dict of contiguous CPU tensors keyed by TENSORS, scale).
     """
     w = WORKLOADS[name]
@@ -119,7 +122,10 @@ def make_inputs(name, seed=0, heads=None, Nq=None, Nk=None, device=None):
     Nk = w.Nk if Nk is None else Nk
     heads = list(range(w.H)) if heads is None else list(heads)
     H_seed = w.seed_H or w.H
-    out_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dtype = w.dtype if dtype is None else dtype
+    if dtype not in ("bf16", "fp32"):
+        raise ValueError("dtype must be 'bf16' or 'fp32'")
+    out_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
     if device is None:
         device = "cuda" if torch.cuda.is_available() else "cpu"
     lens = (Nq, Nk, Nk, Nq, Nk, Nk)
