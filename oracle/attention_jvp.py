@@ -22,6 +22,14 @@ plain mathematical definition of that result, not the tiled algorithm:
     O   = P V
     lse = m + ln(sum_j exp(S_ij - m)),  m = max_j S_ij   (natural log)
 
+  and for a cotangent gO (the gradient of a loss with respect to O), the
+  reverse-mode derivative (vector-Jacobian product) of the same map:
+
+    gV  = P^T gO                                      (O = P V, in V)
+    gP  = gO V^T                                      (O = P V, in P)
+    gS  = P * (gP - D),  D_i = sum_j P_ij gP_ij       (adjoint of the softmax)
+    gQ  = s gS K,  gK = s gS^T Q                      (S = s Q K^T)
+
   and for tangents dQ, dK, dV (a directional derivative of the map above):
 
     dS  = s * (dQ K^T + Q dK^T)                       (product rule on S)
@@ -41,7 +49,7 @@ here is "parity unpinned".
 
 import numpy as np
 
-__all__ = ["attention", "attention_jvp", "attention_jvp_rows"]
+__all__ = ["attention", "attention_jvp", "attention_jvp_rows", "attention_vjp"]
 
 # Rows per chunk: bounds the Nq_chunk x Nk float64 temporaries (512 x 32760 x 8 B
 # = 134 MB each) without changing any value.
@@ -88,6 +96,41 @@ def _head_jvp(q, k, v, dq, dk, dv, scale):
     dO = dP @ v + P @ dv
     # lse = log sum exp(S): its derivative is sum_j P_ij dS_ij = mu.
     return O, dO, lse, mu
+
+
+def _head_vjp(q, k, v, go, scale):
+    """Gradients of <gO, O> for one head: q [n, d], k and v [Nk, d], go [n, d].
+
+    Each line is the adjoint of one line of ``_head_forward``."""
+    _, _, P = _head_forward(q, k, v, scale)
+    gV = P.T @ go
+    gP = go @ v.T
+    D = (P * gP).sum(axis=1, keepdims=True)
+    gS = P * (gP - D)
+    return scale * (gS @ k), scale * (gS.T @ q), gV
+
+
+def attention_vjp(q, k, v, go, scale):
+    """Reverse-mode derivative: the gradients (gQ, gK, gV) of sum(gO * O) with
+    respect to Q, K and V.  q, go: [B, H, Nq, d]; k, v: [B, H, Nk, d].  Float64.
+
+    Query rows are processed in chunks (memory only): gQ is per row, and the
+    key-side gradients gK, gV are sums over rows, accumulated chunk by chunk.
+    """
+    q, k, v, go = (_f64(t) for t in (q, k, v, go))
+    B, H, Nq, d = q.shape
+    gq = np.empty_like(q)
+    gk = np.zeros_like(k)
+    gv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, Nq, ROW_CHUNK):
+                r1 = min(Nq, r0 + ROW_CHUNK)
+                a, c, e = _head_vjp(q[b, h, r0:r1], k[b, h], v[b, h], go[b, h, r0:r1], scale)
+                gq[b, h, r0:r1] = a
+                gk[b, h] += c
+                gv[b, h] += e
+    return gq, gk, gv
 
 
 def attention(q, k, v, scale):
