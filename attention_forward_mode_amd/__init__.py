@@ -14,6 +14,8 @@ device memory and the current stream.  The names mirror the C entry points:
     attn_fwd(q, k, v, ...) -> (o, lse)    forward attention alone
     attn_jvp_merge(lse_parts, o_parts, to_parts=None, tlse_parts=None)
         -> (lse, o, to, tlse): combine results over disjoint key subsets
+    attn_bwd(q, k, v, o, go, lse) -> (gq, gk, gv)
+        the backward pass: gradients of a loss through O
     attn_jvp_fwd_f32(...)  the same with fp32 inputs
     attn_jvp_workspace_bytes(B, H, Nk, d)
     attn_jvp_strerror(status)
@@ -33,7 +35,8 @@ import os
 import torch
 
 __all__ = ["attn_jvp_fwd", "attn_jvp_pack_kv", "attn_jvp_fwd_packed", "attn_jvp_fwd_ex", "attn_fwd",
-           "attn_jvp_merge", "attn_jvp_fwd_f32", "attn_jvp_workspace_bytes",
+           "attn_jvp_merge", "attn_bwd", "attn_bwd_workspace_bytes", "attn_jvp_fwd_f32",
+           "attn_jvp_workspace_bytes",
            "attn_jvp_strerror", "AttnJvpError", "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_jvp.so")
@@ -69,6 +72,10 @@ def lib():
     L.attn_fwd.restype = _i
     L.attn_jvp_merge.argtypes = [_vp] * 4 + [_i] * 3 + [_vp] * 5
     L.attn_jvp_merge.restype = _i
+    L.attn_bwd.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _vp, _sz, _vp]
+    L.attn_bwd.restype = _i
+    L.attn_bwd_workspace_bytes.argtypes = [_i] * 5
+    L.attn_bwd_workspace_bytes.restype = _sz
     L.attn_jvp_fwd_f32.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _vp]
     L.attn_jvp_fwd_f32.restype = _i
     L.attn_jvp_workspace_bytes.argtypes = [_i, _i, _i, _i]
@@ -324,6 +331,35 @@ def attn_jvp_merge(lse_parts, o_parts, to_parts=None, tlse_parts=None):
     if rc != OK:
         raise AttnJvpError(rc)
     return lse, o, to, tlse
+
+
+def attn_bwd_workspace_bytes(B, H, Nq, Nk, d):
+    return int(lib().attn_bwd_workspace_bytes(B, H, Nq, Nk, d))
+
+
+def attn_bwd(q, k, v, o, go, lse, scale=None, workspace=None):
+    """Backward pass: gradients (gq, gk, gv) (fp32) of a loss through O, from
+    bf16 q, k, v, the cotangent go (bf16, like q) and the forward's fp32 o
+    and lse.  Launches on the current stream."""
+    B, H, Nq, Nk, d = _check(q, k, v, go, k, v, torch.bfloat16)
+    if (not isinstance(o, torch.Tensor) or o.dtype != torch.float32 or tuple(o.shape) != (B, H, Nq, d)
+            or not o.is_contiguous() or o.device != q.device):
+        raise ValueError("o must be the forward's contiguous fp32 [B, H, Nq, d] output")
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32
+            or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be the forward's contiguous fp32 [B, H, Nq] lse")
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    gq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    gk = torch.empty((B, H, Nk, d), dtype=torch.float32, device=q.device)
+    gv = torch.empty_like(gk)
+    wp, wb = _ws_arg(workspace, q.device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(go), _ptr(lse), _ptr(gq),
+                            _ptr(gk), _ptr(gv), B, H, Nq, Nk, d, s, wp, wb, stream)
+    if rc != OK:
+        raise AttnJvpError(rc)
+    return gq, gk, gv
 
 
 def attn_jvp_fwd_f32(q, k, v, tq, tk, tv, scale=None, lse=True, out=None):

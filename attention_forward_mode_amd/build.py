@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libattn_jvp.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["attn_jvp_bf16.hip", "attn_jvp_f32.hip", "attn_jvp_merge.hip"]
+HIP_SOURCES = ["attn_jvp_bf16.hip", "attn_jvp_f32.hip", "attn_jvp_merge.hip", "attn_bwd.hip"]
 CXX_SOURCES = ["attn_jvp_api.cpp"]
 
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

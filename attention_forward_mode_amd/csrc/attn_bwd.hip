@@ -1,0 +1,538 @@
+// attn_bwd.hip -- reverse-mode derivative (backward pass) of softmax attention
+// for gfx950, bf16 inputs: FlashAttention-2's gradients of a loss through O.
+//
+// Per (b, h), with S = s Q K^T, P = row-softmax(S) = exp(S - lse), O = P V and
+// the incoming gradient gO (of the loss with respect to O):
+//   gV = P^T gO,  gP = gO V^T,  gS = P * (gP - D),  D_i = sum_j P_ij gP_ij = <gO_i, O_i>,
+//   gQ = s gS K,  gK = s gS^T Q.
+// (rCM record LIT-783 in the Anthology of the SOTA: the student is trained
+// through the attention output, "Key takeaways", "JVP at production scale".)
+//
+// Four kernels per call, all on one stream:
+//  1. pack_q: per 64 queries, a tile image of Q and gO rows (bf16, padded),
+//     Q^T and gO^T (fp16, [d][64 queries] in matrix-core operand order), and
+//     per query lse (+inf past Nq) and D = <gO_i, O_i> (fp32, from O).
+//  2. pack_k: per 64 keys, a tile image of K and V rows (bf16) and K^T (fp16).
+//  3. bwd_kv: one workgroup = 8 waves x 32 keys (K, V fragments held in
+//     registers); it streams the query tiles (direct-to-LDS copies, double
+//     buffered) and per 32-query block forms S = Q K^T and gP = gO V^T (bf16
+//     MFMA), P = exp(S - lse), gS = P (gP - D) (rounded to fp16 pairs), and
+//     accumulates gV^T += gO^T P and gK^T += Q^T gS (fp16 MFMA).
+//  4. bwd_q: one workgroup = 8 waves x 32 queries (Q, gO fragments held in
+//     registers); it streams the key tiles and per 32-key block forms
+//     S^T = K Q^T, gP^T = V gO^T, P^T, gS^T, and accumulates gQ^T += K^T gS^T.
+// Every access to global memory is a buffer access range-checked against its
+// tensor (or one (b, h) slice of the workspace).  Products: 8 (bwd_kv) + 6
+// (bwd_q) Nq x Nk x d contractions' worth of flops, S and gP formed twice.
+#include "cdna4.hpp"
+#include "launch.hpp"
+
+namespace ajvp {
+namespace bwd_path {
+
+constexpr int kTile = 64;            // keys or queries per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;   // keys (bwd_kv) or queries (bwd_q) per workgroup
+constexpr int kPackThreads = 256;
+constexpr int kDmaBytes = 1024;
+constexpr uint32_t kXcds = 8;
+
+// A tile image: NR row tiles (bf16, [64][d], rows padded by 16 bytes), NT
+// transposed tiles (fp16, [d][64], positions in operand order, rows padded),
+// and kExtra bytes of per-row data, rounded up to 8 KiB.
+template <int D, int NR, int NT, int kExtra>
+struct Img {
+  static constexpr int kRRow = D * 2 + 16;
+  static constexpr int kTRow = kTile * 2 + 16;
+  static constexpr int kRTile = kTile * kRRow;
+  static constexpr int kTTile = D * kTRow;
+  static constexpr int kOffT = NR * kRTile;
+  static constexpr int kOffX = kOffT + NT * kTTile;
+  static constexpr int kUsed = kOffX + kExtra;
+  static constexpr int kRound = kThreads * 16;
+  static constexpr int kBytes = (kUsed + kRound - 1) / kRound * kRound;
+  static constexpr int kDmaPerWave = kBytes / (kWaves * kDmaBytes);
+  static constexpr int kKS = D / 16;
+  static constexpr int kCB = D / 32;
+};
+// query image: Q, gO rows; Q^T, gO^T; lse and D in accumulator-row order
+template <int D>
+using QImg = Img<D, 2, 2, 2 * kTile * 4>;
+// key image: K, V rows; K^T
+template <int D>
+using KImg = Img<D, 2, 1, 0>;
+static_assert(QImg<128>::kBytes == 73728 && KImg<128>::kBytes == 57344, "image sizes");
+
+// Row (0..63) of a 64-row tile held at operand position `pos` of a transposed
+// row: positions 16G + 8g + e hold the rows that the accumulator of lane half
+// g puts in slots 8t + e of block G/2, t = G%2.
+__device__ inline int packed_row(int pos) {
+  const int G = pos >> 4, g = (pos >> 3) & 1, e = pos & 7;
+  return 16 * G + (e < 4 ? 4 * g + e : 8 + 4 * g + (e - 4));
+}
+// Accumulator slot r of lane half g holds row 8(r/4) + 4g + r%4 of its block.
+__device__ __attribute__((always_inline)) inline int slot_row(int r, int g) {
+  return 8 * (r >> 2) + 4 * g + (r & 3);
+}
+
+// One tile image (blockIdx.x = tile, blockIdx.y = (b, h)).  Rows past N are
+// zero; with kQuery, the extras are lse (+inf past N) and D = <gO_i, O_i>,
+// 32 floats per 32-row block in slot order (lane half g, slot r at 16 g + r).
+template <int D, bool kQuery>
+__device__ __attribute__((always_inline)) inline void pack_body(
+    const uint16_t* __restrict__ r0, const uint16_t* __restrict__ r1,
+    const uint16_t* __restrict__ t0, const uint16_t* __restrict__ t1,
+    const float* __restrict__ o, const float* __restrict__ lse, char* __restrict__ ws, int N,
+    int ntiles, uint32_t in_bytes) {
+  using G = Img<D, 2, kQuery ? 2 : 1, kQuery ? 2 * kTile * 4 : 0>;
+  constexpr int NT = kQuery ? 2 : 1;
+  __shared__ _Float16 sv[NT][kTile][D + 2];
+  __shared__ float sd[kTile];
+  const int tile = blockIdx.x;
+  const uint32_t bh = blockIdx.y;
+  const auto rr0 = make_rsrc(r0, in_bytes);
+  const auto rr1 = make_rsrc(r1, in_bytes);
+  const auto rt0 = make_rsrc(t0, in_bytes);
+  const auto rt1 = make_rsrc(t1, kQuery ? in_bytes : 0u);
+  const uint32_t slice = (uint32_t)ntiles * G::kBytes;
+  const auto rws = make_rsrc(ws + (size_t)bh * slice, slice);
+  const int row0 = tile * kTile;
+  const uint32_t img = (uint32_t)tile * G::kBytes;
+  constexpr int kC = D / 8;
+  constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
+  constexpr int kRChunks = kTile * (kC + 1);
+  for (int c = threadIdx.x; c < 2 * kRChunks; c += kPackThreads) {
+    const int t = c / kRChunks, rem = c % kRChunks, r = rem / (kC + 1), col = rem % (kC + 1);
+    u32x4 x = kZero;
+    if (col < kC && row0 + r < N)
+      x = buf_load16(t == 0 ? rr0 : rr1, ((bh * (uint32_t)N + row0 + r) * D + 8 * col) * 2);
+    buf_store16(rws, img + t * G::kRTile + r * G::kRRow + col * 16, x);
+  }
+  constexpr int kIn = kTile * kC;
+  for (int c = threadIdx.x; c < NT * kIn; c += kPackThreads) {
+    const int t = c / kIn, rem = c % kIn, r = rem / kC, col = (rem % kC) * 8;
+    u32x4 x = kZero;
+    if (row0 + r < N)
+      x = buf_load16(t == 0 ? rt0 : rt1, ((bh * (uint32_t)N + row0 + r) * D + col) * 2);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t bits = (x[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      sv[t][r][col + e] = (_Float16)__builtin_bit_cast(float, bits << 16);
+    }
+  }
+  if constexpr (kQuery) {
+    // D_i = <gO_i, O_i>: four threads per row, fp32 sums of bf16 gO times fp32 O
+    const auto ro = make_rsrc(o, in_bytes * 2);
+    for (int c = threadIdx.x; c < kTile * 4; c += kPackThreads) {
+      const int r = c / 4, part = c % 4;
+      float acc = 0.f;
+      if (row0 + r < N) {
+        for (int j = part * (D / 4); j < (part + 1) * (D / 4); j += 4) {
+          const uint32_t e = (bh * (uint32_t)N + row0 + r) * D + j;
+          const f32x4 ov = __builtin_bit_cast(f32x4, buf_load16(ro, e * 4));
+          const u32x2 gw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rt1, (int)(e * 2), 0, 0));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t bits = (gw[q >> 1] >> (16 * (q & 1))) & 0xffffu;
+            acc += __builtin_bit_cast(float, bits << 16) * ov[q];
+          }
+        }
+      }
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      if (part == 0) sd[r] = acc;
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < NT * D * 9; c += kPackThreads) {
+    const int t = c / (D * 9), rem = c % (D * 9), col = rem / 9, p = rem % 9;
+    u32x4 x = kZero;
+    if (p < 8) {
+      f16x8 h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = sv[t][packed_row(8 * p + e)][col];
+      x = __builtin_bit_cast(u32x4, h);
+    }
+    buf_store16(rws, img + G::kOffT + t * G::kTTile + col * G::kTRow + p * 16, x);
+  }
+  if constexpr (kQuery) {
+    // extras: [block b][lse | D][lane half g][slot r]
+    const auto rl = make_rsrc(lse, in_bytes / D * 2);
+    for (int c = threadIdx.x; c < 2 * kTile; c += kPackThreads) {
+      const int which = c / kTile, rem = c % kTile;       // 0: lse, 1: D
+      const int b = rem / 32, g = (rem / 16) % 2, r = rem % 16;
+      const int row = 32 * b + slot_row(r, g);
+      float val;
+      if (which == 0)
+        val = row0 + row < N ? buf_load4f(rl, (bh * (uint32_t)N + row0 + row) * 4) : INFINITY;
+      else
+        val = sd[row];
+      buf_store4(rws, img + G::kOffX + (b * 2 + which) * 128 + (g * 16 + r) * 4, val);
+    }
+  }
+  for (int off = G::kUsed + threadIdx.x * 16; off < G::kBytes; off += kPackThreads * 16)
+    buf_store16(rws, img + off, kZero);
+}
+
+template <int D, bool kQuery>
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(
+    const uint16_t* __restrict__ r0, const uint16_t* __restrict__ r1,
+    const uint16_t* __restrict__ t0, const uint16_t* __restrict__ t1,
+    const float* __restrict__ o, const float* __restrict__ lse, char* __restrict__ ws, int N,
+    int ntiles, uint32_t in_bytes) {
+  pack_body<D, kQuery>(r0, r1, t0, t1, o, lse, ws, N, ntiles, in_bytes);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Copy of tile image t into a stage: this wave's kPer consecutive KiB, lane l
+// moving bytes 16 l .. 16 l + 15 of each (LDS address = the wave-uniform stage
+// pointer + 16 l; global = image offset + 16 l).
+template <int kPer, int kBytes>
+__device__ __attribute__((always_inline)) inline void copy_image(__amdgpu_buffer_rsrc_t rimg,
+                                                                 char* stage, uint32_t wave_part,
+                                                                 int lane, int t) {
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rimg, (lds_ptr_t)(stage + wave_part + j * kDmaBytes),
+                                             16, lane * 16,
+                                             (uint32_t)t * kBytes + wave_part + j * kDmaBytes, 0, 0);
+}
+
+// Linear workgroup id -> (tile, slice): XCD x (id % 8) is given the x-th
+// contiguous range of the work list ordered by (slice, tile).
+__device__ __attribute__((always_inline)) inline void work_item(int ntile, int& tile,
+                                                                uint32_t& bh) {
+  const uint32_t wg = blockIdx.x, nwg = gridDim.x;
+  const uint32_t xcd = wg % kXcds, slot = wg / kXcds, per = nwg / kXcds, extra = nwg % kXcds;
+  const uint32_t w = xcd < extra ? xcd * (per + 1) + slot
+                                 : extra * (per + 1) + (xcd - extra) * per + slot;
+  tile = (int)(w % (uint32_t)ntile);
+  bh = w / (uint32_t)ntile;
+}
+
+struct Sizes {
+  uint32_t q_bytes, k_bytes, oq_bytes, ok_bytes;  // bf16 inputs, fp32 outputs
+};
+
+// Fragments of 32 rows of a [N, D] bf16 tensor as the B operand (lane: row
+// l32, d-slice g); rows past N read zero.
+template <int D>
+__device__ __attribute__((always_inline)) inline void load_frags(__amdgpu_buffer_rsrc_t r,
+                                                                 uint32_t row_off, bool ok,
+                                                                 int g, u32x4* f) {
+  const uint32_t base = ok ? row_off : 0x80000000u;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) f[ks] = buf_load16(r, base + (16 * ks + 8 * g) * 2);
+}
+
+// Store a [D][32] accumulator (4 blocks of 32x32; lane: column l32) as rows
+// of a [N, D] fp32 tensor, times `mul`.
+template <int D>
+__device__ __attribute__((always_inline)) inline void store_rows(__amdgpu_buffer_rsrc_t r,
+                                                                 uint32_t row_elem,
+                                                                 const f32x16* acc, int g,
+                                                                 float mul) {
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int c0 = 32 * cb + 8 * qq + 4 * g;
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[cb][4 * qq + e] * mul;
+      buf_store16(r, (row_elem + c0) * 4, __builtin_bit_cast(u32x4, v));
+    }
+}
+
+// ---- bwd_kv: gK, gV for 256 keys per workgroup --------------------------------
+template <int D, bool kMaskQ>
+__device__ __attribute__((always_inline)) inline void kv_block(
+    const char* stage, int qb, const u32x4* kf, const u32x4* vf, int l32, int g,
+    f32x16* gk, f32x16* gv, float c_log2) {
+  using G = QImg<D>;
+  const char* sQ = stage;
+  const char* sGO = stage + G::kRTile;
+  const char* sQT = stage + G::kOffT;
+  const char* sGOT = sQT + G::kTTile;
+  const char* sX = stage + G::kOffX + qb * 256 + g * 64;  // lse at +0, D at +128
+  const int rowoff = (32 * qb + l32) * G::kRRow + 16 * g;
+  // S = Q K^T, gP = gO V^T (rows: query, columns: this wave's keys)
+  f32x16 s, gp;
+#pragma unroll
+  for (int ks = 0; ks < G::kKS; ++ks) {
+    const u32x4 qa = lds_load16(sQ + rowoff + 32 * ks);
+    const u32x4 ga = lds_load16(sGO + rowoff + 32 * ks);
+    s = mma_bf16(qa, kf[ks], ks == 0 ? f32x16{} : s);
+    gp = mma_bf16(ga, vf[ks], ks == 0 ? f32x16{} : gp);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // P = 2^(S c - lse log2 e) (queries past Nq have lse = +inf, so P = 0 there),
+  // gS = P (gP - D); both rounded to fp16 pairs straight into B operands.
+  u32x4 pb[2], sb[2];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const f32x4 l4 = __builtin_bit_cast(f32x4, lds_load16(sX + 16 * q4));
+    const f32x4 d4 = __builtin_bit_cast(f32x4, lds_load16(sX + 128 + 16 * q4));
+    float pp[4], gs[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * q4 + e;
+      pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l4[e] * kLog2e));
+      gs[e] = pp[e] * (gp[r] - d4[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int q = 2 * q4 + e;
+      pb[q >> 2][q & 3] = pack_f16x2(pp[2 * e], pp[2 * e + 1]);
+      sb[q >> 2][q & 3] = pack_f16x2(gs[2 * e], gs[2 * e + 1]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // gV^T += gO^T P, gK^T += Q^T gS
+  constexpr int kSteps = 2 * G::kCB;
+  auto toff = [&](int step) {
+    const int t = step / G::kCB, cb = step % G::kCB;
+    return (32 * cb + l32) * G::kTRow + 16 * g + 16 * (4 * qb + 2 * t);
+  };
+#pragma unroll
+  for (int step = 0; step < kSteps; ++step) {
+    const int t = step / G::kCB, cb = step % G::kCB;
+    const u32x4 go_t = lds_load16(sGOT + toff(step));
+    const u32x4 q_t = lds_load16(sQT + toff(step));
+    gv[cb] = mma_f16(go_t, pb[t], gv[cb]);
+    gk[cb] = mma_f16(q_t, sb[t], gk[cb]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One query tile: the copy of the next tile image into `next` goes first, then
+// both 32-query blocks from `cur`.  The stage pointers are restrict-qualified
+// (disjoint halves of the LDS), so reads of `cur` need not wait for the copy.
+template <int D>
+__device__ __attribute__((always_inline)) inline void kv_tile(
+    char* __restrict__ next, const char* __restrict__ cur, __amdgpu_buffer_rsrc_t rimg,
+    uint32_t wave_part, int lane, int t_next, bool copy, const u32x4* kf, const u32x4* vf,
+    int l32, int g, f32x16* gk, f32x16* gv, float c_log2) {
+  using G = QImg<D>;
+  if (copy) copy_image<G::kDmaPerWave, G::kBytes>(rimg, next, wave_part, lane, t_next);
+  kv_block<D, false>(cur, 0, kf, vf, l32, g, gk, gv, c_log2);
+  kv_block<D, false>(cur, 1, kf, vf, l32, g, gk, gv, c_log2);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_kv_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const char* __restrict__ qimg, float* __restrict__ gk, float* __restrict__ gv, int Nq,
+    int Nk, int nqtiles, int nktile, Sizes sz, float scale, float c_log2) {
+  using G = QImg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::kBytes];
+  int kt;
+  uint32_t bh;
+  work_item(nktile, kt, bh);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int key = kt * kRows + wave * 32 + l32;
+  const bool key_ok = key < Nk;
+  const uint32_t slice = (uint32_t)nqtiles * G::kBytes;
+  const auto rimg = make_rsrc(qimg + (size_t)bh * slice, slice);
+  const uint32_t wave_part = (uint32_t)wave * G::kDmaPerWave * kDmaBytes;
+  copy_image<G::kDmaPerWave, G::kBytes>(rimg, smem, wave_part, lane, 0);
+  u32x4 kf[G::kKS], vf[G::kKS];
+  const uint32_t krow = (bh * (uint32_t)Nk + key) * D * 2;
+  load_frags<D>(make_rsrc(k, sz.k_bytes), krow, key_ok, g, kf);
+  load_frags<D>(make_rsrc(v, sz.k_bytes), krow, key_ok, g, vf);
+  f32x16 acc_k[G::kCB], acc_v[G::kCB];
+#pragma unroll
+  for (int cb = 0; cb < G::kCB; ++cb) {
+    acc_k[cb] = f32x16{};
+    acc_v[cb] = f32x16{};
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // the copy into the other stage starts once every wave has left the tile
+  // that last read it (the barrier at the end of each tile)
+  for (int t = 0; t < nqtiles; ++t) {
+    kv_tile<D>(smem + ((t + 1) & 1) * G::kBytes, smem + (t & 1) * G::kBytes, rimg, wave_part,
+               lane, t + 1, t + 1 < nqtiles, kf, vf, l32, g, acc_k, acc_v, c_log2);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (key_ok) {
+    const uint32_t row = (bh * (uint32_t)Nk + key) * D;
+    store_rows<D>(make_rsrc(gk, sz.ok_bytes), row, acc_k, g, scale);
+    store_rows<D>(make_rsrc(gv, sz.ok_bytes), row, acc_v, g, 1.0f);
+  }
+}
+
+// ---- bwd_q: gQ for 256 queries per workgroup --------------------------------
+template <int D, bool kMaskK>
+__device__ __attribute__((always_inline)) inline void q_block(
+    const char* stage, int kb, const u32x4* qf, const u32x4* gof, int l32, int g, f32x16* gq,
+    float c_log2, float lse2, float dq, int key0, int Nk) {
+  using G = KImg<D>;
+  const char* sK = stage;
+  const char* sV = stage + G::kRTile;
+  const char* sKT = stage + G::kOffT;
+  const int rowoff = (32 * kb + l32) * G::kRRow + 16 * g;
+  // S^T = K Q^T, gP^T = V gO^T (rows: key, columns: this wave's queries)
+  f32x16 s, gp;
+#pragma unroll
+  for (int ks = 0; ks < G::kKS; ++ks) {
+    const u32x4 ka = lds_load16(sK + rowoff + 32 * ks);
+    const u32x4 va = lds_load16(sV + rowoff + 32 * ks);
+    s = mma_bf16(ka, qf[ks], ks == 0 ? f32x16{} : s);
+    gp = mma_bf16(va, gof[ks], ks == 0 ? f32x16{} : gp);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // gS^T = P^T (gP^T - D), P^T = 2^(S^T c - lse log2 e); keys past Nk: 0
+  u32x4 sb[2];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    float gs[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 2 * q + e;
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -lse2));
+      if (kMaskK && key0 + slot_row(r, g) >= Nk) p = 0.f;
+      gs[e] = p * (gp[r] - dq);
+    }
+    sb[q >> 2][q & 3] = pack_f16x2(gs[0], gs[1]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // gQ^T += K^T gS^T
+  constexpr int kSteps = 2 * G::kCB;
+#pragma unroll
+  for (int step = 0; step < kSteps; ++step) {
+    const int t = step / G::kCB, cb = step % G::kCB;
+    const u32x4 kt =
+        lds_load16(sKT + (32 * cb + l32) * G::kTRow + 16 * g + 16 * (4 * kb + 2 * t));
+    gq[cb] = mma_f16(kt, sb[t], gq[cb]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int D>
+__device__ __attribute__((always_inline)) inline void q_tile(
+    char* __restrict__ next, const char* __restrict__ cur, __amdgpu_buffer_rsrc_t rimg,
+    uint32_t wave_part, int lane, int t_next, const u32x4* qf, const u32x4* gof, int l32, int g,
+    f32x16* gq, float c_log2, float lse2, float dq, int Nk) {
+  using G = KImg<D>;
+  copy_image<G::kDmaPerWave, G::kBytes>(rimg, next, wave_part, lane, t_next);
+  q_block<D, false>(cur, 0, qf, gof, l32, g, gq, c_log2, lse2, dq, 0, Nk);
+  q_block<D, false>(cur, 1, qf, gof, l32, g, gq, c_log2, lse2, dq, 0, Nk);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ go,
+    const float* __restrict__ lse, const char* __restrict__ qimg, const char* __restrict__ kimg,
+    float* __restrict__ gq, int Nq, int Nk, int nqtiles, int nktiles, int nqtile, Sizes sz,
+    float scale, float c_log2) {
+  using G = KImg<D>;
+  using GQ = QImg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::kBytes];
+  int qt;
+  uint32_t bh;
+  work_item(nqtile, qt, bh);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int row = qt * kRows + wave * 32 + l32;
+  const bool row_ok = row < Nq;
+  const uint32_t slice = (uint32_t)nktiles * G::kBytes;
+  const auto rimg = make_rsrc(kimg + (size_t)bh * slice, slice);
+  const uint32_t wave_part = (uint32_t)wave * G::kDmaPerWave * kDmaBytes;
+  copy_image<G::kDmaPerWave, G::kBytes>(rimg, smem, wave_part, lane, 0);
+  u32x4 qf[G::kKS], gof[G::kKS];
+  const uint32_t qrow = (bh * (uint32_t)Nq + row) * D * 2;
+  load_frags<D>(make_rsrc(q, sz.q_bytes), qrow, row_ok, g, qf);
+  load_frags<D>(make_rsrc(go, sz.q_bytes), qrow, row_ok, g, gof);
+  // this row's lse and D, from the query image's extras (written by pack_q)
+  float lse2 = 0.f, dq = 0.f;
+  {
+    const uint32_t qslice = (uint32_t)nqtiles * GQ::kBytes;
+    const auto rq = make_rsrc(qimg + (size_t)bh * qslice, qslice);
+    const int in_tile = row % kTile, blk = in_tile / 32, r32 = in_tile % 32;
+    // slot of row r32 within its block: r32 = 8(r/4) + 4 gg + r%4
+    const int gg = (r32 >> 2) & 1, r = ((r32 >> 3) << 2) | (r32 & 3);
+    const uint32_t x = (uint32_t)(row / kTile) * GQ::kBytes + GQ::kOffX + blk * 256 + (gg * 16 + r) * 4;
+    lse2 = buf_load4f(rq, x) * kLog2e;
+    dq = buf_load4f(rq, x + 128);
+  }
+  f32x16 acc[G::kCB];
+#pragma unroll
+  for (int cb = 0; cb < G::kCB; ++cb) acc[cb] = f32x16{};
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int kLast = nktiles - 1;
+  for (int t = 0; t < kLast; ++t) {
+    q_tile<D>(smem + ((t + 1) & 1) * G::kBytes, smem + (t & 1) * G::kBytes, rimg, wave_part,
+              lane, t + 1, qf, gof, l32, g, acc, c_log2, lse2, dq, Nk);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  {
+    const char* cur = smem + (kLast & 1) * G::kBytes;
+    q_block<D, true>(cur, 0, qf, gof, l32, g, acc, c_log2, lse2, dq, kLast * kTile, Nk);
+    q_block<D, true>(cur, 1, qf, gof, l32, g, acc, c_log2, lse2, dq, kLast * kTile + 32, Nk);
+  }
+  if (row_ok)
+    store_rows<D>(make_rsrc(gq, sz.oq_bytes), (bh * (uint32_t)Nq + row) * D, acc, g, scale);
+}
+
+template <int D>
+hipError_t launch_d(const void* q, const void* k, const void* v, const float* o, const void* go,
+                    const float* lse, float* gq, float* gk, float* gv, int B, int H, int Nq,
+                    int Nk, float scale, char* ws, hipStream_t stream) {
+  const int bh = B * H;
+  const int nqt = (Nq + kTile - 1) / kTile, nkt = (Nk + kTile - 1) / kTile;
+  char* qimg = ws;
+  char* kimg = ws + (size_t)bh * nqt * QImg<D>::kBytes;
+  const uint32_t qb = (uint32_t)((size_t)bh * Nq * D * 2), kb = (uint32_t)((size_t)bh * Nk * D * 2);
+  hipLaunchKernelGGL((pack_kernel<D, true>), dim3(nqt, bh), dim3(kPackThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(go),
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(go), o, lse,
+                     qimg, Nq, nqt, qb);
+  hipLaunchKernelGGL((pack_kernel<D, false>), dim3(nkt, bh), dim3(kPackThreads), 0, stream,
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                     static_cast<const uint16_t*>(k), nullptr, nullptr, nullptr, kimg, Nk, nkt,
+                     kb);
+  Sizes sz;
+  sz.q_bytes = qb;
+  sz.k_bytes = kb;
+  sz.oq_bytes = (uint32_t)((size_t)bh * Nq * D * 4);
+  sz.ok_bytes = (uint32_t)((size_t)bh * Nk * D * 4);
+  const int nkw = (Nk + kRows - 1) / kRows, nqw = (Nq + kRows - 1) / kRows;
+  hipLaunchKernelGGL((bwd_kv_kernel<D>), dim3(nkw * bh), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), qimg, gk,
+                     gv, Nq, Nk, nqt, nkw, sz, scale, scale * kLog2e);
+  hipLaunchKernelGGL((bwd_q_kernel<D>), dim3(nqw * bh), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(go), lse, qimg,
+                     kimg, gq, Nq, Nk, nqt, nkt, nqw, sz, scale, scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace bwd_path
+
+size_t bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  using namespace bwd_path;
+  const size_t nqt = ((size_t)Nq + kTile - 1) / kTile, nkt = ((size_t)Nk + kTile - 1) / kTile;
+  const size_t qi = d == 128 ? QImg<128>::kBytes : QImg<64>::kBytes;
+  const size_t ki = d == 128 ? KImg<128>::kBytes : KImg<64>::kBytes;
+  return (size_t)B * H * (nqt * qi + nkt * ki);
+}
+
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const float* o, const void* go,
+                      const float* lse, float* gq, float* gk, float* gv, int B, int H, int Nq,
+                      int Nk, int d, float scale, void* ws, hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  return d == 128 ? bwd_path::launch_d<128>(q, k, v, o, go, lse, gq, gk, gv, B, H, Nq, Nk, scale,
+                                            w, stream)
+                  : bwd_path::launch_d<64>(q, k, v, o, go, lse, gq, gk, gv, B, H, Nq, Nk, scale,
+                                           w, stream);
+}
+
+}  // namespace ajvp

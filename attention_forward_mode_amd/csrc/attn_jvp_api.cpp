@@ -255,6 +255,48 @@ int attn_jvp_merge(const float* lse_parts, const float* o_parts, const float* to
   return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
 }
 
+size_t attn_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128)) return 0;
+  return ajvp::bwd_workspace_bytes(B, H, Nq, Nk, d);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const float* o, const void* go,
+             const float* lse, float* gq, float* gk, float* gv, int B, int H, int Nq, int Nk,
+             int d, float scale, void* workspace, size_t workspace_bytes,
+             attn_jvp_stream_t stream) {
+  const void* need[9] = {q, k, v, o, go, lse, gq, gk, gv};
+  for (int i = 0; i < 9; ++i)
+    if (need[i] == nullptr) return ATTN_JVP_EINVAL;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || bad_scale(scale)) return ATTN_JVP_EINVAL;
+  int rc = check_sizes(B, H, Nq, Nk, d, 2);
+  if (rc != ATTN_JVP_OK) return rc;
+  // one (b, h) slice of each half of the workspace stays under 2^31 bytes
+  if (int64_t(ajvp::bwd_workspace_bytes(1, 1, Nq, Nk, d)) >= kMaxTensorBytes ||
+      int64_t(B) * H * Nk * d * 4 >= kMaxTensorBytes)
+    return ATTN_JVP_EUNSUPPORTED;
+  const void* al16[8] = {q, k, v, o, go, gq, gk, gv};
+  for (const void* p : al16)
+    if (misaligned(p, 16)) return ATTN_JVP_EALIGN;
+  if (misaligned(lse, 4)) return ATTN_JVP_EALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const size_t need_ws = ajvp::bwd_workspace_bytes(B, H, Nq, Nk, d);
+  auto launch = [&](void* ws) {
+    return ajvp::launch_bwd(q, k, v, o, go, lse, gq, gk, gv, B, H, Nq, Nk, d, scale, ws, st);
+  };
+  if (workspace != nullptr) {
+    if (workspace_bytes < need_ws) return ATTN_JVP_EINVAL;
+    if (misaligned(workspace, 256)) return ATTN_JVP_EALIGN;
+    return launch(workspace) == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+  }
+  hipMemPool_t pool = nullptr;
+  if (device_pool(&pool) != hipSuccess) return ATTN_JVP_ELAUNCH;
+  void* ws = nullptr;
+  if (hipMallocFromPoolAsync(&ws, need_ws, pool, st) != hipSuccess) return ATTN_JVP_ELAUNCH;
+  const hipError_t e = launch(ws);
+  const hipError_t f = hipFreeAsync(ws, st);
+  return (e == hipSuccess && f == hipSuccess) ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+}
+
 int attn_jvp_fwd_f32(const float* q, const float* k, const float* v, const float* tq,
                      const float* tk, const float* tv, float* o, float* to, float* lse, int B,
                      int H, int Nq, int Nk, int d, float scale, attn_jvp_stream_t stream) {

@@ -43,6 +43,12 @@ hipError_t launch_merge(const float* lse_p, const float* o_p, const float* to_p,
                         const float* tlse_p, int P, int R, int d, float* lse, float* o,
                         float* to, float* tlse, hipStream_t stream);
 
+// Backward pass (gradients of a loss through O): workspace bytes and launch.
+size_t bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const float* o, const void* go,
+                      const float* lse, float* gq, float* gk, float* gv, int B, int H, int Nq,
+                      int Nk, int d, float scale, void* workspace, hipStream_t stream);
+
 hipError_t launch_f32(const float* q, const float* k, const float* v, const float* tq,
                       const float* tk, const float* tv, float* o, float* to, float* lse,
                       int B, int H, int Nq, int Nk, int d, float scale, hipStream_t stream);

@@ -119,7 +119,8 @@ def calib_copy(nbytes=1 << 30, reps=5):
 
 
 # flops per (b, h) and Nq Nk d of each mode: the contractions it performs
-MODE_FLOPS = {"jvp": 12.0, "frozen": 8.0, "fwd": 4.0}
+# (bwd: S, gP, gV, gQ, gK; the kernels form S and gP twice, 14 Nq Nk d in all)
+MODE_FLOPS = {"jvp": 12.0, "frozen": 8.0, "fwd": 4.0, "bwd": 10.0}
 
 
 def bench_variant(args, ajvp, w, g, x, scale):
@@ -130,9 +131,18 @@ def bench_variant(args, ajvp, w, g, x, scale):
     B, H, Nq, d = g["q"].shape
     Nk = g["k"].shape[2]
     out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
-    ws = torch.empty(ajvp.attn_jvp_workspace_bytes(B, H, Nk, d), dtype=torch.uint8, device="cuda")
+    if args.mode == "bwd":
+        ws = torch.empty(ajvp.attn_bwd_workspace_bytes(B, H, Nq, Nk, d), dtype=torch.uint8,
+                         device="cuda")
+        o_f, lse_f = ajvp.attn_fwd(g["q"], g["k"], g["v"], scale=scale)
+    else:
+        ws = torch.empty(ajvp.attn_jvp_workspace_bytes(B, H, Nk, d), dtype=torch.uint8,
+                         device="cuda")
 
     def step():
+        if args.mode == "bwd":  # the cotangent gO is the dQ draw, N(0, 0.1^2)
+            return ajvp.attn_bwd(g["q"], g["k"], g["v"], o_f, g["dq"], lse_f, scale=scale,
+                                 workspace=ws)
         if args.mode == "fwd":
             return ajvp.attn_fwd(g["q"], g["k"], g["v"], scale=scale, out_dtype=out_dtype,
                                  workspace=ws)
@@ -160,7 +170,7 @@ def bench_variant(args, ajvp, w, g, x, scale):
     fl = MODE_FLOPS[args.mode] * B * H * Nq * Nk * d
     tflops = fl / (ms / 1e3) / 1e12
     names = {"jvp": "attn+JVP", "frozen": "attn+JVP with frozen keys (dK = dV = 0)",
-             "fwd": "forward attention"}
+             "fwd": "forward attention", "bwd": "attention backward (gradients through O)"}
     res = {
         "metric": f"{names[args.mode]} TFLOP/s at 1 GPU ({args.workload})",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -169,11 +179,13 @@ def bench_variant(args, ajvp, w, g, x, scale):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded Gaussians)",
         "config": {"workload": f"{w.name}: {w.description}", "B": B, "H": H, "Nq": Nq, "Nk": Nk,
                    "d": d, "scale": scale, "mode": args.mode,
-                   "outputs": f"{args.out_dtype} O" + ("" if args.mode == "fwd" else ", dO") +
-                              ", fp32 lse"},
+                   "outputs": ("fp32 gQ, gK, gV" if args.mode == "bwd" else
+                               f"{args.out_dtype} O" + ("" if args.mode == "fwd" else ", dO") +
+                               ", fp32 lse")},
         "flops_per_step": fl,
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"kernel": "pack_kv + attn_jvp_bf16 (one call, pack included)",
+        "roofline": {"kernel": ("pack_q + pack_k + bwd_kv + bwd_q (one call)" if args.mode == "bwd"
+                                else "pack_kv + attn_jvp_bf16 (one call, pack included)"),
                      "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
@@ -187,9 +199,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video_1p3b")
-    ap.add_argument("--mode", choices=["jvp", "frozen", "fwd"], default="jvp",
+    ap.add_argument("--mode", choices=["jvp", "frozen", "fwd", "bwd"], default="jvp",
                     help="jvp: the full attention+JVP (the headline); frozen: dK = dV = 0 passed "
-                         "as NULL (8 Nq Nk d flops); fwd: forward attention alone (4 Nq Nk d)")
+                         "as NULL (8 Nq Nk d flops); fwd: forward attention alone (4 Nq Nk d); "
+                         "bwd: the backward pass, gradients through O (10 Nq Nk d algorithmic)")
     ap.add_argument("--out-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")

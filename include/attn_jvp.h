@@ -214,6 +214,35 @@ ATTN_JVP_API int attn_jvp_merge(const float *lse_parts, const float *o_parts,
                    attn_jvp_stream_t stream);
 
 /*
+ * Backward pass of the same attention (FlashAttention-2's reverse mode): the
+ * gradients of a loss L with respect to Q, K and V, given gO = dL/dO.  Per
+ * (b, h), with P = softmax(scale Q K^T) = exp(scale Q K^T - lse):
+ *   gV = P^T gO,  gS = P * (gO V^T - D),  D_i = <gO_i, O_i>,
+ *   gQ = scale gS K,  gK = scale gS^T Q.
+ *   q, k, v, go  bf16 [B, H, Nq|Nk, d] (go like q)
+ *   o, lse       the forward's fp32 O [B, H, Nq, d] and lse [B, H, Nq] for the
+ *                same q, k, v, scale (attn_fwd or attn_jvp_fwd output)
+ *   gq, gk, gv   fp32 outputs, [B, H, Nq, d], [B, H, Nk, d], [B, H, Nk, d]
+ *   workspace    NULL (library pool) or at least attn_bwd_workspace_bytes(B, H,
+ *                Nq, Nk, d) bytes, 256-byte aligned (then nothing is allocated)
+ * bf16 products with fp32 accumulation; P and the softmax gradient gS are
+ * rounded to fp16 for the products with gO^T, Q^T and K^T.  Errors as
+ * attn_jvp_fwd (EINVAL: a NULL pointer, sizes < 1, bad scale, short
+ * workspace; EUNSUPPORTED: d, B*H, or a tensor / workspace slice of 2^31
+ * bytes; EALIGN: 16-byte tensors, 4-byte lse, 256-byte workspace).
+ */
+ATTN_JVP_API int attn_bwd(const void *q, const void *k, const void *v,
+             const float *o, const void *go, const float *lse,
+             float *gq, float *gk, float *gv,
+             int B, int H, int Nq, int Nk, int d, float scale,
+             void *workspace, size_t workspace_bytes,
+             attn_jvp_stream_t stream);
+
+/* Workspace bytes of attn_bwd (tile images of Q, gO and of K, V); 0 if a size
+ * is invalid. */
+ATTN_JVP_API size_t attn_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+
+/*
  * The same operation with fp32 inputs and fp32 arithmetic throughout (the
  * precision reference path).  Same layouts, arguments and errors; needs no
  * workspace and allocates nothing.
