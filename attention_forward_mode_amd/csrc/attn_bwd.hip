@@ -325,12 +325,17 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_kv_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const char* __restrict__ qimg, float* __restrict__ gk, float* __restrict__ gv, int Nq,
-    int Nk, int nqtiles, int nktile, Sizes sz, float scale, float c_log2) {
+    int Nk, int nqtiles, int nktile, int nsplit, Sizes sz, float scale, float c_log2) {
   using G = QImg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * G::kBytes];
-  int kt;
+  // work item: key tile kt of slice bh, over query tiles [t0, t1) of split
+  // `split`; with several splits the outputs are partial sums, one array each
+  int tile;
   uint32_t bh;
-  work_item(nktile, kt, bh);
+  work_item(nktile * nsplit, tile, bh);
+  const int kt = tile % nktile, split = tile / nktile;
+  const int t0 = split * nqtiles / nsplit, t1 = (split + 1) * nqtiles / nsplit;
+  const size_t part = (size_t)split * (sz.ok_bytes / 4);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_kernel(
   const uint32_t slice = (uint32_t)nqtiles * G::kBytes;
   const auto rimg = make_rsrc(qimg + (size_t)bh * slice, slice);
   const uint32_t wave_part = (uint32_t)wave * G::kDmaPerWave * kDmaBytes;
-  copy_image<G::kDmaPerWave, G::kBytes>(rimg, smem, wave_part, lane, 0);
+  copy_image<G::kDmaPerWave, G::kBytes>(rimg, smem, wave_part, lane, t0);
   u32x4 kf[G::kKS], vf[G::kKS];
   const uint32_t krow = (bh * (uint32_t)Nk + key) * D * 2;
   load_frags<D>(make_rsrc(k, sz.k_bytes), krow, key_ok, g, kf);
@@ -354,16 +359,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_kernel(
   __syncthreads();
   // the copy into the other stage starts once every wave has left the tile
   // that last read it (the barrier at the end of each tile)
-  for (int t = 0; t < nqtiles; ++t) {
-    kv_tile<D>(smem + ((t + 1) & 1) * G::kBytes, smem + (t & 1) * G::kBytes, rimg, wave_part,
-               lane, t + 1, t + 1 < nqtiles, kf, vf, l32, g, acc_k, acc_v, c_log2);
+  for (int t = t0; t < t1; ++t) {
+    const int i = t - t0;
+    kv_tile<D>(smem + ((i + 1) & 1) * G::kBytes, smem + (i & 1) * G::kBytes, rimg, wave_part,
+               lane, t + 1, t + 1 < t1, kf, vf, l32, g, acc_k, acc_v, c_log2);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   if (key_ok) {
     const uint32_t row = (bh * (uint32_t)Nk + key) * D;
-    store_rows<D>(make_rsrc(gk, sz.ok_bytes), row, acc_k, g, scale);
-    store_rows<D>(make_rsrc(gv, sz.ok_bytes), row, acc_v, g, 1.0f);
+    store_rows<D>(make_rsrc(gk + part, sz.ok_bytes), row, acc_k, g, scale);
+    store_rows<D>(make_rsrc(gv + part, sz.ok_bytes), row, acc_v, g, 1.0f);
   }
 }
 
@@ -429,14 +435,19 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ go,
     const float* __restrict__ lse, const char* __restrict__ qimg, const char* __restrict__ kimg,
-    float* __restrict__ gq, int Nq, int Nk, int nqtiles, int nktiles, int nqtile, Sizes sz,
-    float scale, float c_log2) {
+    float* __restrict__ gq, int Nq, int Nk, int nqtiles, int nktiles, int nqtile, int nsplit,
+    Sizes sz, float scale, float c_log2) {
   using G = KImg<D>;
   using GQ = QImg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * G::kBytes];
-  int qt;
+  // work item: query tile qt of slice bh, over key tiles [k0, k1) of split
+  // `split` (partial sums, one array per split, when there are several)
+  int tile;
   uint32_t bh;
-  work_item(nqtile, qt, bh);
+  work_item(nqtile * nsplit, tile, bh);
+  const int qt = tile % nqtile, split = tile / nqtile;
+  const int k0 = split * nktiles / nsplit, k1 = (split + 1) * nktiles / nsplit;
+  const size_t part = (size_t)split * (sz.oq_bytes / 4);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
@@ -445,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
   const uint32_t slice = (uint32_t)nktiles * G::kBytes;
   const auto rimg = make_rsrc(kimg + (size_t)bh * slice, slice);
   const uint32_t wave_part = (uint32_t)wave * G::kDmaPerWave * kDmaBytes;
-  copy_image<G::kDmaPerWave, G::kBytes>(rimg, smem, wave_part, lane, 0);
+  copy_image<G::kDmaPerWave, G::kBytes>(rimg, smem, wave_part, lane, k0);
   u32x4 qf[G::kKS], gof[G::kKS];
   const uint32_t qrow = (bh * (uint32_t)Nq + row) * D * 2;
   load_frags<D>(make_rsrc(q, sz.q_bytes), qrow, row_ok, g, qf);
@@ -467,20 +478,74 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
   for (int cb = 0; cb < G::kCB; ++cb) acc[cb] = f32x16{};
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const int kLast = nktiles - 1;
-  for (int t = 0; t < kLast; ++t) {
-    q_tile<D>(smem + ((t + 1) & 1) * G::kBytes, smem + (t & 1) * G::kBytes, rimg, wave_part,
+  const int kLast = k1 - 1;
+  for (int t = k0; t < kLast; ++t) {
+    const int i = t - k0;
+    q_tile<D>(smem + ((i + 1) & 1) * G::kBytes, smem + (i & 1) * G::kBytes, rimg, wave_part,
               lane, t + 1, qf, gof, l32, g, acc, c_log2, lse2, dq, Nk);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   {
-    const char* cur = smem + (kLast & 1) * G::kBytes;
-    q_block<D, true>(cur, 0, qf, gof, l32, g, acc, c_log2, lse2, dq, kLast * kTile, Nk);
-    q_block<D, true>(cur, 1, qf, gof, l32, g, acc, c_log2, lse2, dq, kLast * kTile + 32, Nk);
+    // keys past Nk exist only in the last tile of the last split
+    const char* cur = smem + ((kLast - k0) & 1) * G::kBytes;
+    const int kl = kLast * kTile;
+    if (k1 == nktiles) {
+      q_block<D, true>(cur, 0, qf, gof, l32, g, acc, c_log2, lse2, dq, kl, Nk);
+      q_block<D, true>(cur, 1, qf, gof, l32, g, acc, c_log2, lse2, dq, kl + 32, Nk);
+    } else {
+      q_block<D, false>(cur, 0, qf, gof, l32, g, acc, c_log2, lse2, dq, kl, Nk);
+      q_block<D, false>(cur, 1, qf, gof, l32, g, acc, c_log2, lse2, dq, kl + 32, Nk);
+    }
   }
   if (row_ok)
-    store_rows<D>(make_rsrc(gq, sz.oq_bytes), (bh * (uint32_t)Nq + row) * D, acc, g, scale);
+    store_rows<D>(make_rsrc(gq + part, sz.oq_bytes), (bh * (uint32_t)Nq + row) * D, acc, g,
+                  scale);
+}
+
+// out[i] = sum_s parts[s n + i], i < n (n a multiple of 4); fp32
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ parts,
+                                                        float* __restrict__ out, int nsplit,
+                                                        uint32_t n) {
+  const auto rp = make_rsrc(parts, (uint32_t)((size_t)nsplit * n * 4));
+  const auto ro = make_rsrc(out, n * 4);
+  for (uint32_t i = (blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += gridDim.x * 256 * 4) {
+    f32x4 acc = __builtin_bit_cast(f32x4, buf_load16(rp, i * 4));
+    for (int s = 1; s < nsplit; ++s)
+      acc += __builtin_bit_cast(f32x4, buf_load16(rp, ((uint32_t)s * n + i) * 4));
+    buf_store16(ro, i * 4, __builtin_bit_cast(u32x4, acc));
+  }
+}
+
+// Splits of the query range (gK, gV kernel) and of the key range (gQ kernel):
+// enough workgroups for two rounds over 256 CUs, partial arrays under 2^31 B.
+constexpr int kTargetGroups = 512;
+inline int pick_split(int groups, int tiles, size_t part_bytes) {
+  int n = (kTargetGroups + groups - 1) / groups;
+  n = n < 1 ? 1 : (n > tiles ? tiles : n);
+  while (n > 1 && (size_t)n * part_bytes >= ((size_t)1 << 31)) --n;
+  return n;
+}
+struct Plan {
+  int nqt, nkt, nkw, nqw, split_kv, split_q;
+  size_t qimg, kimg, pkv, pq;  // bytes of each workspace part
+};
+template <int D>
+Plan plan(int B, int H, int Nq, int Nk) {
+  Plan p;
+  const size_t bh = (size_t)B * H;
+  p.nqt = (Nq + kTile - 1) / kTile;
+  p.nkt = (Nk + kTile - 1) / kTile;
+  p.nkw = (Nk + kRows - 1) / kRows;
+  p.nqw = (Nq + kRows - 1) / kRows;
+  const size_t kbytes = bh * Nk * D * 4, qbytes = bh * Nq * D * 4;
+  p.split_kv = pick_split(p.nkw * (int)bh, p.nqt, kbytes);
+  p.split_q = pick_split(p.nqw * (int)bh, p.nkt, qbytes);
+  p.qimg = bh * p.nqt * QImg<D>::kBytes;
+  p.kimg = bh * p.nkt * KImg<D>::kBytes;
+  p.pkv = p.split_kv > 1 ? 2 * (size_t)p.split_kv * kbytes : 0;
+  p.pq = p.split_q > 1 ? (size_t)p.split_q * qbytes : 0;
+  return p;
 }
 
 template <int D>
@@ -488,9 +553,12 @@ hipError_t launch_d(const void* q, const void* k, const void* v, const float* o,
                     const float* lse, float* gq, float* gk, float* gv, int B, int H, int Nq,
                     int Nk, float scale, char* ws, hipStream_t stream) {
   const int bh = B * H;
-  const int nqt = (Nq + kTile - 1) / kTile, nkt = (Nk + kTile - 1) / kTile;
+  const Plan p = plan<D>(B, H, Nq, Nk);
+  const int nqt = p.nqt, nkt = p.nkt;
   char* qimg = ws;
-  char* kimg = ws + (size_t)bh * nqt * QImg<D>::kBytes;
+  char* kimg = qimg + p.qimg;
+  float* pkv = reinterpret_cast<float*>(kimg + p.kimg);
+  float* pq = reinterpret_cast<float*>(kimg + p.kimg + p.pkv);
   const uint32_t qb = (uint32_t)((size_t)bh * Nq * D * 2), kb = (uint32_t)((size_t)bh * Nk * D * 2);
   hipLaunchKernelGGL((pack_kernel<D, true>), dim3(nqt, bh), dim3(kPackThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(go),
@@ -505,13 +573,26 @@ hipError_t launch_d(const void* q, const void* k, const void* v, const float* o,
   sz.k_bytes = kb;
   sz.oq_bytes = (uint32_t)((size_t)bh * Nq * D * 4);
   sz.ok_bytes = (uint32_t)((size_t)bh * Nk * D * 4);
-  const int nkw = (Nk + kRows - 1) / kRows, nqw = (Nq + kRows - 1) / kRows;
-  hipLaunchKernelGGL((bwd_kv_kernel<D>), dim3(nkw * bh), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), qimg, gk,
-                     gv, Nq, Nk, nqt, nkw, sz, scale, scale * kLog2e);
-  hipLaunchKernelGGL((bwd_q_kernel<D>), dim3(nqw * bh), dim3(kThreads), 0, stream,
+  const size_t nk_elems = (size_t)bh * Nk * D;
+  float* ok = p.split_kv > 1 ? pkv : gk;
+  float* ov = p.split_kv > 1 ? pkv + (size_t)p.split_kv * nk_elems : gv;
+  float* oq = p.split_q > 1 ? pq : gq;
+  hipLaunchKernelGGL((bwd_kv_kernel<D>), dim3(p.nkw * bh * p.split_kv), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), qimg, ok,
+                     ov, Nq, Nk, nqt, p.nkw, p.split_kv, sz, scale, scale * kLog2e);
+  hipLaunchKernelGGL((bwd_q_kernel<D>), dim3(p.nqw * bh * p.split_q), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(go), lse, qimg,
-                     kimg, gq, Nq, Nk, nqt, nkt, nqw, sz, scale, scale * kLog2e);
+                     kimg, oq, Nq, Nk, nqt, nkt, p.nqw, p.split_q, sz, scale, scale * kLog2e);
+  auto sum = [&](const float* parts, float* out, int n, size_t elems) {
+    const size_t want = (elems / 4 + 255) / 256;
+    hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)(want < 4096 ? want : 4096)), dim3(256),
+                       0, stream, parts, out, n, (uint32_t)elems);
+  };
+  if (p.split_kv > 1) {
+    sum(ok, gk, p.split_kv, nk_elems);
+    sum(ov, gv, p.split_kv, nk_elems);
+  }
+  if (p.split_q > 1) sum(oq, gq, p.split_q, (size_t)bh * Nq * D);
   return hipGetLastError();
 }
 
@@ -519,10 +600,8 @@ hipError_t launch_d(const void* q, const void* k, const void* v, const float* o,
 
 size_t bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
   using namespace bwd_path;
-  const size_t nqt = ((size_t)Nq + kTile - 1) / kTile, nkt = ((size_t)Nk + kTile - 1) / kTile;
-  const size_t qi = d == 128 ? QImg<128>::kBytes : QImg<64>::kBytes;
-  const size_t ki = d == 128 ? KImg<128>::kBytes : KImg<64>::kBytes;
-  return (size_t)B * H * (nqt * qi + nkt * ki);
+  const Plan p = d == 128 ? plan<128>(B, H, Nq, Nk) : plan<64>(B, H, Nq, Nk);
+  return p.qimg + p.kimg + p.pkv + p.pq;
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const float* o, const void* go,

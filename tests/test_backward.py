@@ -95,6 +95,20 @@ def test_backward_video_full_size():
     assert torch.isfinite(gk).all() and torch.isfinite(gv).all()
 
 
+def test_backward_text_cross_full_size():
+    """The cross-attention shape (32760 queries x 512 keys, 12 heads) at the
+    launch configuration the benchmark times (the gK/gV kernel split over
+    query ranges, partial sums added by a second kernel): heads 0 and 11
+    against the oracle in full."""
+    x, s = make_inputs("text_cross")
+    g = to_device(x)
+    gq, gk, gv = _run(g, s)
+    for h in (0, 11):
+        sub = {n: x[n][:, h:h + 1].contiguous() for n in ("q", "k", "v", "dq")}
+        want = oracle.attention_vjp(sub["q"], sub["k"], sub["v"], sub["dq"], s)
+        _gate(f"bwd text_cross head {h}", (gq[:, h:h + 1], gk[:, h:h + 1], gv[:, h:h + 1]), want)
+
+
 def test_backward_workspace_and_pool_agree():
     x, s = make_inputs("image_dit", Nq=333, Nk=271, heads=[0, 1, 2])
     g = to_device(x)
