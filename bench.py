@@ -209,8 +209,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the kernel shards by head; see the design notes for the multi-GPU layout)",
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard by head, one all-to-all before and after the kernel)",
               file=sys.stderr)
         sys.exit(2)
 
