@@ -10,10 +10,11 @@
 // Two kernels per call:
 //  1. pack_kv: K, dK, V, dV -> one "tile image" per 64 keys in the workspace,
 //     byte for byte the LDS layout the fused kernel computes from: K and dK
-//     rows (bf16, padded), then V^T and dV^T (fp16, [d][64 keys] in
-//     matrix-core operand order, padded), zero past Nk.  HBM bound, under 1%
-//     of the fused kernel's time at N = 32760.  fp16 instead of bf16 for the
-//     second contraction keeps P and P*dS at 11 significant bits.
+//     (bf16), then V^T and dV^T (fp16), each stored as the sequence of
+//     matrix-core operand fragments the waves read (1 KiB per fragment, lane l
+//     at bytes 16 l .. 16 l + 15), zero past Nk.  HBM bound, under 1% of the
+//     fused kernel's time at N = 32760.  fp16 instead of bf16 for the second
+//     contraction keeps P and P*dS at 11 significant bits.
 //  2. attn_jvp_bf16: one workgroup = 8 waves x 32 query rows of one (b, h),
 //     two waves per SIMD.  Per 64-key tile the waves copy the next tile image
 //     from the workspace straight into LDS (buffer loads with the LDS-direct
@@ -64,17 +65,17 @@ struct Mode {
 };
 
 // Tile image of 64 keys: K | dK | V^T | dV^T (without dK and dV when kKV is
-// false), rounded up to a whole number of workgroup-wide copy rounds.
+// false), each part a sequence of 1 KiB operand fragments in the order the
+// waves read them: a wave's 16-byte read is lane l at fragment base + 16 l,
+// consecutive lanes on consecutive bytes (no bank conflicts, no padding), and
+// every address is the per-lane 16 l plus a constant.
+//   K, dK:     fragment kb * kKS + ks = keys 32 kb + (l % 32), d 16 ks + 8 (l / 32) .. +8
+//   V^T, dV^T: fragment (2 kb + t) kCB + cb = d 32 cb + (l % 32), keys at packed
+//              positions 8 (4 kb + 2 t + l / 32) .. +8 (packed_key)
 template <int D, bool kKV>
 struct Geo {
-  // LDS rows are padded by 16 bytes: the 16 rows that one phase of a 16-byte
-  // matrix-operand read touches then start 16 bytes apart modulo the bank
-  // width, so the reads are conflict-free, and every address is a per-lane
-  // base plus a constant.
-  static constexpr int kKRow = D * 2 + 16;                // K, dK: 64 key rows
-  static constexpr int kVRow = kBC * 2 + 16;              // V^T, dV^T: D rows of 64 keys
-  static constexpr int kKTile = kBC * kKRow;
-  static constexpr int kVTile = D * kVRow;
+  static constexpr int kKTile = kBC * D * 2;              // K, dK: 64 keys x D bf16
+  static constexpr int kVTile = D * kBC * 2;              // V^T, dV^T: D x 64 keys fp16
   static constexpr int kNT = kKV ? 2 : 1;                 // tiles per kind
   static constexpr int kOffdK = kKTile;
   static constexpr int kOffV = kNT * kKTile;
@@ -86,8 +87,9 @@ struct Geo {
   static constexpr int kKS = D / 16;                      // contraction steps over d
   static constexpr int kCB = D / 32;                      // 32-column output blocks
 };
-static_assert(Geo<128, true>::kImgBytes == 73728 && Geo<64, true>::kImgBytes == 40960 &&
-                  Geo<128, false>::kImgBytes == 40960 && Geo<64, false>::kImgBytes == 24576,
+static_assert(Geo<128, true>::kImgBytes == 65536 && Geo<64, true>::kImgBytes == 32768 &&
+                  Geo<128, false>::kImgBytes == 32768 && Geo<64, false>::kImgBytes == 16384 &&
+                  Geo<128, true>::kImgUsed == Geo<128, true>::kImgBytes,
               "tile image sizes");
 
 // Key held at position `pos` (0..63) of a packed V^T row.  Positions
@@ -124,19 +126,19 @@ __device__ __attribute__((always_inline)) inline void pack_kv_body(
   const uint32_t img = (uint32_t)tile * G::kImgBytes;
   constexpr int kChunksPerRow = D / 8;  // 16-byte chunks of one input row
   constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
-  // K, dK: rows copied with a zero pad chunk after each; keys >= Nk are zero.
-  constexpr int kKChunks = kBC * (kChunksPerRow + 1);
+  // K, dK: 16-byte chunk col of key row r goes to lane (r % 32) + 32 (col % 2)
+  // of fragment (r / 32) kKS + col / 2; keys >= Nk are zero.
+  constexpr int kKChunks = kBC * kChunksPerRow;
   for (int c = threadIdx.x; c < kT * kKChunks; c += kPackThreads) {
     const int t = c / kKChunks, rem = c % kKChunks;
-    const int r = rem / (kChunksPerRow + 1), col = rem % (kChunksPerRow + 1);
+    const int r = rem / kChunksPerRow, col = rem % kChunksPerRow;
     const int key = key0 + r;
     u32x4 x = kZero;
-    if (col < kChunksPerRow && key < Nk)
-      x = buf_load16(t == 0 ? rk : rdk, ((bh * (uint32_t)Nk + key) * D + 8 * col) * 2);
-    buf_store16(rws, img + t * G::kOffdK + r * G::kKRow + col * 16, x);
+    if (key < Nk) x = buf_load16(t == 0 ? rk : rdk, ((bh * (uint32_t)Nk + key) * D + 8 * col) * 2);
+    const int frag = (r >> 5) * G::kKS + (col >> 1), ln = (r & 31) + 32 * (col & 1);
+    buf_store16(rws, img + t * G::kOffdK + frag * kDmaBytes + ln * 16, x);
   }
-  // V, dV: to fp16 in LDS, then written transposed ([d][64 keys], keys in
-  // packed_key order) with a zero pad chunk after each row.
+  // V, dV: to fp16 in LDS, then written transposed as operand fragments.
   constexpr int kIn = kBC * kChunksPerRow;
   for (int c = threadIdx.x; c < kT * kIn; c += kPackThreads) {
     const int t = c / kIn, rem = c % kIn, r = rem / kChunksPerRow, col = (rem % kChunksPerRow) * 8;
@@ -150,16 +152,16 @@ __device__ __attribute__((always_inline)) inline void pack_kv_body(
     }
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < kT * D * 9; c += kPackThreads) {
-    const int t = c / (D * 9), rem = c % (D * 9), col = rem / 9, p = rem % 9;
-    u32x4 x = kZero;
-    if (p < 8) {
-      f16x8 h;
+  constexpr int kVChunks = G::kVTile / 16;  // = 64 lanes x fragments
+  for (int c = threadIdx.x; c < kT * kVChunks; c += kPackThreads) {
+    const int t = c / kVChunks, rem = c % kVChunks, frag = rem >> 6, ln = rem & 63;
+    const int kb = frag / (2 * G::kCB), tt = (frag / G::kCB) & 1, cb = frag % G::kCB;
+    const int col = 32 * cb + (ln & 31), p = 4 * kb + 2 * tt + (ln >> 5);
+    f16x8 h;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = sv[t][packed_key(8 * p + e)][col];
-      x = __builtin_bit_cast(u32x4, h);
-    }
-    buf_store16(rws, img + G::kOffV + t * G::kVTile + col * G::kVRow + p * 16, x);
+    for (int e = 0; e < 8; ++e) h[e] = sv[t][packed_key(8 * p + e)][col];
+    buf_store16(rws, img + G::kOffV + t * G::kVTile + frag * kDmaBytes + ln * 16,
+                __builtin_bit_cast(u32x4, h));
   }
   // the image's tail beyond its tiles
   for (int o = G::kImgUsed + threadIdx.x * 16; o < G::kImgBytes; o += kPackThreads * 16)
@@ -202,15 +204,16 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
   // fragments are read at their own step (the other wave on the SIMD covers
   // the LDS latency); scheduling barriers keep the compiler from hoisting
   // reads, and their registers, across steps.
-  const int krow = (32 * kb + l32) * G::kKRow + 16 * g;
+  const int lane16 = 16 * l32 + 512 * g;  // this lane's 16 bytes of a fragment
   f32x16 s, ds;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < G::kKS; ++ks) {
     issue(ks);
-    const u32x4 kf = lds_load16(sK + krow + 32 * ks);
+    const int kfrag = (kb * G::kKS + ks) * kDmaBytes;
+    const u32x4 kf = lds_load16(sK + lane16 + kfrag);
     u32x4 dkf;
-    if constexpr (M::kKV) dkf = lds_load16(sdK + krow + 32 * ks);
+    if constexpr (M::kKV) dkf = lds_load16(sdK + lane16 + kfrag);
     s = mma_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s);
     if constexpr (M::kTan) ds = mma_bf16(kf, dqf[ks], ks == 0 ? f32x16{} : ds);
     if constexpr (M::kKV) ds = mma_bf16(dkf, qf[ks], ds);
@@ -282,9 +285,8 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
   // V^T and dV^T fragments read one step ahead (S and dS are dead by now, so
   // the prefetch registers come free)
   constexpr int kSteps = 2 * G::kCB;
-  auto voff = [&](int step) {
-    const int t = step / G::kCB, cb = step % G::kCB;
-    return (32 * cb + l32) * G::kVRow + 16 * g + 16 * (4 * kb + 2 * t);
+  auto voff = [&](int step) {  // fragment (2 kb + t) kCB + cb, step = t kCB + cb
+    return lane16 + (2 * kb * G::kCB + step) * kDmaBytes;
   };
   // (the forward mode, held to 128 registers, reads each fragment at its step)
   constexpr bool kPf = M::kTan;

@@ -108,9 +108,10 @@ ATTN_JVP_API int attn_jvp_fwd(const void *q, const void *k, const void *v,
 /*
  * Bytes of workspace the bf16 path needs for these sizes: one 64-key tile
  * image per (b, h) and key tile, holding K and dK (bf16) and V^T and dV^T
- * (fp16, in matrix-core operand order), each row padded, laid out byte for
- * byte as the fused kernel holds them in LDS (72 KiB per tile at d = 128,
- * 40 KiB at d = 64); 0 if a size is invalid.  Same operation as attn_jvp_fwd.
+ * (fp16) as the sequence of matrix-core operand fragments the fused kernel
+ * reads, laid out byte for byte as it holds them in LDS (64 KiB per tile at
+ * d = 128, 32 KiB at d = 64); 0 if a size is invalid.  Same operation as
+ * attn_jvp_fwd.
  */
 ATTN_JVP_API size_t attn_jvp_workspace_bytes(int B, int H, int Nk, int d);
 

@@ -53,12 +53,12 @@ def test_strerror():
 
 
 def test_workspace_bytes():
-    # one tile image per (b, h) and 64-key tile: K, dK rows of 2d + 16 bytes,
-    # V^T, dV^T rows of 64 * 2 + 16 bytes, rounded up to 8 KiB
+    # one tile image per (b, h) and 64-key tile: K, dK (64 x d bf16) and V^T,
+    # dV^T (d x 64 fp16), unpadded operand fragments, a whole number of 8 KiB
     def img(d):
-        used = 2 * 64 * (2 * d + 16) + 2 * d * (2 * 64 + 16)
+        used = 2 * 64 * d * 2 + 2 * d * 64 * 2
         return -(-used // 8192) * 8192
-    assert img(128) == 72 * 1024 and img(64) == 40 * 1024
+    assert img(128) == 64 * 1024 and img(64) == 32 * 1024
     assert ajvp.attn_jvp_workspace_bytes(1, 1, 1, 128) == img(128)
     assert ajvp.attn_jvp_workspace_bytes(1, 12, 32760, 128) == 12 * 512 * img(128)
     assert ajvp.attn_jvp_workspace_bytes(2, 3, 65, 64) == 6 * 2 * img(64)
