@@ -100,3 +100,28 @@ def test_increasing_max_along_keys():
 def test_cross_frozen_text_reduced():
     x, s = make_inputs("text_cross_frozen", Nq=700, heads=[0, 3])
     _cmp("text_cross_frozen reduced", x, s)
+
+
+@pytest.mark.parametrize("Nk", [1, 130, 200])
+def test_more_row_tiles_than_resident_workgroups(Nk):
+    """40 heads x 17 row tiles (the last one ragged) = 680 workgroups, more than
+    the chip holds at once (one per CU), in the XCD-aware order; 1, 3 and 4 key
+    tiles.  Full JVP with fp32 and bf16 outputs, the frozen-key kernel
+    (dK = dV = 0) and the tangent of lse, all against the oracle."""
+    import attention_forward_mode_amd as ajvp
+    s = 1.0 / math.sqrt(128)
+    x = _rand(1, 40, 4100, Nk, 128, torch.bfloat16, seed=Nk)
+    _cmp(f"items Nk={Nk}", x, s)
+    g = to_device(x)
+    print(f"  launch ex frozen/bf16 q{tuple(g['q'].shape)} k{tuple(g['k'].shape)}", flush=True)
+    fro = ajvp.attn_jvp_fwd_ex(g["q"], g["k"], g["v"], g["dq"], None, None, scale=s)
+    b16 = ajvp.attn_jvp_fwd_ex(g["q"], g["k"], g["v"], g["dq"], g["dk"], g["dv"], scale=s,
+                               out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    zero = torch.zeros_like(x["dk"])
+    ref_f = oracle.attention_jvp(x["q"], x["k"], x["v"], x["dq"], zero, zero, s, with_dlse=True)
+    check(f"items frozen Nk={Nk}", fro[:3], ref_f[:3], fp32=False)
+    # the fourth output is the tangent of lse, mu = rowsum(P * dS) (checked as "O")
+    check(f"items frozen tlse Nk={Nk}", (fro[3],), (ref_f[3],), fp32=False)
+    ref = oracle.attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], s)
+    check(f"items bf16-out Nk={Nk}", b16[:3], ref, fp32=False)
