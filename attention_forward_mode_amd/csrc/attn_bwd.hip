@@ -157,7 +157,7 @@ __device__ __attribute__((always_inline)) inline void pack_body(
     buf_store16(rws, img + G::kOffT + t * G::kTTile + col * G::kTRow + p * 16, x);
   }
   if constexpr (kQuery) {
-    // extras: [block b][lse | D][lane half g][slot r]
+    // extras: [block b][lse log2 e | D][lane half g][slot r]
     const auto rl = make_rsrc(lse, in_bytes / D * 2);
     for (int c = threadIdx.x; c < 2 * kTile; c += kPackThreads) {
       const int which = c / kTile, rem = c % kTile;       // 0: lse, 1: D
@@ -165,7 +165,8 @@ __device__ __attribute__((always_inline)) inline void pack_body(
       const int row = 32 * b + slot_row(r, g);
       float val;
       if (which == 0)
-        val = row0 + row < N ? buf_load4f(rl, (bh * (uint32_t)N + row0 + row) * 4) : INFINITY;
+        val = row0 + row < N ? buf_load4f(rl, (bh * (uint32_t)N + row0 + row) * 4) * kLog2e
+                             : INFINITY;
       else
         val = sd[row];
       buf_store4(rws, img + G::kOffX + (b * 2 + which) * 128 + (g * 16 + r) * 4, val);
@@ -256,7 +257,7 @@ __device__ __attribute__((always_inline)) inline void kv_block(
   const char* sGO = stage + G::kRTile;
   const char* sQT = stage + G::kOffT;
   const char* sGOT = sQT + G::kTTile;
-  const char* sX = stage + G::kOffX + qb * 256 + g * 64;  // lse at +0, D at +128
+  const char* sX = stage + G::kOffX + qb * 256 + g * 64;  // lse log2 e at +0, D at +128
   const int rowoff = (32 * qb + l32) * G::kRRow + 16 * g;
   // S = Q K^T, gP = gO V^T (rows: query, columns: this wave's keys)
   f32x16 s, gp;
@@ -279,7 +280,7 @@ __device__ __attribute__((always_inline)) inline void kv_block(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * q4 + e;
-      pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l4[e] * kLog2e));
+      pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l4[e]));
       gs[e] = pp[e] * (gp[r] - d4[e]);
     }
 #pragma unroll
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     // slot of row r32 within its block: r32 = 8(r/4) + 4 gg + r%4
     const int gg = (r32 >> 2) & 1, r = ((r32 >> 3) << 2) | (r32 & 3);
     const uint32_t x = (uint32_t)(row / kTile) * GQ::kBytes + GQ::kOffX + blk * 256 + (gg * 16 + r) * 4;
-    lse2 = buf_load4f(rq, x) * kLog2e;
+    lse2 = buf_load4f(rq, x);
     dq = buf_load4f(rq, x + 128);
   }
   f32x16 acc[G::kCB];
