@@ -34,13 +34,14 @@
 //  kTau (log2 units): results are exact either way, p stays <= 2^kTau, and the
 //  accumulator rescale is skipped on most blocks.
 //
-// Three modes share that body:
+// Two modes share that body:
 //  kFull    the JVP along (dQ, dK, dV); a NULL tangent reads as zeros;
 //  kFrozen  the JVP with dK = dV = 0 (e.g. frozen text keys of cross-attention):
 //           the products with dK and dV and their tiles are left out (4 of the
-//           6 contractions remain);
-//  kFwd     the forward pass alone (O, lse: 2 contractions).
-// Outputs O and dO are written in fp32 or bf16 (round to nearest even).
+//           6 contractions remain).
+// The forward pass alone (O, lse: 2 contractions) has a kernel of its own
+// (attn_fwd_bf16_kernel, 64 rows per wave).  Outputs O and dO are written in
+// fp32 or bf16 (round to nearest even).
 #include "cdna4.hpp"
 #include "launch.hpp"
 
@@ -57,10 +58,9 @@ constexpr float kTau = 4.0f;        // lazy-rescale headroom, log2 units
 constexpr int kDmaBytes = 1024;     // one LDS-direct load: 64 lanes x 16 bytes
 constexpr uint32_t kXcds = 8;       // accelerator dies (each with its own L2) on MI355X
 
-enum : int { kFull = 0, kFrozen = 1, kFwd = 2 };
+enum : int { kFull = 0, kFrozen = 1 };
 template <int kMode>
 struct Mode {
-  static constexpr bool kTan = kMode != kFwd;  // the tangent is computed
   static constexpr bool kKV = kMode == kFull;  // dK and dV take part
 };
 
@@ -215,7 +215,7 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
     u32x4 dkf;
     if constexpr (M::kKV) dkf = lds_load16(sdK + lane16 + kfrag);
     s = mma_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s);
-    if constexpr (M::kTan) ds = mma_bf16(kf, dqf[ks], ks == 0 ? f32x16{} : ds);
+    ds = mma_bf16(kf, dqf[ks], ks == 0 ? f32x16{} : ds);
     if constexpr (M::kKV) ds = mma_bf16(dkf, qf[ks], ds);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -252,30 +252,25 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
       // keys past Nk: p = 0 (their K and dK rows are zero, so dS is 0 there
       // unless the row's own Q or dQ is not finite)
       if (kMask && key0 + slot_key(r, g) >= Nk) pp[e] = 0.f;
-      if constexpr (M::kTan) pdd[e] = pp[e] * ds[r] * scale;
+      pdd[e] = pp[e] * ds[r] * scale;
     }
     const uint32_t hp = pack_f16x2(pp[0], pp[1]);
     p[q >> 2][q & 3] = hp;
     lsum = add_f16x2(hp, lsum);
-    if constexpr (M::kTan) {
-      const uint32_t hd = pack_f16x2(pdd[0], pdd[1]);
-      pd[q >> 2][q & 3] = hd;
-      usum = add_f16x2(hd, usum);
-    }
+    const uint32_t hd = pack_f16x2(pdd[0], pdd[1]);
+    pd[q >> 2][q & 3] = hd;
+    usum = add_f16x2(hd, usum);
   }
   st.l = st.l * alpha + lsum;
-  if constexpr (M::kTan) st.u = st.u * alpha + usum;
+  st.u = st.u * alpha + usum;
   // Pin the sums here (empty asm: a register constraint only); left alone, the
   // compiler sinks them into the next block and keeps P alive until then.
-  if constexpr (M::kTan)
-    asm volatile("" : "+v"(st.l), "+v"(st.u));
-  else
-    asm volatile("" : "+v"(st.l));
+  asm volatile("" : "+v"(st.l), "+v"(st.u));
   if (wave_any(alpha != 1.0f)) {
 #pragma unroll
     for (int cb = 0; cb < G::kCB; ++cb) {
       st.accA[cb] *= alpha;
-      if constexpr (M::kTan) st.accG[cb] *= alpha;
+      st.accG[cb] *= alpha;
     }
   }
 
@@ -288,22 +283,19 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
   auto voff = [&](int step) {  // fragment (2 kb + t) kCB + cb, step = t kCB + cb
     return lane16 + (2 * kb * G::kCB + step) * kDmaBytes;
   };
-  // (the forward mode, held to 128 registers, reads each fragment at its step)
-  constexpr bool kPf = M::kTan;
   u32x4 vf[2], dvf[2];
-  if constexpr (kPf) vf[0] = lds_load16(sV + voff(0));
+  vf[0] = lds_load16(sV + voff(0));
   if constexpr (M::kKV) dvf[0] = lds_load16(sdV + voff(0));
 #pragma unroll
   for (int step = 0; step < kSteps; ++step) {
     const int t = step / G::kCB, cb = step % G::kCB;
     issue(G::kKS + step);
-    if constexpr (!kPf) vf[step & 1] = lds_load16(sV + voff(step));
-    if (kPf && step + 1 < kSteps) {
+    if (step + 1 < kSteps) {
       vf[(step + 1) & 1] = lds_load16(sV + voff(step + 1));
       if constexpr (M::kKV) dvf[(step + 1) & 1] = lds_load16(sdV + voff(step + 1));
     }
     st.accA[cb] = mma_f16(vf[step & 1], p[t], st.accA[cb]);
-    if constexpr (M::kTan) st.accG[cb] = mma_f16(vf[step & 1], pd[t], st.accG[cb]);
+    st.accG[cb] = mma_f16(vf[step & 1], pd[t], st.accG[cb]);
     if constexpr (M::kKV) st.accG[cb] = mma_f16(dvf[step & 1], p[t], st.accG[cb]);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -351,11 +343,9 @@ __device__ __attribute__((always_inline)) inline void store4(__amdgpu_buffer_rsr
 }
 
 // o, to: [B, H, Nq, D] in fp32 (kOutBf16 false) or bf16; lse, tlse: [B, H, Nq]
-// fp32, each may be NULL.  kFwd reads no tq and writes no to, tlse.
-// Waves per SIMD: 2 for the JVP modes (256 registers each); 4 for the forward
-// mode, whose 128 registers and 80 KiB of LDS let two workgroups share a CU.
+// fp32, each may be NULL.  Two waves per SIMD (256 registers each).
 template <int D, int kMode, bool kOutBf16>
-__global__ __launch_bounds__(kThreads, kMode == kFwd ? 4 : 2) void attn_jvp_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ tq,
     const char* __restrict__ img, void* __restrict__ o, void* __restrict__ to,
     float* __restrict__ lse, float* __restrict__ tlse, int Nq, int Nk, int ntiles, int nqt,
@@ -409,7 +399,7 @@ __global__ __launch_bounds__(kThreads, kMode == kFwd ? 4 : 2) void attn_jvp_bf16
   for (int ks = 0; ks < G::kKS; ++ks) {
     const uint32_t off = qrow + (16 * ks + 8 * g) * 2;
     qf[ks] = buf_load16(rq, off);
-    if constexpr (M::kTan) dqf[ks] = buf_load16(rtq, off);
+    dqf[ks] = buf_load16(rtq, off);
   }
 
   RowState<D> st;
@@ -450,11 +440,11 @@ __global__ __launch_bounds__(kThreads, kMode == kFwd ? 4 : 2) void attn_jvp_bf16
   // ---- epilogue: O = A / l, mu = u / l, dO = G / l - mu O, lse, tlse = mu ----
   const float l = halves_sum(st.l);
   const float inv_l = 1.0f / l;
-  const float mu = M::kTan ? halves_sum(st.u) * inv_l : 0.f;
+  const float mu = halves_sum(st.u) * inv_l;
   if (row_ok) {
     const uint32_t orow = (bh * (uint32_t)Nq + row) * D;  // first element of the row
     const auto ro = make_rsrc(o, ext.o_bytes);
-    const auto rto = make_rsrc(to, M::kTan ? ext.o_bytes : 0u);
+    const auto rto = make_rsrc(to, ext.o_bytes);
 #pragma unroll
     for (int cb = 0; cb < G::kCB; ++cb)
 #pragma unroll
@@ -465,15 +455,218 @@ __global__ __launch_bounds__(kThreads, kMode == kFwd ? 4 : 2) void attn_jvp_bf16
         for (int e = 0; e < 4; ++e) {
           const float a = st.accA[cb][4 * qq + e] * inv_l;
           ov[e] = a;
-          if constexpr (M::kTan) tv[e] = st.accG[cb][4 * qq + e] * inv_l - mu * a;
+          tv[e] = st.accG[cb][4 * qq + e] * inv_l - mu * a;
         }
         store4<kOutBf16>(ro, orow + c0, ov);
-        if constexpr (M::kTan) store4<kOutBf16>(rto, orow + c0, tv);
+        store4<kOutBf16>(rto, orow + c0, tv);
       }
     if (g == 0) {
       const uint32_t off = (bh * (uint32_t)Nq + row) * 4;
       if (lse != nullptr) buf_store4(make_rsrc(lse, ext.lse_bytes), off, (st.m + __log2f(l)) * kLn2);
-      if (M::kTan && tlse != nullptr) buf_store4(make_rsrc(tlse, ext.lse_bytes), off, mu);
+      if (tlse != nullptr) buf_store4(make_rsrc(tlse, ext.lse_bytes), off, mu);
+    }
+  }
+}
+
+// ---- forward attention alone (O, lse) ----
+// Each wave holds 64 query rows (two 32-row blocks), so every K and V^T
+// fragment it reads from LDS feeds two matrix products, and a workgroup of 8
+// waves covers 512 rows per pass over the key tiles: half the LDS reads and
+// half the tile-image stream per row of a 32-row wave.  Registers: 128
+// accumulators, 64 for the Q fragments, 32 for the two S blocks.
+constexpr int kFwdRB = 2;                         // 32-row blocks per wave
+constexpr int kFwdBR = kWaves * 32 * kFwdRB;      // query rows per workgroup
+
+template <int D>
+struct FwdState {
+  f32x16 acc[kFwdRB][D / 32];  // A^T = sum p v per row block (rows: output column)
+  float m[kFwdRB];             // running max, log2 units
+  float l[kFwdRB];             // this lane's half of sum p (of the fp16-rounded p)
+};
+
+// One 32-key block for the wave's two row blocks; same arithmetic as the
+// tangent-free part of jvp_block (online softmax with the lazy rescale, P
+// rounded to fp16 for the second product, l summed from those values).
+template <int D, bool kMask, typename Issue>
+__device__ __attribute__((always_inline)) inline void fwd_block(
+    FwdState<D>& st, const char* stage, int kb, const u32x4 (*qf)[D / 16], int l32, int g,
+    int key0, int Nk, float c_log2, Issue issue) {
+  using G = Geo<D, false>;
+  const char* sK = stage;
+  const char* sV = stage + G::kOffV;
+  const int lane16 = 16 * l32 + 512 * g;
+  f32x16 s[kFwdRB];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < G::kKS; ++ks) {
+    issue(ks);
+    const u32x4 kf = lds_load16(sK + lane16 + (kb * G::kKS + ks) * kDmaBytes);
+#pragma unroll
+    for (int rb = 0; rb < kFwdRB; ++rb)
+      s[rb] = mma_bf16(kf, qf[rb][ks], ks == 0 ? f32x16{} : s[rb]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  u32x4 p[kFwdRB][2];
+  float alpha[kFwdRB];
+#pragma unroll
+  for (int rb = 0; rb < kFwdRB; ++rb) {
+    if constexpr (kMask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (key0 + slot_key(r, g) >= Nk) s[rb][r] = -INFINITY;
+    }
+    float mx = s[rb][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, s[rb][r]);
+    mx = halves_max(mx);
+    const float mt = mx * c_log2;
+    const float m_new = (mt > st.m[rb] + kTau) ? mt : st.m[rb];
+    alpha[rb] = __builtin_amdgcn_exp2f(st.m[rb] - m_new);
+    st.m[rb] = m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      float pp[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * q + e;
+        pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][r], c_log2, -m_new));
+        if (kMask && key0 + slot_key(r, g) >= Nk) pp[e] = 0.f;
+      }
+      const uint32_t hp = pack_f16x2(pp[0], pp[1]);
+      p[rb][q >> 2][q & 3] = hp;
+      lsum = add_f16x2(hp, lsum);
+    }
+    st.l[rb] = st.l[rb] * alpha[rb] + lsum;
+  }
+  // pin the sums here (an empty asm with register constraints only)
+  asm volatile("" : "+v"(st.l[0]), "+v"(st.l[1]));
+  if (wave_any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+#pragma unroll
+    for (int rb = 0; rb < kFwdRB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < G::kCB; ++cb) st.acc[rb][cb] *= alpha[rb];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // A^T += V^T P^T for both row blocks; step = (t, cb) reads fragment
+  // (2 kb + t) kCB + cb, one step ahead
+  constexpr int kSteps = 2 * G::kCB;
+  auto voff = [&](int step) { return lane16 + (2 * kb * G::kCB + step) * kDmaBytes; };
+  u32x4 vfp[2];
+  vfp[0] = lds_load16(sV + voff(0));
+#pragma unroll
+  for (int step = 0; step < kSteps; ++step) {
+    const int t = step / G::kCB, cb = step % G::kCB;
+    issue(G::kKS + step);
+    if (step + 1 < kSteps) vfp[(step + 1) & 1] = lds_load16(sV + voff(step + 1));
+    const u32x4 vf = vfp[step & 1];
+#pragma unroll
+    for (int rb = 0; rb < kFwdRB; ++rb) st.acc[rb][cb] = mma_f16(vf, p[rb][t], st.acc[rb][cb]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int D, typename Copy>
+__device__ __attribute__((always_inline)) inline void fwd_tile(
+    char* __restrict__ next, const char* __restrict__ cur, Copy copy, FwdState<D>& st,
+    const u32x4 (*qf)[D / 16], int l32, int g, int Nk, float c_log2) {
+  using G = Geo<D, false>;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+    fwd_block<D, false>(st, cur, kb, qf, l32, g, 0, Nk, c_log2, [&](int slot) {
+      if (kb == 0 && slot < G::kDmaPerWave) copy(next, slot);
+    });
+}
+
+// o: [B, H, Nq, D] fp32 or bf16; lse: [B, H, Nq] fp32 or NULL.  Tile images
+// hold K and V^T only (the layout of the frozen-key mode).
+template <int D, bool kOutBf16>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
+    const uint16_t* __restrict__ q, const char* __restrict__ img, void* __restrict__ o,
+    float* __restrict__ lse, int Nq, int Nk, int ntiles, int nqt, Extents ext, float c_log2) {
+  using G = Geo<D, false>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * G::kImgBytes];
+  // XCD-aware work order, as in attn_jvp_bf16_kernel
+  const uint32_t wg = blockIdx.x, nwg = gridDim.x;
+  const uint32_t xcd = wg % kXcds, slot = wg / kXcds, per = nwg / kXcds, extra = nwg % kXcds;
+  const uint32_t work = xcd < extra ? xcd * (per + 1) + slot
+                                    : extra * (per + 1) + (xcd - extra) * per + slot;
+  const int qt = (int)(work % (uint32_t)nqt);
+  const uint32_t bh = work / (uint32_t)nqt;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int row0 = qt * kFwdBR + wave * 32 * kFwdRB + l32;  // row of block rb: row0 + 32 rb
+
+  const auto rq = make_rsrc(q, ext.q_bytes);
+  const uint32_t slice_bytes = (uint32_t)ntiles * G::kImgBytes;
+  const auto rimg = make_rsrc(img + (size_t)bh * slice_bytes, slice_bytes);
+  const uint32_t wave_part = (uint32_t)wave * G::kDmaPerWave * kDmaBytes;
+  auto copy_one = [&](int kt, char* stage, int j) {
+    const uint32_t src = (uint32_t)kt * G::kImgBytes + wave_part + j * kDmaBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rimg, (lds_ptr_t)(stage + wave_part + j * kDmaBytes),
+                                             16, lane * 16, src, 0, 0);
+  };
+#pragma unroll
+  for (int j = 0; j < G::kDmaPerWave; ++j) copy_one(0, smem, j);
+
+  // Q fragments of both row blocks (rows past Nq read as 0 through the descriptor)
+  u32x4 qf[kFwdRB][G::kKS];
+#pragma unroll
+  for (int rb = 0; rb < kFwdRB; ++rb) {
+    const int row = row0 + 32 * rb;
+    const uint32_t qrow = row < Nq ? (bh * (uint32_t)Nq + row) * D * 2 : 0x80000000u;
+#pragma unroll
+    for (int ks = 0; ks < G::kKS; ++ks) qf[rb][ks] = buf_load16(rq, qrow + (16 * ks + 8 * g) * 2);
+  }
+
+  FwdState<D> st;
+#pragma unroll
+  for (int rb = 0; rb < kFwdRB; ++rb) {
+#pragma unroll
+    for (int cb = 0; cb < G::kCB; ++cb) st.acc[rb][cb] = f32x16{};
+    st.m[rb] = -INFINITY;
+    st.l[rb] = 0.f;
+  }
+
+  const int kLast = ntiles - 1;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < kLast; ++kt) {
+    fwd_tile<D>(smem + ((kt + 1) & 1) * G::kImgBytes, smem + (kt & 1) * G::kImgBytes,
+                [&](char* next, int j) { copy_one(kt + 1, next, j); }, st, qf, l32, g, Nk,
+                c_log2);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  {
+    const char* cur = smem + (kLast & 1) * G::kImgBytes;
+    const int kl = kLast * kBC;
+    auto none = [](int) {};
+    fwd_block<D, true>(st, cur, 0, qf, l32, g, kl, Nk, c_log2, none);
+    fwd_block<D, true>(st, cur, 1, qf, l32, g, kl + 32, Nk, c_log2, none);
+  }
+
+  const auto ro = make_rsrc(o, ext.o_bytes);
+#pragma unroll
+  for (int rb = 0; rb < kFwdRB; ++rb) {
+    const int row = row0 + 32 * rb;
+    const float l = halves_sum(st.l[rb]);
+    const float inv_l = 1.0f / l;
+    if (row < Nq) {
+      const uint32_t orow = (bh * (uint32_t)Nq + row) * D;
+#pragma unroll
+      for (int cb = 0; cb < G::kCB; ++cb)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          f32x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = st.acc[rb][cb][4 * qq + e] * inv_l;
+          store4<kOutBf16>(ro, orow + 32 * cb + 8 * qq + 4 * g, ov);
+        }
+      if (g == 0 && lse != nullptr)
+        buf_store4(make_rsrc(lse, ext.lse_bytes), (bh * (uint32_t)Nq + row) * 4,
+                   (st.m[rb] + __log2f(l)) * kLn2);
     }
   }
 }
@@ -585,13 +778,32 @@ hipError_t launch_bf16_ex(const void* q, const void* k, const void* v, const voi
                                    stream);
 }
 
+template <int D, bool kOutBf16>
+hipError_t launch_fwd_d(const void* q, const void* ws, void* o, float* lse, int B, int H, int Nq,
+                        int Nk, float scale, hipStream_t stream) {
+  const int ntiles = (Nk + kBC - 1) / kBC;
+  const int nqt = (Nq + kFwdBR - 1) / kFwdBR;
+  const int bh = B * H;
+  Extents ext;
+  ext.q_bytes = (uint32_t)((size_t)bh * Nq * D * 2);
+  ext.o_bytes = (uint32_t)((size_t)bh * Nq * D * (kOutBf16 ? 2 : 4));
+  ext.lse_bytes = (uint32_t)((size_t)bh * Nq * 4);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, kOutBf16>), dim3(nqt * bh), dim3(kThreads), 0,
+                     stream, static_cast<const uint16_t*>(q), static_cast<const char*>(ws), o, lse,
+                     Nq, Nk, ntiles, nqt, ext, scale * kLog2e);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int Nq, int Nk, int d, float scale, bool out_bf16, void* ws,
                       hipStream_t stream) {
   hipError_t e = launch_pack(false, k, v, nullptr, nullptr, B, H, Nk, d, ws, stream);
   if (e != hipSuccess) return e;
-  return launch_main<kFwd>(q, nullptr, ws, o, nullptr, lse, nullptr, B, H, Nq, Nk, d, scale,
-                           out_bf16, stream);
+  if (d == 128)
+    return out_bf16 ? launch_fwd_d<128, true>(q, ws, o, lse, B, H, Nq, Nk, scale, stream)
+                    : launch_fwd_d<128, false>(q, ws, o, lse, B, H, Nq, Nk, scale, stream);
+  return out_bf16 ? launch_fwd_d<64, true>(q, ws, o, lse, B, H, Nq, Nk, scale, stream)
+                  : launch_fwd_d<64, false>(q, ws, o, lse, B, H, Nq, Nk, scale, stream);
 }
 
 }  // namespace ajvp
