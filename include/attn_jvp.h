@@ -183,9 +183,10 @@ ATTN_JVP_API int attn_jvp_fwd_ex(const void *q, const void *k, const void *v,
 /*
  * Forward attention alone (FlashAttention-2's output, without a tangent):
  * O = softmax(scale Q K^T) V and lse, bf16 inputs as in attn_jvp_fwd, O in fp32
- * or bf16 (out_dtype), lse fp32 or NULL.  The same kernel as attn_jvp_fwd with
- * the tangent left out (2 of the 6 contractions); its O and lse equal
- * attn_jvp_fwd's bit for bit.  Workspace and errors as attn_jvp_fwd_ex.
+ * or bf16 (out_dtype), lse fp32 or NULL.  The pass of attn_jvp_fwd with the
+ * tangent left out (2 of the 6 contractions, 64 query rows per wave); its O and
+ * lse equal attn_jvp_fwd's bit for bit.  Workspace and errors as
+ * attn_jvp_fwd_ex.
  */
 ATTN_JVP_API int attn_fwd(const void *q, const void *k, const void *v,
              void *o, float *lse,
