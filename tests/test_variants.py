@@ -131,6 +131,26 @@ def test_forward_only(name, Nq, Nk, d):
     check(f"fwd {name} {Nq}x{Nk} d={d}", (o, None, lse), (O, None, L), fp32=False)
 
 
+@pytest.mark.parametrize("name", ["video_1p3b", "video_14b", "text_cross", "image_dit"])
+def test_forward_only_full_size(name):
+    """attn_fwd at the full workload sizes (the launch configuration the
+    forward benchmark times: 512-row workgroups, two row blocks per wave)
+    returns the JVP kernel's O and lse bit for bit; the JVP kernel itself is
+    held to the oracle at these sizes by the parity tests."""
+    x, s = make_inputs(name)
+    g = to_device(x)
+    print(f"  launch attn_fwd / attn_jvp_fwd {name} q{tuple(g['q'].shape)}", flush=True)
+    o, lse = ajvp.attn_fwd(g["q"], g["k"], g["v"], scale=s)
+    ref = ajvp.attn_jvp_fwd(*[g[n] for n in NAMES], scale=s)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref[0]) and torch.equal(lse, ref[2])
+    # and a few rows against the oracle directly
+    rows = [0, 1, x["q"].shape[2] // 2, x["q"].shape[2] - 1]
+    O, L = oracle.attention(x["q"][:, :, rows], x["k"], x["v"], s)
+    check(f"fwd {name} full, rows {rows}", (o[:, :, rows], None, lse[:, :, rows]), (O, None, L),
+          fp32=False)
+
+
 @pytest.mark.parametrize("parts", [2, 5])
 def test_merge_of_key_splits(parts):
     """Results over disjoint key ranges, merged on the GPU, pass the gate
