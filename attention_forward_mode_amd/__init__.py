@@ -68,6 +68,10 @@ def lib():
     L.attn_jvp_fwd_packed.restype = _i
     L.attn_jvp_fwd_ex.argtypes = [_vp] * 10 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
     L.attn_jvp_fwd_ex.restype = _i
+    L.attn_jvp_fwd_splitkv.argtypes = [_vp] * 10 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
+    L.attn_jvp_fwd_splitkv.restype = _i
+    L.attn_jvp_splitkv_workspace_bytes.argtypes = [_i] * 6
+    L.attn_jvp_splitkv_workspace_bytes.restype = _sz
     L.attn_fwd.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
     L.attn_fwd.restype = _i
     L.attn_jvp_merge.argtypes = [_vp] * 4 + [_i] * 3 + [_vp] * 5
@@ -275,6 +279,35 @@ def attn_jvp_fwd_ex(q, k, v, tq=None, tk=None, tv=None, scale=None, lse=True, tl
         rc = lib().attn_jvp_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
                                    _ptr(o), _ptr(to), _ptr(lse_t), _ptr(tlse_t), B, H, Nq, Nk, d,
                                    s, code, wp, wb, stream)
+    if rc != OK:
+        raise AttnJvpError(rc)
+    return o, to, lse_t, tlse_t
+
+
+def attn_jvp_splitkv_workspace_bytes(B, H, Nq, Nk, d, nsplit=0):
+    return int(lib().attn_jvp_splitkv_workspace_bytes(B, H, Nq, Nk, d, nsplit))
+
+
+def attn_jvp_fwd_splitkv(q, k, v, tq=None, tk=None, tv=None, scale=None, nsplit=0, lse=True,
+                         tlse=True, workspace=None):
+    """attn_jvp_fwd_ex with the key tiles cut into nsplit ranges (0: chosen
+    from the sizes) on separate workgroups and the partial states merged: for
+    few query rows against many keys.  fp32 outputs; returns (o, to, lse, tlse)."""
+    B, H, Nq, Nk, d = _check(q, k, v, q, k, v, torch.bfloat16)
+    _check_opt(tq, q, "tq")
+    _check_opt(tk, k, "tk")
+    _check_opt(tv, v, "tv")
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    to = torch.empty_like(o)
+    lse_t = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse else None
+    tlse_t = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if tlse else None
+    wp, wb = _ws_arg(workspace, q.device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_jvp_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                                        _ptr(o), _ptr(to), _ptr(lse_t), _ptr(tlse_t), B, H, Nq,
+                                        Nk, d, s, int(nsplit), wp, wb, stream)
     if rc != OK:
         raise AttnJvpError(rc)
     return o, to, lse_t, tlse_t

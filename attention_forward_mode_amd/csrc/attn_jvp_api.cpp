@@ -94,25 +94,32 @@ hipError_t device_pool(hipMemPool_t* out) {
   return hipSuccess;
 }
 
-// Runs `launch(ws)` with the caller's workspace (checked) or, when it is NULL,
-// with one taken from the device pool and returned stream-ordered.
+// Runs `launch(ws)` with the caller's workspace (at least `need` bytes,
+// 256-byte aligned) or, when it is NULL, with `need` bytes taken from the
+// device pool and returned stream-ordered.
 template <typename Launch>
-int with_workspace(void* workspace, size_t workspace_bytes, int B, int H, int Nk, int d,
-                   hipStream_t st, Launch launch) {
+int with_workspace_n(void* workspace, size_t workspace_bytes, size_t need, hipStream_t st,
+                     Launch launch) {
   if (workspace != nullptr) {
-    const int rc = check_workspace(workspace, workspace_bytes, B, H, Nk, d);
-    if (rc != ATTN_JVP_OK) return rc;
+    if (workspace_bytes < need) return ATTN_JVP_EINVAL;
+    if (misaligned(workspace, 256)) return ATTN_JVP_EALIGN;
     return launch(workspace) == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
   }
   hipMemPool_t pool = nullptr;
   if (device_pool(&pool) != hipSuccess) return ATTN_JVP_ELAUNCH;
   void* ws = nullptr;
-  if (hipMallocFromPoolAsync(&ws, ajvp::bf16_workspace_bytes(B, H, Nk, d), pool, st) !=
-      hipSuccess)
-    return ATTN_JVP_ELAUNCH;
+  if (hipMallocFromPoolAsync(&ws, need, pool, st) != hipSuccess) return ATTN_JVP_ELAUNCH;
   const hipError_t e = launch(ws);
   const hipError_t f = hipFreeAsync(ws, st);
   return (e == hipSuccess && f == hipSuccess) ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+}
+
+// The same with the tile-image workspace of the bf16 path.
+template <typename Launch>
+int with_workspace(void* workspace, size_t workspace_bytes, int B, int H, int Nk, int d,
+                   hipStream_t st, Launch launch) {
+  return with_workspace_n(workspace, workspace_bytes, ajvp::bf16_workspace_bytes(B, H, Nk, d), st,
+                          launch);
 }
 
 bool bad_out_dtype(int t) { return t != ATTN_JVP_OUT_F32 && t != ATTN_JVP_OUT_BF16; }
@@ -213,6 +220,32 @@ int attn_jvp_fwd_ex(const void* q, const void* k, const void* v, const void* tq,
   return with_workspace(workspace, workspace_bytes, B, H, Nk, d, st, [&](void* ws) {
     return ajvp::launch_bf16_ex(q, k, v, tq, tk, tv, o, to, lse, tlse, B, H, Nq, Nk, d, scale,
                                 out_dtype == ATTN_JVP_OUT_BF16, ws, st);
+  });
+}
+
+size_t attn_jvp_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int nsplit) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128) || nsplit < 0) return 0;
+  return ajvp::splitkv_workspace_bytes(B, H, Nq, Nk, d, nsplit);
+}
+
+int attn_jvp_fwd_splitkv(const void* q, const void* k, const void* v, const void* tq,
+                         const void* tk, const void* tv, float* o, float* to, float* lse,
+                         float* tlse, int B, int H, int Nq, int Nk, int d, float scale,
+                         int nsplit, void* workspace, size_t workspace_bytes,
+                         attn_jvp_stream_t stream) {
+  const void* in[3] = {q, k, v};
+  int rc = validate(in, 3, o, to, lse, B, H, Nq, Nk, d, scale, 2);
+  if (rc != ATTN_JVP_OK) return rc;
+  if (nsplit < 0) return ATTN_JVP_EINVAL;
+  const void* tan[3] = {tq, tk, tv};
+  for (const void* t : tan)
+    if (t != nullptr && misaligned(t, 16)) return ATTN_JVP_EALIGN;
+  if (tlse != nullptr && misaligned(tlse, 4)) return ATTN_JVP_EALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const size_t need = ajvp::splitkv_workspace_bytes(B, H, Nq, Nk, d, nsplit);
+  return with_workspace_n(workspace, workspace_bytes, need, st, [&](void* ws) {
+    return ajvp::launch_bf16_splitkv(q, k, v, tq, tk, tv, o, to, lse, tlse, B, H, Nq, Nk, d,
+                                     scale, nsplit, ws, st);
   });
 }
 

@@ -42,6 +42,8 @@
 // The forward pass alone (O, lse: 2 contractions) has a kernel of its own
 // (attn_fwd_bf16_kernel, 64 rows per wave).  Outputs O and dO are written in
 // fp32 or bf16 (round to nearest even).
+#include <cmath>
+
 #include "cdna4.hpp"
 #include "launch.hpp"
 
@@ -344,28 +346,36 @@ __device__ __attribute__((always_inline)) inline void store4(__amdgpu_buffer_rsr
 
 // o, to: [B, H, Nq, D] in fp32 (kOutBf16 false) or bf16; lse, tlse: [B, H, Nq]
 // fp32, each may be NULL.  Two waves per SIMD (256 registers each).
+// Split-KV: with nsplit > 1 the key tiles are cut into ranges of tps tiles;
+// split s computes the state over its range alone and writes it as (b, h)
+// slice s * nbh + bh of o, to, lse and tlse (partial results that the merge
+// kernel combines).  nsplit = 1, tps = ntiles is the plain pass.
 template <int D, int kMode, bool kOutBf16>
 __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ tq,
     const char* __restrict__ img, void* __restrict__ o, void* __restrict__ to,
     float* __restrict__ lse, float* __restrict__ tlse, int Nq, int Nk, int ntiles, int nqt,
-    Extents ext, float scale, float c_log2) {
+    int nbh, int tps, Extents ext, float scale, float c_log2) {
   using M = Mode<kMode>;
   using G = Geo<D, M::kKV>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * G::kImgBytes];
 
-  // Work item (query tile qt of kBR rows, (b, h) slice bh) from the linear
-  // workgroup id: the dispatcher deals workgroups to the 8 XCDs in turn
-  // (id % 8), so XCD x is given the x-th contiguous range of the work list
-  // ordered by (bh, qt).  The row tiles of one head then run on one XCD and
-  // share its L2, which holds the head's tile images once instead of once per
-  // XCD.  Any XCD count still gives a bijection (only locality changes).
+  // Work item (query tile qt of kBR rows, (b, h) slice bh, key split) from
+  // the linear workgroup id: the dispatcher deals workgroups to the 8 XCDs in
+  // turn (id % 8), so XCD x is given the x-th contiguous range of the work
+  // list ordered by (split, bh, qt).  The row tiles of one head then run on
+  // one XCD and share its L2, which holds the head's tile images once instead
+  // of once per XCD.  Any XCD count still gives a bijection (only locality
+  // changes).
   const uint32_t wg = blockIdx.x, nwg = gridDim.x;
   const uint32_t xcd = wg % kXcds, slot = wg / kXcds, per = nwg / kXcds, extra = nwg % kXcds;
   const uint32_t work = xcd < extra ? xcd * (per + 1) + slot
                                     : extra * (per + 1) + (xcd - extra) * per + slot;
   const int qt = (int)(work % (uint32_t)nqt);
-  const uint32_t bh = work / (uint32_t)nqt;
+  const uint32_t obh = work / (uint32_t)nqt;  // output slice: split * nbh + bh
+  const uint32_t bh = obh % (uint32_t)nbh;
+  const int t0 = (int)(obh / (uint32_t)nbh) * tps;
+  const int t1 = t0 + tps < ntiles ? t0 + tps : ntiles;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
@@ -389,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
                                              16, lane * 16, src, 0, 0);
   };
 #pragma unroll
-  for (int j = 0; j < G::kDmaPerWave; ++j) copy_one(0, smem, j);
+  for (int j = 0; j < G::kDmaPerWave; ++j) copy_one(t0, smem, j);
 
   // Q and dQ fragments: the B operand of S^T = K Q^T (lane: row l32, d-slice g).
   // Rows past Nq get an offset past the tensor, which the descriptor reads as 0.
@@ -412,25 +422,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
   st.l = 0.f;
   st.u = 0.f;
 
-  // Tile kt is computed from stage kt % 2 while tile kt + 1 is copied into
-  // the other stage; the wait for the copies and the barrier at the end of
-  // each tile make tile kt + 1 visible to every wave and retire every read of
-  // stage kt % 2 before the next copy into it starts.
-  const int kLast = ntiles - 1;
+  // Tile kt is computed from stage (kt - t0) % 2 while tile kt + 1 is copied
+  // into the other stage; the wait for the copies and the barrier at the end
+  // of each tile make tile kt + 1 visible to every wave and retire every read
+  // of the stage the next copy overwrites.
+  const int kLast = t1 - 1;
   auto finish_tile = [&]() {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   finish_tile();
-  for (int kt = 0; kt < kLast; ++kt) {
-    tile_step<D, kMode>(smem + ((kt + 1) & 1) * G::kImgBytes, smem + (kt & 1) * G::kImgBytes,
+  for (int kt = t0; kt < kLast; ++kt) {
+    const int sc = (kt - t0) & 1;
+    tile_step<D, kMode>(smem + (sc ^ 1) * G::kImgBytes, smem + sc * G::kImgBytes,
                         [&](char* next, int j) { copy_one(kt + 1, next, j); }, st, qf, dqf, l32,
                         g, Nk, c_log2, scale);
     finish_tile();
   }
-  // last tile: keys past Nk are masked (the tile image holds zeros there)
+  // last tile of the range: keys past Nk are masked (the tile image holds
+  // zeros there; in a range that ends before the last tile nothing is masked)
   {
-    const char* cur = smem + (kLast & 1) * G::kImgBytes;
+    const char* cur = smem + ((kLast - t0) & 1) * G::kImgBytes;
     const int kl = kLast * kBC;
     auto none = [](int) {};
     jvp_block<D, kMode, true>(st, cur, 0, qf, dqf, l32, g, kl, Nk, c_log2, scale, none);
@@ -442,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
   const float inv_l = 1.0f / l;
   const float mu = halves_sum(st.u) * inv_l;
   if (row_ok) {
-    const uint32_t orow = (bh * (uint32_t)Nq + row) * D;  // first element of the row
+    const uint32_t orow = (obh * (uint32_t)Nq + row) * D;  // first element of the row
     const auto ro = make_rsrc(o, ext.o_bytes);
     const auto rto = make_rsrc(to, ext.o_bytes);
 #pragma unroll
@@ -461,8 +473,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
         store4<kOutBf16>(rto, orow + c0, tv);
       }
     if (g == 0) {
-      const uint32_t off = (bh * (uint32_t)Nq + row) * 4;
-      if (lse != nullptr) buf_store4(make_rsrc(lse, ext.lse_bytes), off, (st.m + __log2f(l)) * kLn2);
+      const uint32_t off = (obh * (uint32_t)Nq + row) * 4;
+      if (lse != nullptr)
+        buf_store4(make_rsrc(lse, ext.lse_bytes), off, (st.m + __log2f(l)) * kLn2);
       if (tlse != nullptr) buf_store4(make_rsrc(tlse, ext.lse_bytes), off, mu);
     }
   }
@@ -695,34 +708,36 @@ hipError_t launch_pack_d(const void* k, const void* v, const void* tk, const voi
 template <int D, int kMode, bool kOutBf16>
 hipError_t launch_main_d(const void* q, const void* tq, const void* ws, void* o, void* to,
                          float* lse, float* tlse, int B, int H, int Nq, int Nk, float scale,
-                         hipStream_t stream) {
+                         int nsplit, hipStream_t stream) {
   const int ntiles = (Nk + kBC - 1) / kBC;
   const int nqt = (Nq + kBR - 1) / kBR;
   const int bh = B * H;
+  const int tps = (ntiles + nsplit - 1) / nsplit;
+  const int ns = (ntiles + tps - 1) / tps;  // no empty range
   Extents ext;
   ext.q_bytes = (uint32_t)((size_t)bh * Nq * D * 2);
-  ext.o_bytes = (uint32_t)((size_t)bh * Nq * D * (kOutBf16 ? 2 : 4));
-  ext.lse_bytes = (uint32_t)((size_t)bh * Nq * 4);
-  hipLaunchKernelGGL((attn_jvp_bf16_kernel<D, kMode, kOutBf16>), dim3(nqt * bh),
+  ext.o_bytes = (uint32_t)((size_t)ns * bh * Nq * D * (kOutBf16 ? 2 : 4));
+  ext.lse_bytes = (uint32_t)((size_t)ns * bh * Nq * 4);
+  hipLaunchKernelGGL((attn_jvp_bf16_kernel<D, kMode, kOutBf16>), dim3(nqt * bh * ns),
                      dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(tq), static_cast<const char*>(ws), o, to, lse,
-                     tlse, Nq, Nk, ntiles, nqt, ext, scale, scale * kLog2e);
+                     tlse, Nq, Nk, ntiles, nqt, bh, tps, ext, scale, scale * kLog2e);
   return hipGetLastError();
 }
 
 template <int kMode>
 hipError_t launch_main(const void* q, const void* tq, const void* ws, void* o, void* to,
                        float* lse, float* tlse, int B, int H, int Nq, int Nk, int d, float scale,
-                       bool out_bf16, hipStream_t stream) {
+                       bool out_bf16, hipStream_t stream, int nsplit = 1) {
   if (d == 128)
     return out_bf16 ? launch_main_d<128, kMode, true>(q, tq, ws, o, to, lse, tlse, B, H, Nq, Nk,
-                                                      scale, stream)
+                                                      scale, nsplit, stream)
                     : launch_main_d<128, kMode, false>(q, tq, ws, o, to, lse, tlse, B, H, Nq, Nk,
-                                                       scale, stream);
+                                                       scale, nsplit, stream);
   return out_bf16 ? launch_main_d<64, kMode, true>(q, tq, ws, o, to, lse, tlse, B, H, Nq, Nk,
-                                                   scale, stream)
+                                                   scale, nsplit, stream)
                   : launch_main_d<64, kMode, false>(q, tq, ws, o, to, lse, tlse, B, H, Nq, Nk,
-                                                    scale, stream);
+                                                    scale, nsplit, stream);
 }
 
 hipError_t launch_pack(bool kv_tangents, const void* k, const void* v, const void* tk,
@@ -804,6 +819,92 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                     : launch_fwd_d<128, false>(q, ws, o, lse, B, H, Nq, Nk, scale, stream);
   return out_bf16 ? launch_fwd_d<64, true>(q, ws, o, lse, B, H, Nq, Nk, scale, stream)
                   : launch_fwd_d<64, false>(q, ws, o, lse, B, H, Nq, Nk, scale, stream);
+}
+
+// ---- split-KV: key-tile ranges on separate workgroups, then the merge ----
+// Ranges of whole 64-key tiles: the number actually used is
+// ceil(ntiles / ceil(ntiles / nsplit)) (no empty range).
+namespace {
+constexpr int kSplitMinTiles = 4;        // at least 256 keys per range
+constexpr int kSplitMaxParts = 1024;     // the merge kernel's limit
+constexpr int kSplitCUs = 256;           // one workgroup per compute unit at a time
+// HBM bytes moved in the time of one 64-key tile step of a workgroup
+// (~5 TB/s x ~4.7 us): the unit in which a range's partial state is priced
+constexpr double kSplitTileBytes = 24e6;
+inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+inline int ranges_used(int ntiles, int n) {
+  const int tps = (ntiles + n - 1) / n;
+  return (ntiles + tps - 1) / tps;
+}
+}  // namespace
+
+// The automatic count (nsplit = 0) minimises a model of the time in units of
+// one tile step: rounds of workgroups (items x ranges over 256 compute units)
+// times tiles per range, plus, per extra range, the partial O, dO, lse, mu
+// written and read back by the merge.  A count is taken only if it is at least
+// 5% below the best smaller one.
+int splitkv_count(int B, int H, int Nq, int Nk, int d, int nsplit) {
+  const int ntiles = (Nk + kBC - 1) / kBC;
+  if (nsplit == 0) {
+    const double items = (double)((Nq + kBR - 1) / kBR) * B * H;
+    const double state = (double)B * H * Nq * (2.0 * d + 2.0) * 4.0 * 2.0 / kSplitTileBytes;
+    double best = std::ceil(items / kSplitCUs) * ntiles;
+    nsplit = 1;
+    const int cap = ntiles / kSplitMinTiles < kSplitMaxParts ? ntiles / kSplitMinTiles
+                                                              : kSplitMaxParts;
+    for (int n = 2; n <= cap; ++n) {
+      const int used = ranges_used(ntiles, n);
+      const int tps = (ntiles + n - 1) / n;
+      const double cost = std::ceil(items * used / kSplitCUs) * tps + state * used;
+      if (cost < 0.95 * best) {
+        best = cost;
+        nsplit = n;
+      }
+    }
+  }
+  if (nsplit > ntiles) nsplit = ntiles;
+  if (nsplit > kSplitMaxParts) nsplit = kSplitMaxParts;
+  if (nsplit < 1) nsplit = 1;
+  // partial O and dO arrays each stay under 2^31 bytes
+  const size_t per = (size_t)B * H * Nq * d * 4;
+  while (nsplit > 1 && (size_t)ranges_used(ntiles, nsplit) * per >= ((size_t)1 << 31)) --nsplit;
+  return ranges_used(ntiles, nsplit);
+}
+
+size_t splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int nsplit) {
+  const int ns = splitkv_count(B, H, Nq, Nk, d, nsplit);
+  size_t n = align256(bf16_workspace_bytes(B, H, Nk, d));
+  if (ns > 1) {
+    const size_t rows = (size_t)ns * B * H * Nq;
+    n += 2 * align256(rows * d * 4) + 2 * align256(rows * 4);
+  }
+  return n;
+}
+
+hipError_t launch_bf16_splitkv(const void* q, const void* k, const void* v, const void* tq,
+                               const void* tk, const void* tv, float* o, float* to, float* lse,
+                               float* tlse, int B, int H, int Nq, int Nk, int d, float scale,
+                               int nsplit, void* ws, hipStream_t stream) {
+  const int ns = splitkv_count(B, H, Nq, Nk, d, nsplit);
+  const bool kv = tk != nullptr || tv != nullptr;
+  hipError_t e = launch_pack(kv, k, v, tk, tv, B, H, Nk, d, ws, stream);
+  if (e != hipSuccess) return e;
+  auto fused = [&](float* mo, float* mto, float* ml, float* mtl, int n) {
+    return kv ? launch_main<kFull>(q, tq, ws, mo, mto, ml, mtl, B, H, Nq, Nk, d, scale, false,
+                                   stream, n)
+              : launch_main<kFrozen>(q, tq, ws, mo, mto, ml, mtl, B, H, Nq, Nk, d, scale, false,
+                                     stream, n);
+  };
+  if (ns == 1) return fused(o, to, lse, tlse, 1);
+  char* p = static_cast<char*>(ws) + align256(bf16_workspace_bytes(B, H, Nk, d));
+  const size_t rows = (size_t)ns * B * H * Nq;
+  float* o_p = reinterpret_cast<float*>(p);
+  float* to_p = reinterpret_cast<float*>(p + align256(rows * d * 4));
+  float* lse_p = reinterpret_cast<float*>(p + 2 * align256(rows * d * 4));
+  float* mu_p = reinterpret_cast<float*>(p + 2 * align256(rows * d * 4) + align256(rows * 4));
+  e = fused(o_p, to_p, lse_p, mu_p, ns);
+  if (e != hipSuccess) return e;
+  return launch_merge(lse_p, o_p, to_p, mu_p, ns, B * H * Nq, d, lse, o, to, tlse, stream);
 }
 
 }  // namespace ajvp

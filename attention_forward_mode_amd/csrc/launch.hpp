@@ -33,6 +33,15 @@ hipError_t launch_bf16_ex(const void* q, const void* k, const void* v, const voi
                           float* tlse, int B, int H, int Nq, int Nk, int d, float scale,
                           bool out_bf16, void* workspace, hipStream_t stream);
 
+// Split-KV: the key tiles cut into ranges that run on separate workgroups
+// (nsplit ranges, 0 = chosen from the sizes), partial states merged.
+int splitkv_count(int B, int H, int Nq, int Nk, int d, int nsplit);
+size_t splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int nsplit);
+hipError_t launch_bf16_splitkv(const void* q, const void* k, const void* v, const void* tq,
+                               const void* tk, const void* tv, float* o, float* to, float* lse,
+                               float* tlse, int B, int H, int Nq, int Nk, int d, float scale,
+                               int nsplit, void* ws, hipStream_t stream);
+
 // Forward attention alone (O, lse).
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int Nq, int Nk, int d, float scale, bool out_bf16, void* workspace,

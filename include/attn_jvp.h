@@ -181,6 +181,40 @@ ATTN_JVP_API int attn_jvp_fwd_ex(const void *q, const void *k, const void *v,
                     attn_jvp_stream_t stream);
 
 /*
+ * Split-KV form of the same operation, for few query rows against many keys
+ * (the merge of partial states that exporting the tangent of lse allows; the
+ * rCM record in the Anthology of the SOTA, "Key takeaways", "JVP at
+ * production scale", on the kernel composing with context parallelism): the
+ * 64-key tiles are cut into contiguous ranges that run on separate
+ * workgroups, each range's (lse, O, dO, mu) goes to the workspace, and the
+ * merge of attn_jvp_merge combines them.
+ *   q, k, v, tq, tk, tv, o, to, lse, tlse   as attn_jvp_fwd_ex (tangents may be
+ *                NULL; tk = tv = NULL runs the frozen-key kernel); o, to fp32
+ *   nsplit       number of ranges: 0 chooses one from the sizes (enough
+ *                workgroups for two rounds on the chip, at least 4 tiles per
+ *                range); a larger value than the tile count (or 1024) is
+ *                clamped, and the count used is ceil(ntiles / ceil(ntiles /
+ *                nsplit)).  With one range the result equals attn_jvp_fwd_ex's
+ *                bit for bit.
+ *   workspace    NULL (library pool) or at least
+ *                attn_jvp_splitkv_workspace_bytes(B, H, Nq, Nk, d, nsplit)
+ *                bytes, 256-byte aligned
+ * Results differ from the unsplit pass by rounding only (sums regrouped).
+ * Errors as attn_jvp_fwd_ex; EINVAL also for nsplit < 0.
+ */
+ATTN_JVP_API int attn_jvp_fwd_splitkv(const void *q, const void *k, const void *v,
+                         const void *tq, const void *tk, const void *tv,
+                         float *o, float *to, float *lse, float *tlse,
+                         int B, int H, int Nq, int Nk, int d, float scale, int nsplit,
+                         void *workspace, size_t workspace_bytes,
+                         attn_jvp_stream_t stream);
+
+/* Workspace bytes of attn_jvp_fwd_splitkv (tile images, then the partial
+ * states when more than one range is used); 0 if a size is invalid. */
+ATTN_JVP_API size_t attn_jvp_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d,
+                                                     int nsplit);
+
+/*
  * Forward attention alone (FlashAttention-2's output, without a tangent):
  * O = softmax(scale Q K^T) V and lse, bf16 inputs as in attn_jvp_fwd, O in fp32
  * or bf16 (out_dtype), lse fp32 or NULL.  The pass of attn_jvp_fwd with the

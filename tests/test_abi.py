@@ -290,3 +290,67 @@ def test_merge_rejects_bad_arguments():
         p = [A + j * 0x100000 for j in range(8)]
         p[i] += 2
         assert _merge(p) == EALIGN, i
+
+
+def _split(p=None, nsplit=0, ws=None, ws_bytes=None, **kw):
+    L = ajvp.lib()
+    p = [A + j * 0x100000 for j in range(10)] if p is None else p
+    size = dict(B=1, H=1, Nq=4, Nk=4, d=128, scale=0.1)
+    size.update(kw)
+    return L.attn_jvp_fwd_splitkv(*[ctypes.c_void_p(x) for x in p], size["B"], size["H"],
+                                  size["Nq"], size["Nk"], size["d"], ctypes.c_float(size["scale"]),
+                                  nsplit, ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes or 0),
+                                  ctypes.c_void_p(0))
+
+
+def test_splitkv_rejects_bad_arguments():
+    for i in (0, 1, 2, 6, 7):  # q k v o to are required
+        p = [A + j * 0x100000 for j in range(10)]
+        p[i] = 0
+        assert _split(p) == EINVAL, i
+    assert _split(nsplit=-1) == EINVAL and _split(Nq=0) == EINVAL
+    assert _split(scale=float("inf")) == EINVAL and _split(d=96) == EUNSUPPORTED
+    for i in range(8):
+        p = [A + j * 0x100000 for j in range(10)]
+        p[i] += 8
+        assert _split(p) == EALIGN, i
+    nb = ajvp.attn_jvp_splitkv_workspace_bytes(1, 1, 4, 4, 128, 0)
+    assert _split(ws=A + 0x3000000, ws_bytes=nb - 1) == EINVAL
+    assert _split(ws=A + 0x3000000 + 64, ws_bytes=nb) == EALIGN
+
+
+def test_splitkv_workspace_bytes():
+    """Tile images (as attn_jvp_workspace_bytes, rounded up to 256 bytes), then
+    with more than one range the partial O, dO (fp32 rows x d) and lse, mu
+    (fp32 rows) of every range, each array rounded up to 256 bytes."""
+    img = lambda B, H, Nk, d: ajvp.attn_jvp_workspace_bytes(B, H, Nk, d)
+    r256 = lambda n: -(-n // 256) * 256
+    def want(B, H, Nq, Nk, d, ns):
+        n = r256(img(B, H, Nk, d))
+        if ns > 1:
+            rows = ns * B * H * Nq
+            n += 2 * r256(rows * d * 4) + 2 * r256(rows * 4)
+        return n
+    # one range: the images alone
+    assert ajvp.attn_jvp_splitkv_workspace_bytes(1, 12, 32760, 32760, 128, 1) == \
+        want(1, 12, 32760, 32760, 128, 1)
+    # explicit counts: 512 tiles in ranges of ceil(512 / n) tiles, so
+    # ceil(512 / ceil(512 / n)) ranges (100 -> 6 tiles each -> 86 ranges)
+    for n, used in ((2, 2), (3, 3), (7, 7), (100, 86), (300, 256), (5000, 512)):
+        assert ajvp.attn_jvp_splitkv_workspace_bytes(1, 2, 100, 32760, 128, n) == \
+            want(1, 2, 100, 32760, 128, used), n
+    # automatic: the count is one of the explicit ones, 1 when the row tiles
+    # fill the chip, several for few rows against many keys, and never fewer
+    # than 4 tiles per range
+    def auto_count(B, H, Nq, Nk, d):
+        nb = ajvp.attn_jvp_splitkv_workspace_bytes(B, H, Nq, Nk, d, 0)
+        for n in range(1, 1025):
+            if nb == want(B, H, Nq, Nk, d, n):
+                return n
+        raise AssertionError("no count matches the automatic workspace size")
+    assert auto_count(1, 12, 32760, 32760, 128) == 1      # 1536 row tiles
+    assert auto_count(1, 12, 32760, 512, 128) == 1        # cross-attention shape
+    assert auto_count(2, 16, 4096, 4096, 128) == 1        # 512 row tiles
+    assert auto_count(1, 12, 256, 32760, 128) > 8         # 12 row tiles, 512 key tiles
+    assert 1 < auto_count(1, 1, 10, 512, 64) <= 2         # 8 key tiles: ranges of >= 4
+    assert ajvp.attn_jvp_splitkv_workspace_bytes(1, 1, 10, 512, 64, -1) == 0
