@@ -482,47 +482,50 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
 }
 
 // ---- forward attention alone (O, lse) ----
-// Each wave holds 64 query rows (two 32-row blocks), so every K and V^T
-// fragment it reads from LDS feeds two matrix products, and a workgroup of 8
-// waves covers 512 rows per pass over the key tiles: half the LDS reads and
+// RB = 2: each wave holds 64 query rows (two 32-row blocks), so every K and
+// V^T fragment it reads from LDS feeds two matrix products, and a workgroup of
+// 8 waves covers 512 rows per pass over the key tiles: half the LDS reads and
 // half the tile-image stream per row of a 32-row wave.  Registers: 128
-// accumulators, 64 for the Q fragments, 32 for the two S blocks.
-constexpr int kFwdRB = 2;                         // 32-row blocks per wave
-constexpr int kFwdBR = kWaves * 32 * kFwdRB;      // query rows per workgroup
+// accumulators, 64 for the Q fragments, 32 for the two S blocks; two waves per
+// SIMD.  RB = 1 (32 rows per wave, 256 per workgroup, 128 registers, four
+// waves per SIMD and two workgroups per CU) is used when its 256-row tiles
+// fit the chip one per CU.
+template <int RB>
+constexpr int fwd_rows() { return kWaves * 32 * RB; }  // query rows per workgroup
 
-template <int D>
+template <int D, int RB>
 struct FwdState {
-  f32x16 acc[kFwdRB][D / 32];  // A^T = sum p v per row block (rows: output column)
-  float m[kFwdRB];             // running max, log2 units
-  float l[kFwdRB];             // this lane's half of sum p (of the fp16-rounded p)
+  f32x16 acc[RB][D / 32];  // A^T = sum p v per row block (rows: output column)
+  float m[RB];             // running max, log2 units
+  float l[RB];             // this lane's half of sum p (of the fp16-rounded p)
 };
 
-// One 32-key block for the wave's two row blocks; same arithmetic as the
+// One 32-key block for the wave's RB row blocks; same arithmetic as the
 // tangent-free part of jvp_block (online softmax with the lazy rescale, P
 // rounded to fp16 for the second product, l summed from those values).
-template <int D, bool kMask, typename Issue>
+template <int D, int RB, bool kMask, typename Issue>
 __device__ __attribute__((always_inline)) inline void fwd_block(
-    FwdState<D>& st, const char* stage, int kb, const u32x4 (*qf)[D / 16], int l32, int g,
+    FwdState<D, RB>& st, const char* stage, int kb, const u32x4 (*qf)[D / 16], int l32, int g,
     int key0, int Nk, float c_log2, Issue issue) {
   using G = Geo<D, false>;
   const char* sK = stage;
   const char* sV = stage + G::kOffV;
   const int lane16 = 16 * l32 + 512 * g;
-  f32x16 s[kFwdRB];
+  f32x16 s[RB];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < G::kKS; ++ks) {
     issue(ks);
     const u32x4 kf = lds_load16(sK + lane16 + (kb * G::kKS + ks) * kDmaBytes);
 #pragma unroll
-    for (int rb = 0; rb < kFwdRB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
       s[rb] = mma_bf16(kf, qf[rb][ks], ks == 0 ? f32x16{} : s[rb]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  u32x4 p[kFwdRB][2];
-  float alpha[kFwdRB];
+  u32x4 p[RB][2];
+  float alpha[RB];
 #pragma unroll
-  for (int rb = 0; rb < kFwdRB; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     if constexpr (kMask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -553,48 +556,59 @@ __device__ __attribute__((always_inline)) inline void fwd_block(
     st.l[rb] = st.l[rb] * alpha[rb] + lsum;
   }
   // pin the sums here (an empty asm with register constraints only)
-  asm volatile("" : "+v"(st.l[0]), "+v"(st.l[1]));
-  if (wave_any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+  bool moved = false;
 #pragma unroll
-    for (int rb = 0; rb < kFwdRB; ++rb)
+  for (int rb = 0; rb < RB; ++rb) {
+    asm volatile("" : "+v"(st.l[rb]));
+    moved = moved || alpha[rb] != 1.0f;
+  }
+  if (wave_any(moved)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < G::kCB; ++cb) st.acc[rb][cb] *= alpha[rb];
   }
   __builtin_amdgcn_sched_barrier(0);
-  // A^T += V^T P^T for both row blocks; step = (t, cb) reads fragment
-  // (2 kb + t) kCB + cb, one step ahead
+  // A^T += V^T P^T for every row block; step = (t, cb) reads fragment
+  // (2 kb + t) kCB + cb, one step ahead with two row blocks (the one-block
+  // instance, held to 128 registers, reads it at its step)
   constexpr int kSteps = 2 * G::kCB;
+  constexpr bool kPf = RB > 1;
   auto voff = [&](int step) { return lane16 + (2 * kb * G::kCB + step) * kDmaBytes; };
   u32x4 vfp[2];
-  vfp[0] = lds_load16(sV + voff(0));
+  if constexpr (kPf) vfp[0] = lds_load16(sV + voff(0));
 #pragma unroll
   for (int step = 0; step < kSteps; ++step) {
     const int t = step / G::kCB, cb = step % G::kCB;
     issue(G::kKS + step);
-    if (step + 1 < kSteps) vfp[(step + 1) & 1] = lds_load16(sV + voff(step + 1));
+    if constexpr (kPf) {
+      if (step + 1 < kSteps) vfp[(step + 1) & 1] = lds_load16(sV + voff(step + 1));
+    } else {
+      vfp[step & 1] = lds_load16(sV + voff(step));
+    }
     const u32x4 vf = vfp[step & 1];
 #pragma unroll
-    for (int rb = 0; rb < kFwdRB; ++rb) st.acc[rb][cb] = mma_f16(vf, p[rb][t], st.acc[rb][cb]);
+    for (int rb = 0; rb < RB; ++rb) st.acc[rb][cb] = mma_f16(vf, p[rb][t], st.acc[rb][cb]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int D, typename Copy>
+template <int D, int RB, typename Copy>
 __device__ __attribute__((always_inline)) inline void fwd_tile(
-    char* __restrict__ next, const char* __restrict__ cur, Copy copy, FwdState<D>& st,
+    char* __restrict__ next, const char* __restrict__ cur, Copy copy, FwdState<D, RB>& st,
     const u32x4 (*qf)[D / 16], int l32, int g, int Nk, float c_log2) {
   using G = Geo<D, false>;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
-    fwd_block<D, false>(st, cur, kb, qf, l32, g, 0, Nk, c_log2, [&](int slot) {
+    fwd_block<D, RB, false>(st, cur, kb, qf, l32, g, 0, Nk, c_log2, [&](int slot) {
       if (kb == 0 && slot < G::kDmaPerWave) copy(next, slot);
     });
 }
 
 // o: [B, H, Nq, D] fp32 or bf16; lse: [B, H, Nq] fp32 or NULL.  Tile images
 // hold K and V^T only (the layout of the frozen-key mode).
-template <int D, bool kOutBf16>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
+template <int D, int RB, bool kOutBf16>
+__global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const char* __restrict__ img, void* __restrict__ o,
     float* __restrict__ lse, int Nq, int Nk, int ntiles, int nqt, Extents ext, float c_log2) {
   using G = Geo<D, false>;
@@ -609,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int row0 = qt * kFwdBR + wave * 32 * kFwdRB + l32;  // row of block rb: row0 + 32 rb
+  const int row0 = qt * fwd_rows<RB>() + wave * 32 * RB + l32;  // block rb: row0 + 32 rb
 
   const auto rq = make_rsrc(q, ext.q_bytes);
   const uint32_t slice_bytes = (uint32_t)ntiles * G::kImgBytes;
@@ -624,18 +638,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   for (int j = 0; j < G::kDmaPerWave; ++j) copy_one(0, smem, j);
 
   // Q fragments of both row blocks (rows past Nq read as 0 through the descriptor)
-  u32x4 qf[kFwdRB][G::kKS];
+  u32x4 qf[RB][G::kKS];
 #pragma unroll
-  for (int rb = 0; rb < kFwdRB; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int row = row0 + 32 * rb;
     const uint32_t qrow = row < Nq ? (bh * (uint32_t)Nq + row) * D * 2 : 0x80000000u;
 #pragma unroll
     for (int ks = 0; ks < G::kKS; ++ks) qf[rb][ks] = buf_load16(rq, qrow + (16 * ks + 8 * g) * 2);
   }
 
-  FwdState<D> st;
+  FwdState<D, RB> st;
 #pragma unroll
-  for (int rb = 0; rb < kFwdRB; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int cb = 0; cb < G::kCB; ++cb) st.acc[rb][cb] = f32x16{};
     st.m[rb] = -INFINITY;
@@ -646,7 +660,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < kLast; ++kt) {
-    fwd_tile<D>(smem + ((kt + 1) & 1) * G::kImgBytes, smem + (kt & 1) * G::kImgBytes,
+    fwd_tile<D, RB>(smem + ((kt + 1) & 1) * G::kImgBytes, smem + (kt & 1) * G::kImgBytes,
                 [&](char* next, int j) { copy_one(kt + 1, next, j); }, st, qf, l32, g, Nk,
                 c_log2);
     __builtin_amdgcn_s_waitcnt(0);
@@ -656,13 +670,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const char* cur = smem + (kLast & 1) * G::kImgBytes;
     const int kl = kLast * kBC;
     auto none = [](int) {};
-    fwd_block<D, true>(st, cur, 0, qf, l32, g, kl, Nk, c_log2, none);
-    fwd_block<D, true>(st, cur, 1, qf, l32, g, kl + 32, Nk, c_log2, none);
+    fwd_block<D, RB, true>(st, cur, 0, qf, l32, g, kl, Nk, c_log2, none);
+    fwd_block<D, RB, true>(st, cur, 1, qf, l32, g, kl + 32, Nk, c_log2, none);
   }
 
   const auto ro = make_rsrc(o, ext.o_bytes);
 #pragma unroll
-  for (int rb = 0; rb < kFwdRB; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int row = row0 + 32 * rb;
     const float l = halves_sum(st.l[rb]);
     const float inv_l = 1.0f / l;
@@ -793,20 +807,32 @@ hipError_t launch_bf16_ex(const void* q, const void* k, const void* v, const voi
                                    stream);
 }
 
-template <int D, bool kOutBf16>
-hipError_t launch_fwd_d(const void* q, const void* ws, void* o, float* lse, int B, int H, int Nq,
-                        int Nk, float scale, hipStream_t stream) {
+template <int D, int RB, bool kOutBf16>
+hipError_t launch_fwd_rb(const void* q, const void* ws, void* o, float* lse, int B, int H, int Nq,
+                         int Nk, float scale, hipStream_t stream) {
   const int ntiles = (Nk + kBC - 1) / kBC;
-  const int nqt = (Nq + kFwdBR - 1) / kFwdBR;
+  const int nqt = (Nq + fwd_rows<RB>() - 1) / fwd_rows<RB>();
   const int bh = B * H;
   Extents ext;
   ext.q_bytes = (uint32_t)((size_t)bh * Nq * D * 2);
   ext.o_bytes = (uint32_t)((size_t)bh * Nq * D * (kOutBf16 ? 2 : 4));
   ext.lse_bytes = (uint32_t)((size_t)bh * Nq * 4);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, kOutBf16>), dim3(nqt * bh), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, RB, kOutBf16>), dim3(nqt * bh), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(q), static_cast<const char*>(ws), o, lse,
                      Nq, Nk, ntiles, nqt, ext, scale * kLog2e);
   return hipGetLastError();
+}
+
+// 512-row workgroups, unless even the 256-row ones fit the chip's 256 CUs
+// one per CU (then twice as many CUs work; measured at Nk = 32760, H = 12:
+// Nq = 4096 1446 -> 994 us, Nq = 8192 with 512 rows 1534 us vs 1730)
+template <int D, bool kOutBf16>
+hipError_t launch_fwd_d(const void* q, const void* ws, void* o, float* lse, int B, int H, int Nq,
+                        int Nk, float scale, hipStream_t stream) {
+  const long tiles256 = (long)(Nq + fwd_rows<1>() - 1) / fwd_rows<1>() * B * H;
+  if (tiles256 > 256)
+    return launch_fwd_rb<D, 2, kOutBf16>(q, ws, o, lse, B, H, Nq, Nk, scale, stream);
+  return launch_fwd_rb<D, 1, kOutBf16>(q, ws, o, lse, B, H, Nq, Nk, scale, stream);
 }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
