@@ -184,8 +184,10 @@ def bench_variant(args, ajvp, w, g, x, scale):
                                ", fp32 lse")},
         "flops_per_step": fl,
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"kernel": ("pack_q + pack_k + bwd_kv + bwd_q (one call)" if args.mode == "bwd"
-                                else "pack_kv + attn_jvp_bf16 (one call, pack included)"),
+        "roofline": {"kernel": {"bwd": "pack_q + pack_k + bwd_kv + bwd_q (one call)",
+                                "fwd": "pack_kv + attn_fwd_bf16_kernel (one call, pack included)"}
+                               .get(args.mode, "pack_kv + attn_jvp_bf16_kernel (one call, pack "
+                                               "included)"),
                      "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
@@ -295,7 +297,7 @@ def main():
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "hbm_gbs_algorithmic": round(alg_bytes / (ms / 1e3) / 1e9, 1),
         "roofline": {
-            "kernel": f"attn_jvp_bf16_d{d}",
+            "kernel": f"attn_jvp_bf16_kernel<{d}, 0, false>",
             "bound": "mfma",
             "achieved": round(kern_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
