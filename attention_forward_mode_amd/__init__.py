@@ -72,6 +72,8 @@ def lib():
     L.attn_jvp_fwd_splitkv.restype = _i
     L.attn_jvp_splitkv_workspace_bytes.argtypes = [_i] * 6
     L.attn_jvp_splitkv_workspace_bytes.restype = _sz
+    L.attn_fwd_splitkv.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
+    L.attn_fwd_splitkv.restype = _i
     L.attn_fwd.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
     L.attn_fwd.restype = _i
     L.attn_jvp_merge.argtypes = [_vp] * 4 + [_i] * 3 + [_vp] * 5
@@ -311,6 +313,23 @@ def attn_jvp_fwd_splitkv(q, k, v, tq=None, tk=None, tv=None, scale=None, nsplit=
     if rc != OK:
         raise AttnJvpError(rc)
     return o, to, lse_t, tlse_t
+
+
+def attn_fwd_splitkv(q, k, v, scale=None, nsplit=0, lse=True, workspace=None):
+    """attn_fwd with the key tiles cut into nsplit ranges (0: chosen from the
+    sizes) and the partial states merged.  fp32 outputs; returns (o, lse)."""
+    B, H, Nq, Nk, d = _check(q, k, v, q, k, v, torch.bfloat16)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    lse_t = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse else None
+    wp, wb = _ws_arg(workspace, q.device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Nq, Nk,
+                                    d, s, int(nsplit), wp, wb, stream)
+    if rc != OK:
+        raise AttnJvpError(rc)
+    return o, lse_t
 
 
 def attn_fwd(q, k, v, scale=None, lse=True, out_dtype=torch.float32, workspace=None):

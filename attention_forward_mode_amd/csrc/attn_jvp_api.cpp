@@ -249,6 +249,22 @@ int attn_jvp_fwd_splitkv(const void* q, const void* k, const void* v, const void
   });
 }
 
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                     int H, int Nq, int Nk, int d, float scale, int nsplit, void* workspace,
+                     size_t workspace_bytes, attn_jvp_stream_t stream) {
+  const void* in[3] = {q, k, v};
+  if (o == nullptr) return ATTN_JVP_EINVAL;
+  // validate() also wants a tangent output; o stands in for it here
+  int rc = validate(in, 3, o, o, lse, B, H, Nq, Nk, d, scale, 2);
+  if (rc != ATTN_JVP_OK) return rc;
+  if (nsplit < 0) return ATTN_JVP_EINVAL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const size_t need = ajvp::splitkv_workspace_bytes(B, H, Nq, Nk, d, nsplit);
+  return with_workspace_n(workspace, workspace_bytes, need, st, [&](void* ws) {
+    return ajvp::launch_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, nsplit, ws, st);
+  });
+}
+
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int Nq, int Nk, int d, float scale, int out_dtype, void* workspace,
              size_t workspace_bytes, attn_jvp_stream_t stream) {

@@ -610,16 +610,20 @@ __device__ __attribute__((always_inline)) inline void fwd_tile(
 template <int D, int RB, bool kOutBf16>
 __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const char* __restrict__ img, void* __restrict__ o,
-    float* __restrict__ lse, int Nq, int Nk, int ntiles, int nqt, Extents ext, float c_log2) {
+    float* __restrict__ lse, int Nq, int Nk, int ntiles, int nqt, int nbh, int tps, Extents ext,
+    float c_log2) {
   using G = Geo<D, false>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * G::kImgBytes];
-  // XCD-aware work order, as in attn_jvp_bf16_kernel
+  // XCD-aware work order and key-tile ranges, as in attn_jvp_bf16_kernel
   const uint32_t wg = blockIdx.x, nwg = gridDim.x;
   const uint32_t xcd = wg % kXcds, slot = wg / kXcds, per = nwg / kXcds, extra = nwg % kXcds;
   const uint32_t work = xcd < extra ? xcd * (per + 1) + slot
                                     : extra * (per + 1) + (xcd - extra) * per + slot;
   const int qt = (int)(work % (uint32_t)nqt);
-  const uint32_t bh = work / (uint32_t)nqt;
+  const uint32_t obh = work / (uint32_t)nqt;  // output slice: split * nbh + bh
+  const uint32_t bh = obh % (uint32_t)nbh;
+  const int t0 = (int)(obh / (uint32_t)nbh) * tps;
+  const int t1 = t0 + tps < ntiles ? t0 + tps : ntiles;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
@@ -635,9 +639,9 @@ __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kerne
                                              16, lane * 16, src, 0, 0);
   };
 #pragma unroll
-  for (int j = 0; j < G::kDmaPerWave; ++j) copy_one(0, smem, j);
+  for (int j = 0; j < G::kDmaPerWave; ++j) copy_one(t0, smem, j);
 
-  // Q fragments of both row blocks (rows past Nq read as 0 through the descriptor)
+  // Q fragments of the row blocks (rows past Nq read as 0 through the descriptor)
   u32x4 qf[RB][G::kKS];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -656,18 +660,19 @@ __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kerne
     st.l[rb] = 0.f;
   }
 
-  const int kLast = ntiles - 1;
+  const int kLast = t1 - 1;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = 0; kt < kLast; ++kt) {
-    fwd_tile<D, RB>(smem + ((kt + 1) & 1) * G::kImgBytes, smem + (kt & 1) * G::kImgBytes,
-                [&](char* next, int j) { copy_one(kt + 1, next, j); }, st, qf, l32, g, Nk,
-                c_log2);
+  for (int kt = t0; kt < kLast; ++kt) {
+    const int sc = (kt - t0) & 1;
+    fwd_tile<D, RB>(smem + (sc ^ 1) * G::kImgBytes, smem + sc * G::kImgBytes,
+                    [&](char* next, int j) { copy_one(kt + 1, next, j); }, st, qf, l32, g, Nk,
+                    c_log2);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   {
-    const char* cur = smem + (kLast & 1) * G::kImgBytes;
+    const char* cur = smem + ((kLast - t0) & 1) * G::kImgBytes;
     const int kl = kLast * kBC;
     auto none = [](int) {};
     fwd_block<D, RB, true>(st, cur, 0, qf, l32, g, kl, Nk, c_log2, none);
@@ -681,7 +686,7 @@ __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kerne
     const float l = halves_sum(st.l[rb]);
     const float inv_l = 1.0f / l;
     if (row < Nq) {
-      const uint32_t orow = (bh * (uint32_t)Nq + row) * D;
+      const uint32_t orow = (obh * (uint32_t)Nq + row) * D;
 #pragma unroll
       for (int cb = 0; cb < G::kCB; ++cb)
 #pragma unroll
@@ -692,7 +697,7 @@ __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kerne
           store4<kOutBf16>(ro, orow + 32 * cb + 8 * qq + 4 * g, ov);
         }
       if (g == 0 && lse != nullptr)
-        buf_store4(make_rsrc(lse, ext.lse_bytes), (bh * (uint32_t)Nq + row) * 4,
+        buf_store4(make_rsrc(lse, ext.lse_bytes), (obh * (uint32_t)Nq + row) * 4,
                    (st.m[rb] + __log2f(l)) * kLn2);
     }
   }
@@ -809,30 +814,33 @@ hipError_t launch_bf16_ex(const void* q, const void* k, const void* v, const voi
 
 template <int D, int RB, bool kOutBf16>
 hipError_t launch_fwd_rb(const void* q, const void* ws, void* o, float* lse, int B, int H, int Nq,
-                         int Nk, float scale, hipStream_t stream) {
+                         int Nk, float scale, int ns, hipStream_t stream) {
   const int ntiles = (Nk + kBC - 1) / kBC;
   const int nqt = (Nq + fwd_rows<RB>() - 1) / fwd_rows<RB>();
   const int bh = B * H;
+  const int tps = (ntiles + ns - 1) / ns;
+  ns = (ntiles + tps - 1) / tps;
   Extents ext;
   ext.q_bytes = (uint32_t)((size_t)bh * Nq * D * 2);
-  ext.o_bytes = (uint32_t)((size_t)bh * Nq * D * (kOutBf16 ? 2 : 4));
-  ext.lse_bytes = (uint32_t)((size_t)bh * Nq * 4);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, RB, kOutBf16>), dim3(nqt * bh), dim3(kThreads), 0,
-                     stream, static_cast<const uint16_t*>(q), static_cast<const char*>(ws), o, lse,
-                     Nq, Nk, ntiles, nqt, ext, scale * kLog2e);
+  ext.o_bytes = (uint32_t)((size_t)ns * bh * Nq * D * (kOutBf16 ? 2 : 4));
+  ext.lse_bytes = (uint32_t)((size_t)ns * bh * Nq * 4);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, RB, kOutBf16>), dim3(nqt * bh * ns), dim3(kThreads),
+                     0, stream, static_cast<const uint16_t*>(q), static_cast<const char*>(ws), o,
+                     lse, Nq, Nk, ntiles, nqt, bh, tps, ext, scale * kLog2e);
   return hipGetLastError();
 }
 
 // 512-row workgroups, unless even the 256-row ones fit the chip's 256 CUs
 // one per CU (then twice as many CUs work; measured at Nk = 32760, H = 12:
-// Nq = 4096 1446 -> 994 us, Nq = 8192 with 512 rows 1534 us vs 1730)
+// Nq = 4096 1446 -> 994 us, Nq = 8192 with 512 rows 1534 us vs 1730).  ns
+// key-tile ranges (1: the plain pass).
 template <int D, bool kOutBf16>
 hipError_t launch_fwd_d(const void* q, const void* ws, void* o, float* lse, int B, int H, int Nq,
-                        int Nk, float scale, hipStream_t stream) {
-  const long tiles256 = (long)(Nq + fwd_rows<1>() - 1) / fwd_rows<1>() * B * H;
+                        int Nk, float scale, int ns, hipStream_t stream) {
+  const long tiles256 = (long)(Nq + fwd_rows<1>() - 1) / fwd_rows<1>() * B * H * ns;
   if (tiles256 > 256)
-    return launch_fwd_rb<D, 2, kOutBf16>(q, ws, o, lse, B, H, Nq, Nk, scale, stream);
-  return launch_fwd_rb<D, 1, kOutBf16>(q, ws, o, lse, B, H, Nq, Nk, scale, stream);
+    return launch_fwd_rb<D, 2, kOutBf16>(q, ws, o, lse, B, H, Nq, Nk, scale, ns, stream);
+  return launch_fwd_rb<D, 1, kOutBf16>(q, ws, o, lse, B, H, Nq, Nk, scale, ns, stream);
 }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -841,11 +849,12 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
   hipError_t e = launch_pack(false, k, v, nullptr, nullptr, B, H, Nk, d, ws, stream);
   if (e != hipSuccess) return e;
   if (d == 128)
-    return out_bf16 ? launch_fwd_d<128, true>(q, ws, o, lse, B, H, Nq, Nk, scale, stream)
-                    : launch_fwd_d<128, false>(q, ws, o, lse, B, H, Nq, Nk, scale, stream);
-  return out_bf16 ? launch_fwd_d<64, true>(q, ws, o, lse, B, H, Nq, Nk, scale, stream)
-                  : launch_fwd_d<64, false>(q, ws, o, lse, B, H, Nq, Nk, scale, stream);
+    return out_bf16 ? launch_fwd_d<128, true>(q, ws, o, lse, B, H, Nq, Nk, scale, 1, stream)
+                    : launch_fwd_d<128, false>(q, ws, o, lse, B, H, Nq, Nk, scale, 1, stream);
+  return out_bf16 ? launch_fwd_d<64, true>(q, ws, o, lse, B, H, Nq, Nk, scale, 1, stream)
+                  : launch_fwd_d<64, false>(q, ws, o, lse, B, H, Nq, Nk, scale, 1, stream);
 }
+
 
 // ---- split-KV: key-tile ranges on separate workgroups, then the merge ----
 // Ranges of whole 64-key tiles: the number actually used is
@@ -865,14 +874,15 @@ inline int ranges_used(int ntiles, int n) {
 }  // namespace
 
 // The automatic count (nsplit = 0) minimises a model of the time in units of
-// one tile step: rounds of workgroups (items x ranges over 256 compute units)
-// times tiles per range, plus, per extra range, the partial O, dO, lse, mu
-// written and read back by the merge.  A count is taken only if it is at least
-// 5% below the best smaller one.
-int splitkv_count(int B, int H, int Nq, int Nk, int d, int nsplit) {
+// one tile step: rounds of workgroups (items of `rows` query rows x ranges
+// over 256 compute units) times tiles per range, plus, per extra range, the
+// partial O, dO, lse, mu written and read back by the merge.  A count is taken
+// only if it is at least 5% below the best smaller one.  rows: 256 for the
+// JVP kernel, 512 for the forward one.
+int splitkv_count(int B, int H, int Nq, int Nk, int d, int nsplit, int rows) {
   const int ntiles = (Nk + kBC - 1) / kBC;
   if (nsplit == 0) {
-    const double items = (double)((Nq + kBR - 1) / kBR) * B * H;
+    const double items = (double)((Nq + rows - 1) / rows) * B * H;
     const double state = (double)B * H * Nq * (2.0 * d + 2.0) * 4.0 * 2.0 / kSplitTileBytes;
     double best = std::ceil(items / kSplitCUs) * ntiles;
     nsplit = 1;
@@ -897,8 +907,11 @@ int splitkv_count(int B, int H, int Nq, int Nk, int d, int nsplit) {
   return ranges_used(ntiles, nsplit);
 }
 
+// Workspace for either kernel's count (the forward one may choose more ranges).
 size_t splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int nsplit) {
-  const int ns = splitkv_count(B, H, Nq, Nk, d, nsplit);
+  const int a = splitkv_count(B, H, Nq, Nk, d, nsplit, kBR);
+  const int b = splitkv_count(B, H, Nq, Nk, d, nsplit, fwd_rows<2>());
+  const int ns = a > b ? a : b;
   size_t n = align256(bf16_workspace_bytes(B, H, Nk, d));
   if (ns > 1) {
     const size_t rows = (size_t)ns * B * H * Nq;
@@ -911,7 +924,7 @@ hipError_t launch_bf16_splitkv(const void* q, const void* k, const void* v, cons
                                const void* tk, const void* tv, float* o, float* to, float* lse,
                                float* tlse, int B, int H, int Nq, int Nk, int d, float scale,
                                int nsplit, void* ws, hipStream_t stream) {
-  const int ns = splitkv_count(B, H, Nq, Nk, d, nsplit);
+  const int ns = splitkv_count(B, H, Nq, Nk, d, nsplit, kBR);
   const bool kv = tk != nullptr || tv != nullptr;
   hipError_t e = launch_pack(kv, k, v, tk, tv, B, H, Nk, d, ws, stream);
   if (e != hipSuccess) return e;
@@ -931,6 +944,29 @@ hipError_t launch_bf16_splitkv(const void* q, const void* k, const void* v, cons
   e = fused(o_p, to_p, lse_p, mu_p, ns);
   if (e != hipSuccess) return e;
   return launch_merge(lse_p, o_p, to_p, mu_p, ns, B * H * Nq, d, lse, o, to, tlse, stream);
+}
+
+// Forward alone with key-tile ranges: partial O and lse in the workspace
+// (after the tile images, laid out as for the JVP's split), then the merge.
+hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, float* o, float* lse,
+                              int B, int H, int Nq, int Nk, int d, float scale, int nsplit,
+                              void* ws, hipStream_t stream) {
+  const int ns = splitkv_count(B, H, Nq, Nk, d, nsplit, fwd_rows<2>());
+  hipError_t e = launch_pack(false, k, v, nullptr, nullptr, B, H, Nk, d, ws, stream);
+  if (e != hipSuccess) return e;
+  auto fwd = [&](float* mo, float* ml, int n) {
+    return d == 128 ? launch_fwd_d<128, false>(q, ws, mo, ml, B, H, Nq, Nk, scale, n, stream)
+                    : launch_fwd_d<64, false>(q, ws, mo, ml, B, H, Nq, Nk, scale, n, stream);
+  };
+  if (ns == 1) return fwd(o, lse, 1);
+  char* p = static_cast<char*>(ws) + align256(bf16_workspace_bytes(B, H, Nk, d));
+  const size_t rows = (size_t)ns * B * H * Nq;
+  float* o_p = reinterpret_cast<float*>(p);
+  float* lse_p = reinterpret_cast<float*>(p + 2 * align256(rows * d * 4));
+  e = fwd(o_p, lse_p, ns);
+  if (e != hipSuccess) return e;
+  return launch_merge(lse_p, o_p, nullptr, nullptr, ns, B * H * Nq, d, lse, o, nullptr, nullptr,
+                      stream);
 }
 
 }  // namespace ajvp

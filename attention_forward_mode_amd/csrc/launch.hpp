@@ -35,12 +35,17 @@ hipError_t launch_bf16_ex(const void* q, const void* k, const void* v, const voi
 
 // Split-KV: the key tiles cut into ranges that run on separate workgroups
 // (nsplit ranges, 0 = chosen from the sizes), partial states merged.
-int splitkv_count(int B, int H, int Nq, int Nk, int d, int nsplit);
+int splitkv_count(int B, int H, int Nq, int Nk, int d, int nsplit, int rows);
 size_t splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int nsplit);
 hipError_t launch_bf16_splitkv(const void* q, const void* k, const void* v, const void* tq,
                                const void* tk, const void* tv, float* o, float* to, float* lse,
                                float* tlse, int B, int H, int Nq, int Nk, int d, float scale,
                                int nsplit, void* ws, hipStream_t stream);
+
+// Forward attention alone with key-tile ranges (fp32 O), merged.
+hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, float* o, float* lse,
+                              int B, int H, int Nq, int Nk, int d, float scale, int nsplit,
+                              void* ws, hipStream_t stream);
 
 // Forward attention alone (O, lse).
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,

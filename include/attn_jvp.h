@@ -215,6 +215,20 @@ ATTN_JVP_API size_t attn_jvp_splitkv_workspace_bytes(int B, int H, int Nq, int N
                                                      int nsplit);
 
 /*
+ * attn_fwd (forward attention alone) with the key tiles cut into ranges as in
+ * attn_jvp_fwd_splitkv, partial (lse, O) merged: for few query rows against
+ * many keys.  o fp32 [B, H, Nq, d], lse fp32 [B, H, Nq] or NULL; nsplit and
+ * the workspace as attn_jvp_fwd_splitkv (attn_jvp_splitkv_workspace_bytes
+ * bytes suffice).  With one range the result equals attn_fwd's bit for bit.
+ * Errors as attn_fwd; EINVAL also for nsplit < 0.
+ */
+ATTN_JVP_API int attn_fwd_splitkv(const void *q, const void *k, const void *v,
+                     float *o, float *lse,
+                     int B, int H, int Nq, int Nk, int d, float scale, int nsplit,
+                     void *workspace, size_t workspace_bytes,
+                     attn_jvp_stream_t stream);
+
+/*
  * Forward attention alone (FlashAttention-2's output, without a tangent):
  * O = softmax(scale Q K^T) V and lse, bf16 inputs as in attn_jvp_fwd, O in fp32
  * or bf16 (out_dtype), lse fp32 or NULL.  The pass of attn_jvp_fwd with the

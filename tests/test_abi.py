@@ -354,3 +354,22 @@ def test_splitkv_workspace_bytes():
     assert auto_count(1, 12, 256, 32760, 128) > 8         # 12 row tiles, 512 key tiles
     assert 1 < auto_count(1, 1, 10, 512, 64) <= 2         # 8 key tiles: ranges of >= 4
     assert ajvp.attn_jvp_splitkv_workspace_bytes(1, 1, 10, 512, 64, -1) == 0
+
+
+def test_fwd_splitkv_rejects_bad_arguments():
+    L = ajvp.lib()
+    def call(p=None, nsplit=0, ws=None, ws_bytes=0, d=128, Nq=4):
+        p = [A + j * 0x100000 for j in range(5)] if p is None else p  # q k v o lse
+        return L.attn_fwd_splitkv(*[ctypes.c_void_p(x) for x in p], 1, 1, Nq, 4, d,
+                                  ctypes.c_float(0.1), nsplit, ctypes.c_void_p(ws),
+                                  ctypes.c_size_t(ws_bytes), ctypes.c_void_p(0))
+    for i in range(4):  # q k v o (lse optional)
+        p = [A + j * 0x100000 for j in range(5)]
+        p[i] = 0
+        assert call(p) == EINVAL, i
+    assert call(nsplit=-2) == EINVAL and call(Nq=0) == EINVAL and call(d=96) == EUNSUPPORTED
+    p = [A + j * 0x100000 for j in range(5)]
+    p[3] += 8
+    assert call(p) == EALIGN
+    nb = ajvp.attn_jvp_splitkv_workspace_bytes(1, 1, 4, 4, 128, 0)
+    assert call(ws=A + 0x3000000, ws_bytes=nb - 1) == EINVAL

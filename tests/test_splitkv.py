@@ -69,3 +69,25 @@ def test_short_queries_long_keys_full_length():
             ref[i].append(r)
     check("split 256 x 32760 H12 auto", tuple(np.concatenate(a) for a in got),
           tuple(np.concatenate(r) for r in ref), fp32=False)
+
+
+def test_forward_one_range_is_attn_fwd():
+    x, s = make_inputs("image_dit", Nq=333, Nk=2000, heads=[0, 1])
+    g = to_device(x)
+    print("  launch attn_fwd_splitkv nsplit=1 / attn_fwd", flush=True)
+    a = ajvp.attn_fwd_splitkv(g["q"], g["k"], g["v"], scale=s, nsplit=1)
+    b = ajvp.attn_fwd(g["q"], g["k"], g["v"], scale=s)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("Nq,Nk,nsplit", [(1, 5000, 0), (100, 1000, 3), (77, 4097, 16),
+                                          (600, 2000, 0)])
+def test_forward_split_ranges_against_oracle(Nq, Nk, nsplit):
+    x, s = make_inputs("video_14b", Nq=Nq, Nk=Nk, heads=[0, 1])
+    g = to_device(x)
+    print(f"  launch attn_fwd_splitkv nsplit={nsplit} Nq={Nq} Nk={Nk}", flush=True)
+    o, lse = ajvp.attn_fwd_splitkv(g["q"], g["k"], g["v"], scale=s, nsplit=nsplit)
+    torch.cuda.synchronize()
+    O, L = oracle.attention(x["q"], x["k"], x["v"], s)
+    check(f"fwd split Nq={Nq} Nk={Nk} n={nsplit}", (o, None, lse), (O, None, L), fp32=False)
