@@ -184,44 +184,47 @@ __device__ __attribute__((always_inline)) inline int slot_key(int r, int g) {
   return 8 * (r >> 2) + 4 * g + (r & 3);
 }
 
-// One 32-key block (block `kb` of the tile in `stage`) for this wave's 32
-// query rows.  kMask: the block lies in the last tile, whose keys >= Nk get
-// p = 0 and contribute nothing to u.  issue(slot) is called at the start of
-// each step (slots 0..kKS-1: the S/dS steps, then the P V steps).
+// One 32-key block for this wave's 32 query rows, in two phases so that a
+// caller can put other work between them: qk_phase forms S^T and dS^T from
+// the K and dK fragments at kbase, dkbase; sm_pv_phase runs the softmax on
+// them and adds the block's P V products with the V^T and dV^T fragments at
+// vbase, dvbase (fragment f of a part at base + f KiB, the tile image's
+// layout).  kMask: the block may hold keys >= Nk, which get p = 0 and
+// contribute nothing to u.  issue(slot) is called at the start of each step
+// (slots 0..kKS-1: the S/dS steps, then kKS.. the P V steps).
 // Online-softmax order: the accumulators hold sums normalised to the running
 // max m; a raised max rescales them by alpha = 2^(m_old - m_new) before this
 // block's P V is added.
-template <int D, int kMode, bool kMask, typename Issue>
-__device__ __attribute__((always_inline)) inline void jvp_block(
-    RowState<D>& st, const char* stage, int kb, const u32x4* qf, const u32x4* dqf, int l32,
-    int g, int key0, int Nk, float c_log2, float scale, Issue issue) {
+template <int D, int kMode, typename Issue>
+__device__ __attribute__((always_inline)) inline void qk_phase(
+    f32x16& s, f32x16& ds, const char* kbase, const char* dkbase, const u32x4* qf,
+    const u32x4* dqf, int lane16, Issue issue) {
   using M = Mode<kMode>;
   using G = Geo<D, M::kKV>;
-  const char* sK = stage;
-  const char* sdK = stage + G::kOffdK;
-  const char* sV = stage + G::kOffV;
-  const char* sdV = stage + G::kOffdV;
-
   // S^T and dS^T (rows: key, columns: this wave's queries).  The K and dK
   // fragments are read at their own step (the other wave on the SIMD covers
   // the LDS latency); scheduling barriers keep the compiler from hoisting
   // reads, and their registers, across steps.
-  const int lane16 = 16 * l32 + 512 * g;  // this lane's 16 bytes of a fragment
-  f32x16 s, ds;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < G::kKS; ++ks) {
     issue(ks);
-    const int kfrag = (kb * G::kKS + ks) * kDmaBytes;
-    const u32x4 kf = lds_load16(sK + lane16 + kfrag);
+    const u32x4 kf = lds_load16(kbase + lane16 + ks * kDmaBytes);
     u32x4 dkf;
-    if constexpr (M::kKV) dkf = lds_load16(sdK + lane16 + kfrag);
+    if constexpr (M::kKV) dkf = lds_load16(dkbase + lane16 + ks * kDmaBytes);
     s = mma_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s);
     ds = mma_bf16(kf, dqf[ks], ks == 0 ? f32x16{} : ds);
     if constexpr (M::kKV) ds = mma_bf16(dkf, qf[ks], ds);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
 
+template <int D, int kMode, bool kMask, typename Issue>
+__device__ __attribute__((always_inline)) inline void sm_pv_phase(
+    RowState<D>& st, f32x16 s, f32x16 ds, const char* vbase, const char* dvbase, int lane16,
+    int g, int key0, int Nk, float c_log2, float scale, Issue issue) {
+  using M = Mode<kMode>;
+  using G = Geo<D, M::kKV>;
   // running max (NaN-propagating maximum, combined across the half-waves)
   if constexpr (kMask) {
 #pragma unroll
@@ -282,25 +285,40 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
   // V^T and dV^T fragments read one step ahead (S and dS are dead by now, so
   // the prefetch registers come free)
   constexpr int kSteps = 2 * G::kCB;
-  auto voff = [&](int step) {  // fragment (2 kb + t) kCB + cb, step = t kCB + cb
-    return lane16 + (2 * kb * G::kCB + step) * kDmaBytes;
+  auto voff = [&](int step) {  // fragment t kCB + cb of the block, step = t kCB + cb
+    return lane16 + step * kDmaBytes;
   };
   u32x4 vf[2], dvf[2];
-  vf[0] = lds_load16(sV + voff(0));
-  if constexpr (M::kKV) dvf[0] = lds_load16(sdV + voff(0));
+  vf[0] = lds_load16(vbase + voff(0));
+  if constexpr (M::kKV) dvf[0] = lds_load16(dvbase + voff(0));
 #pragma unroll
   for (int step = 0; step < kSteps; ++step) {
     const int t = step / G::kCB, cb = step % G::kCB;
     issue(G::kKS + step);
     if (step + 1 < kSteps) {
-      vf[(step + 1) & 1] = lds_load16(sV + voff(step + 1));
-      if constexpr (M::kKV) dvf[(step + 1) & 1] = lds_load16(sdV + voff(step + 1));
+      vf[(step + 1) & 1] = lds_load16(vbase + voff(step + 1));
+      if constexpr (M::kKV) dvf[(step + 1) & 1] = lds_load16(dvbase + voff(step + 1));
     }
     st.accA[cb] = mma_f16(vf[step & 1], p[t], st.accA[cb]);
     st.accG[cb] = mma_f16(vf[step & 1], pd[t], st.accG[cb]);
     if constexpr (M::kKV) st.accG[cb] = mma_f16(dvf[step & 1], p[t], st.accG[cb]);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// One 32-key block (block `kb` of the 64-key tile image in `stage`): both
+// phases back to back.
+template <int D, int kMode, bool kMask, typename Issue>
+__device__ __attribute__((always_inline)) inline void jvp_block(
+    RowState<D>& st, const char* stage, int kb, const u32x4* qf, const u32x4* dqf, int l32,
+    int g, int key0, int Nk, float c_log2, float scale, Issue issue) {
+  using G = Geo<D, Mode<kMode>::kKV>;
+  const int lane16 = 16 * l32 + 512 * g;  // this lane's 16 bytes of a fragment
+  const int kf0 = kb * G::kKS * kDmaBytes, vf0 = 2 * kb * G::kCB * kDmaBytes;
+  f32x16 s, ds;
+  qk_phase<D, kMode>(s, ds, stage + kf0, stage + G::kOffdK + kf0, qf, dqf, lane16, issue);
+  sm_pv_phase<D, kMode, kMask>(st, s, ds, stage + G::kOffV + vf0, stage + G::kOffdV + vf0, lane16,
+                               g, key0, Nk, c_log2, scale, issue);
 }
 
 // One full tile: the copy of the next tile image into `next` is spread over
@@ -341,6 +359,44 @@ __device__ __attribute__((always_inline)) inline void store4(__amdgpu_buffer_rsr
     buf_store8(r, elem * 2, __builtin_bit_cast(u32x2, h));
   } else {
     buf_store16(r, elem * 4, __builtin_bit_cast(u32x4, x));
+  }
+}
+
+// Epilogue of one wave: O = A / l, mu = u / l, dO = G / l - mu O, lse and
+// tlse = mu for this lane's query row of output slice obh (rows past Nq are
+// not stored).
+template <int D, bool kOutBf16>
+__device__ __attribute__((always_inline)) inline void jvp_epilogue(
+    const RowState<D>& st, uint32_t obh, int row, int Nq, int g, void* o, void* to, float* lse,
+    float* tlse, const Extents& ext) {
+  const float l = halves_sum(st.l);
+  const float inv_l = 1.0f / l;
+  const float mu = halves_sum(st.u) * inv_l;
+  if (row < Nq) {
+    const uint32_t orow = (obh * (uint32_t)Nq + row) * D;  // first element of the row
+    const auto ro = make_rsrc(o, ext.o_bytes);
+    const auto rto = make_rsrc(to, ext.o_bytes);
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int c0 = 32 * cb + 8 * qq + 4 * g;
+        f32x4 ov, tv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = st.accA[cb][4 * qq + e] * inv_l;
+          ov[e] = a;
+          tv[e] = st.accG[cb][4 * qq + e] * inv_l - mu * a;
+        }
+        store4<kOutBf16>(ro, orow + c0, ov);
+        store4<kOutBf16>(rto, orow + c0, tv);
+      }
+    if (g == 0) {
+      const uint32_t off = (obh * (uint32_t)Nq + row) * 4;
+      if (lse != nullptr)
+        buf_store4(make_rsrc(lse, ext.lse_bytes), off, (st.m + __log2f(l)) * kLn2);
+      if (tlse != nullptr) buf_store4(make_rsrc(tlse, ext.lse_bytes), off, mu);
+    }
   }
 }
 
@@ -449,36 +505,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
     jvp_block<D, kMode, true>(st, cur, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, scale, none);
   }
 
-  // ---- epilogue: O = A / l, mu = u / l, dO = G / l - mu O, lse, tlse = mu ----
-  const float l = halves_sum(st.l);
-  const float inv_l = 1.0f / l;
-  const float mu = halves_sum(st.u) * inv_l;
-  if (row_ok) {
-    const uint32_t orow = (obh * (uint32_t)Nq + row) * D;  // first element of the row
-    const auto ro = make_rsrc(o, ext.o_bytes);
-    const auto rto = make_rsrc(to, ext.o_bytes);
-#pragma unroll
-    for (int cb = 0; cb < G::kCB; ++cb)
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int c0 = 32 * cb + 8 * qq + 4 * g;
-        f32x4 ov, tv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a = st.accA[cb][4 * qq + e] * inv_l;
-          ov[e] = a;
-          tv[e] = st.accG[cb][4 * qq + e] * inv_l - mu * a;
-        }
-        store4<kOutBf16>(ro, orow + c0, ov);
-        store4<kOutBf16>(rto, orow + c0, tv);
-      }
-    if (g == 0) {
-      const uint32_t off = (obh * (uint32_t)Nq + row) * 4;
-      if (lse != nullptr)
-        buf_store4(make_rsrc(lse, ext.lse_bytes), off, (st.m + __log2f(l)) * kLn2);
-      if (tlse != nullptr) buf_store4(make_rsrc(tlse, ext.lse_bytes), off, mu);
-    }
-  }
+  jvp_epilogue<D, kOutBf16>(st, obh, row, Nq, g, o, to, lse, tlse, ext);
 }
 
 // ---- forward attention alone (O, lse) ----
