@@ -125,3 +125,21 @@ def test_more_row_tiles_than_resident_workgroups(Nk):
     check(f"items frozen tlse Nk={Nk}", (fro[3],), (ref_f[3],), fp32=False)
     ref = oracle.attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], s)
     check(f"items bf16-out Nk={Nk}", b16[:3], ref, fp32=False)
+
+
+def test_many_small_slices():
+    """320 (b, h) slices of 100 query rows and 70 keys: a grid of one row tile
+    per slice, more workgroups than CUs, against the oracle."""
+    x = _rand(8, 40, 100, 70, 128, torch.bfloat16, seed=11)
+    _cmp("B=8 H=40 Nq=100 Nk=70", x, 1.0 / math.sqrt(128))
+
+
+def test_long_key_sequence():
+    """131072 keys (2048 tile images, 128 MiB for the slice) against 300 query
+    rows: offsets deep into the workspace slice, checked against the oracle on
+    sampled rows."""
+    from _gpu import check_sampled
+    x = _rand(1, 1, 300, 131072, 128, torch.bfloat16, seed=12)
+    s = 1.0 / math.sqrt(128)
+    outs = run(to_device(x), s)
+    check_sampled("Nq=300 Nk=131072", x, s, outs, rows_per_head=12, extra_rows=(0, 299))
