@@ -41,7 +41,9 @@
 //           6 contractions remain).
 // The forward pass alone (O, lse: 2 contractions) has a kernel of its own
 // (attn_fwd_bf16_kernel, 64 rows per wave).  Outputs O and dO are written in
-// fp32 or bf16 (round to nearest even).
+// fp32 or bf16 (round to nearest even).  Both kernels can also run a range of
+// key tiles per work item and write partial states (split-KV for few query
+// rows), which the merge kernel of attn_jvp_merge.hip combines.
 #include <cmath>
 
 #include "cdna4.hpp"
