@@ -5,8 +5,8 @@
 // in fp32 end to end: it is the precision reference the pages motivate (the
 // record's second takeaway: BF16 JVP error is much larger than BF16 output
 // error, Fig. 11).  Structure: one workgroup = 4 waves x 32 query rows; 32-key
-// tiles of K, dK, V, dV staged in LDS through registers (double buffered,
-// loads one tile ahead); fp32 MFMA 32x32x2 for S^T = K Q^T, dS^T = dK Q^T + K dQ^T,
+// tiles of K, dK, V, dV copied straight into LDS (double buffered, one tile
+// ahead); fp32 MFMA 32x32x2 for S^T = K Q^T, dS^T = dK Q^T + K dQ^T,
 // A^T += V^T P^T and G^T += V^T (s P dS)^T + dV^T P^T; online softmax per lane.
 #include "cdna4.hpp"
 #include "launch.hpp"
@@ -145,6 +145,19 @@ __device__ __attribute__((always_inline)) inline void jvp_tile_f32(
   }
 }
 
+// One tile: the copy of the next tile into `next` is issued first, then the
+// tile in `cur` is computed.  The stage pointers are restrict-qualified
+// (disjoint halves of the LDS), so the compiler does not make the LDS reads
+// of `cur` wait for the copy into `next`.
+template <int D, typename Copy>
+__device__ __attribute__((always_inline)) inline void f32_tile_step(
+    char* __restrict__ next, const char* __restrict__ cur, Copy copy, RowStateF<D>& st,
+    const f32x4* qf, const f32x4* dqf, int l32, int g, int key0, int Nk, float c_log2,
+    float scale) {
+  copy(next);
+  jvp_tile_f32<D, false>(st, cur, qf, dqf, l32, g, key0, Nk, c_log2, scale);
+}
+
 // Sizes of the whole tensors (bytes); every global access is checked against
 // them by its buffer descriptor.
 struct ExtentsF {
@@ -180,39 +193,27 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_f32_body(
     dqf[j] = __builtin_bit_cast(f32x4, buf_load16(rtq, off));
   }
 
-  // Staging through registers: each thread loads kChunks 16-byte chunks of the
-  // four 32-key tiles one tile ahead of the compute (key rows past Nk are set
-  // to zero) and writes them, XOR-swizzled, to the other LDS buffer at the end
-  // of the iteration.
-  constexpr int kChunks = G::kStageBytes / 16 / kThreads;
-  constexpr int kChunksPerTensor = kChunks / 4;
-  const __amdgpu_buffer_rsrc_t rsrc[4] = {make_rsrc(k, ext.k_bytes), make_rsrc(tk, ext.k_bytes),
-                                          make_rsrc(v, ext.k_bytes), make_rsrc(tv, ext.k_bytes)};
+  // Direct-to-LDS copies of the next 32-key tile (no staging registers): wave
+  // w copies tensor w (K, dK, V, dV), kChunks 1 KiB loads, load n writing
+  // the stage's 16-byte chunks 64 n + lane of that tensor.  The XOR swizzle
+  // is applied on the global side: LDS chunk c holds row r = c / kRowChunks,
+  // column chunk (c % kRowChunks) ^ (r & 7).  Rows past Nk get an offset past
+  // the tensor, which the descriptor reads as zeros.
+  constexpr int kChunks = G::kTileBytes / 16 / 64;  // loads per wave and tile
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  const float* const srcs[4] = {k, tk, v, tv};
+  const auto rsrc = make_rsrc(srcs[wave], ext.k_bytes);
   const uint32_t kslice = bh * (uint32_t)Nk * D * 4;
-  uint32_t g_off[kChunks], l_off[kChunks];
-  int c_row[kChunks];
-#pragma unroll
-  for (int n = 0; n < kChunks; ++n) {
-    const int c = (tid + kThreads * n) % (kBC * G::kRowChunks);
-    const int r = c / G::kRowChunks, ch = c % G::kRowChunks;
-    c_row[n] = r;
-    g_off[n] = (uint32_t)(r * D * 4 + ch * 16);
-    l_off[n] = (uint32_t)((n / kChunksPerTensor) * G::kTileBytes + swz<D>(r, ch));
-  }
-  u32x4 stg[kChunks];
-  auto load_stage = [&](int kt) {
-    const uint32_t base = kslice + (uint32_t)kt * kBC * D * 4;
+  auto copy_tile = [&](char* stage, int kt) {
 #pragma unroll
     for (int n = 0; n < kChunks; ++n) {
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      const u32x4 x = buf_load16(rsrc[n / kChunksPerTensor], base + g_off[n]);
-      stg[n] = (kt * kBC + c_row[n] < Nk) ? x : zero;
+      const int c = 64 * n + lane, r = c / G::kRowChunks, pos = c % G::kRowChunks;
+      const int key = kt * kBC + r;
+      const uint32_t off = key < Nk ? kslice + (uint32_t)(key * D * 4 + ((pos ^ (r & 7)) << 4))
+                                    : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (lds_ptr_t)(stage + wave * G::kTileBytes + n * 1024), 16, off, 0, 0, 0);
     }
-  };
-  auto store_stage = [&](int buf) {
-    char* sb = smem + buf * G::kStageBytes;
-#pragma unroll
-    for (int n = 0; n < kChunks; ++n) lds_store16(sb + l_off[n], stg[n]);
   };
 
   RowStateF<D> st;
@@ -225,14 +226,14 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_f32_body(
   st.l = 0.f;
   st.u = 0.f;
 
-  load_stage(0);
-  store_stage(0);
+  copy_tile(smem, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < ntiles - 1; ++kt) {
-    load_stage(kt + 1);
-    jvp_tile_f32<D, false>(st, smem + (kt & 1) * G::kStageBytes, qf, dqf, l32, g, kt * kBC, Nk,
-                           c_log2, scale);
-    store_stage((kt + 1) & 1);
+    f32_tile_step<D>(smem + ((kt + 1) & 1) * G::kStageBytes, smem + (kt & 1) * G::kStageBytes,
+                     [&](char* next) { copy_tile(next, kt + 1); }, st, qf, dqf, l32, g,
+                     kt * kBC, Nk, c_log2, scale);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   {
