@@ -9,33 +9,81 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "launch.hpp"
 
 namespace {
 
-// Every tensor is addressed with 32-bit byte offsets from its base (buffer
-// descriptors spanning the whole tensor), and B*H is the grid's y extent.
+// Every kernel addresses a tensor with 32-bit byte offsets from its base
+// (buffer descriptors), so one launch's tensors stay under 2^31 bytes.  A call
+// over more runs as consecutive launches over groups of whole (b, h) slices:
+// the layout [B, H, N, d] keeps a group contiguous, and every slice is
+// independent.  A group also holds at most 65535 slices (the pack kernels'
+// grid y extent).  What stays bounded is one slice: Nq*d*4 and Nk*d*4 bytes
+// (fp32 outputs, fp32 inputs) under 2^31.
 constexpr int64_t kMaxTensorBytes = int64_t(1) << 31;
-constexpr int64_t kMaxSlices = 65535;
+constexpr int64_t kMaxGroupSlices = 65535;
+constexpr int64_t kMaxSlices = INT32_MAX;
 constexpr int kMaxMergeParts = 1024;
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
-// Sizes shared by every entry point: counts >= 1, d in {64, 128}, every
-// tensor under 2^31 bytes, and one (b, h) slice of the bf16 path's tile-image
-// workspace under 2^31 bytes (the kernels address it per slice).
-// Grid: (ceil(Nq/256), B*H) workgroups; pack: (ceil(Nk/64), B*H).  esize is
-// the input element size.
+// Bytes of one (b, h) slice of each kind of tensor, and the slices per launch.
+struct Slices {
+  int64_t bh = 0, g = 0;  // slices in all, slices per launch (group)
+  int64_t q = 0;          // Q-side input (q, tq, go): Nq*d*esize
+  int64_t k = 0;          // K-side input (k, v, tk, tv): Nk*d*esize
+  int64_t o = 0;          // Q-side fp32 output (o, to, gq): Nq*d*4
+  int64_t ko = 0;         // K-side fp32 output (gk, gv): Nk*d*4
+  int64_t r = 0;          // row scalars (lse, tlse): Nq*4
+  int64_t img = 0;        // the bf16 path's tile images (workspace)
+};
+
+Slices slices(int B, int H, int Nq, int Nk, int d, int esize) {
+  Slices s;
+  s.bh = int64_t(B) * H;
+  s.q = int64_t(Nq) * d * esize;
+  s.k = int64_t(Nk) * d * esize;
+  s.o = int64_t(Nq) * d * 4;
+  s.ko = int64_t(Nk) * d * 4;
+  s.r = int64_t(Nq) * 4;
+  s.img = int64_t(ajvp::bf16_workspace_bytes(1, 1, Nk, d));
+  const int64_t widest = s.o > s.ko ? s.o : s.ko;
+  s.g = (kMaxTensorBytes - 1) / widest;
+  if (s.g > kMaxGroupSlices) s.g = kMaxGroupSlices;
+  if (s.g > s.bh) s.g = s.bh;
+  return s;
+}
+
+// Runs f(s0, n) over the groups [s0, s0 + n) of s.g slices; stops at the
+// first failure.
+template <typename F>
+hipError_t each_group(const Slices& s, F f) {
+  for (int64_t s0 = 0; s0 < s.bh; s0 += s.g) {
+    const hipError_t e = f(s0, static_cast<int>(s.bh - s0 < s.g ? s.bh - s0 : s.g));
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// p advanced by `bytes`; NULL stays NULL (absent tangents and outputs).
+template <typename T>
+T* shift(T* p, int64_t bytes) {
+  using C = std::conditional_t<std::is_const_v<T>, const char, char>;
+  return p == nullptr ? nullptr : (T*)((C*)p + bytes);
+}
+
+// Sizes shared by every entry point: counts >= 1, d in {64, 128}, one slice
+// of every tensor (inputs of esize bytes, fp32 outputs, the bf16 path's tile
+// images) under 2^31 bytes, and B*H at most 2^31 - 1.
 int check_sizes(int B, int H, int Nq, int Nk, int d, int esize) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_JVP_EINVAL;
   if (d != 64 && d != 128) return ATTN_JVP_EUNSUPPORTED;
-  const int64_t bh = int64_t(B) * H;
-  if (bh > kMaxSlices) return ATTN_JVP_EUNSUPPORTED;
-  const int64_t qb = bh * Nq * d * esize, kb = bh * Nk * d * esize, ob = bh * Nq * d * 4;
-  const int64_t wsb = int64_t(ajvp::bf16_workspace_bytes(1, 1, Nk, d));  // one slice
-  if (qb >= kMaxTensorBytes || kb >= kMaxTensorBytes || ob >= kMaxTensorBytes ||
-      wsb >= kMaxTensorBytes)
+  const Slices s = slices(B, H, Nq, Nk, d, esize);
+  if (s.bh > kMaxSlices) return ATTN_JVP_EUNSUPPORTED;
+  if (s.q >= kMaxTensorBytes || s.k >= kMaxTensorBytes || s.o >= kMaxTensorBytes ||
+      s.ko >= kMaxTensorBytes || s.img >= kMaxTensorBytes)
     return ATTN_JVP_EUNSUPPORTED;
   return ATTN_JVP_OK;
 }
@@ -122,6 +170,23 @@ int with_workspace(void* workspace, size_t workspace_bytes, int B, int H, int Nk
                           launch);
 }
 
+// Split-KV and the backward pass: each group reuses the workspace from its start (images of the
+// group, then its partial states, or its backward tile images and partial sums), so
+// it holds the larger of the two group sizes' needs.
+size_t splitkv_need(const Slices& s, int Nq, int Nk, int d, int nsplit) {
+  const int64_t last = s.bh - (s.bh - 1) / s.g * s.g;
+  const size_t a = ajvp::splitkv_workspace_bytes(1, int(s.g), Nq, Nk, d, nsplit);
+  const size_t b = ajvp::splitkv_workspace_bytes(1, int(last), Nq, Nk, d, nsplit);
+  return a > b ? a : b;
+}
+
+size_t bwd_need(const Slices& s, int Nq, int Nk, int d) {
+  const int64_t last = s.bh - (s.bh - 1) / s.g * s.g;
+  const size_t a = ajvp::bwd_workspace_bytes(1, int(s.g), Nq, Nk, d);
+  const size_t b = ajvp::bwd_workspace_bytes(1, int(last), Nq, Nk, d);
+  return a > b ? a : b;
+}
+
 bool bad_out_dtype(int t) { return t != ATTN_JVP_OUT_F32 && t != ATTN_JVP_OUT_BF16; }
 
 }  // namespace
@@ -132,7 +197,7 @@ const char* attn_jvp_strerror(int status) {
   switch (status) {
     case ATTN_JVP_OK: return "ok";
     case ATTN_JVP_EINVAL: return "invalid argument (null pointer, size < 1, bad scale or workspace, or size overflow)";
-    case ATTN_JVP_EUNSUPPORTED: return "unsupported (head dim must be 64 or 128, B*H at most 65535, each tensor under 2^31 bytes)";
+    case ATTN_JVP_EUNSUPPORTED: return "unsupported (head dim must be 64 or 128; one (b, h) slice of each tensor under 2^31 bytes)";
     case ATTN_JVP_EALIGN: return "misaligned pointer (tensors need 16-byte, workspace 256-byte alignment)";
     case ATTN_JVP_ELAUNCH: return "HIP launch or allocation failed";
     default: return "unknown status";
@@ -144,6 +209,10 @@ size_t attn_jvp_workspace_bytes(int B, int H, int Nk, int d) {
   return ajvp::bf16_workspace_bytes(B, H, Nk, d);
 }
 
+// The bf16 entry points below run each group of slices with the caller's
+// pointers advanced to the group's first slice; the tile-image workspace keeps
+// one region per slice, so a group's images sit at s0 * (one slice's bytes).
+
 int attn_jvp_fwd_ws(const void* q, const void* k, const void* v, const void* tq, const void* tk,
                     const void* tv, float* o, float* to, float* lse, int B, int H, int Nq, int Nk,
                     int d, float scale, void* workspace, size_t workspace_bytes,
@@ -153,8 +222,14 @@ int attn_jvp_fwd_ws(const void* q, const void* k, const void* v, const void* tq,
   if (rc != ATTN_JVP_OK) return rc;
   rc = check_workspace(workspace, workspace_bytes, B, H, Nk, d);
   if (rc != ATTN_JVP_OK) return rc;
-  hipError_t e = ajvp::launch_bf16(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, d, scale,
-                                   workspace, reinterpret_cast<hipStream_t>(stream));
+  const Slices s = slices(B, H, Nq, Nk, d, 2);
+  const hipError_t e = each_group(s, [&](int64_t s0, int n) {
+    return ajvp::launch_bf16(shift(q, s0 * s.q), shift(k, s0 * s.k), shift(v, s0 * s.k),
+                             shift(tq, s0 * s.q), shift(tk, s0 * s.k), shift(tv, s0 * s.k),
+                             shift(o, s0 * s.o), shift(to, s0 * s.o), shift(lse, s0 * s.r), 1, n,
+                             Nq, Nk, d, scale, shift(workspace, s0 * s.img),
+                             reinterpret_cast<hipStream_t>(stream));
+  });
   return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
 }
 
@@ -168,8 +243,12 @@ int attn_jvp_pack_kv(const void* k, const void* v, const void* tk, const void* t
   if (rc != ATTN_JVP_OK) return rc;
   if (misaligned(k, 16) || misaligned(v, 16) || misaligned(tk, 16) || misaligned(tv, 16))
     return ATTN_JVP_EALIGN;
-  hipError_t e = ajvp::launch_pack_kv(k, v, tk, tv, B, H, Nk, d, workspace,
-                                      reinterpret_cast<hipStream_t>(stream));
+  const Slices s = slices(B, H, 1, Nk, d, 2);
+  const hipError_t e = each_group(s, [&](int64_t s0, int n) {
+    return ajvp::launch_pack_kv(shift(k, s0 * s.k), shift(v, s0 * s.k), shift(tk, s0 * s.k),
+                                shift(tv, s0 * s.k), 1, n, Nk, d, shift(workspace, s0 * s.img),
+                                reinterpret_cast<hipStream_t>(stream));
+  });
   return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
 }
 
@@ -181,8 +260,13 @@ int attn_jvp_fwd_packed(const void* q, const void* tq, const void* workspace,
   if (rc != ATTN_JVP_OK) return rc;
   rc = check_workspace(workspace, workspace_bytes, B, H, Nk, d);
   if (rc != ATTN_JVP_OK) return rc;
-  hipError_t e = ajvp::launch_bf16_packed(q, tq, workspace, o, to, lse, B, H, Nq, Nk, d, scale,
-                                          reinterpret_cast<hipStream_t>(stream));
+  const Slices s = slices(B, H, Nq, Nk, d, 2);
+  const hipError_t e = each_group(s, [&](int64_t s0, int n) {
+    return ajvp::launch_bf16_packed(shift(q, s0 * s.q), shift(tq, s0 * s.q),
+                                    shift(workspace, s0 * s.img), shift(o, s0 * s.o),
+                                    shift(to, s0 * s.o), shift(lse, s0 * s.r), 1, n, Nq, Nk, d,
+                                    scale, reinterpret_cast<hipStream_t>(stream));
+  });
   return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
 }
 
@@ -193,14 +277,16 @@ int attn_jvp_fwd(const void* q, const void* k, const void* v, const void* tq, co
   int rc = validate(in, 6, o, to, lse, B, H, Nq, Nk, d, scale, 2);
   if (rc != ATTN_JVP_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipMemPool_t pool = nullptr;
-  if (device_pool(&pool) != hipSuccess) return ATTN_JVP_ELAUNCH;
-  const size_t bytes = ajvp::bf16_workspace_bytes(B, H, Nk, d);
-  void* ws = nullptr;
-  if (hipMallocFromPoolAsync(&ws, bytes, pool, st) != hipSuccess) return ATTN_JVP_ELAUNCH;
-  hipError_t e = ajvp::launch_bf16(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, d, scale, ws, st);
-  hipError_t f = hipFreeAsync(ws, st);
-  return (e == hipSuccess && f == hipSuccess) ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+  const Slices s = slices(B, H, Nq, Nk, d, 2);
+  // one group's images, reused by the next group in stream order
+  return with_workspace_n(nullptr, 0, size_t(s.g * s.img), st, [&](void* ws) {
+    return each_group(s, [&](int64_t s0, int n) {
+      return ajvp::launch_bf16(shift(q, s0 * s.q), shift(k, s0 * s.k), shift(v, s0 * s.k),
+                               shift(tq, s0 * s.q), shift(tk, s0 * s.k), shift(tv, s0 * s.k),
+                               shift(o, s0 * s.o), shift(to, s0 * s.o), shift(lse, s0 * s.r), 1,
+                               n, Nq, Nk, d, scale, ws, st);
+    });
+  });
 }
 
 int attn_jvp_fwd_ex(const void* q, const void* k, const void* v, const void* tq, const void* tk,
@@ -217,15 +303,23 @@ int attn_jvp_fwd_ex(const void* q, const void* k, const void* v, const void* tq,
     if (t != nullptr && misaligned(t, 16)) return ATTN_JVP_EALIGN;
   if (tlse != nullptr && misaligned(tlse, 4)) return ATTN_JVP_EALIGN;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool bf16 = out_dtype == ATTN_JVP_OUT_BF16;
+  const Slices s = slices(B, H, Nq, Nk, d, 2);
+  const int64_t os = bf16 ? s.o / 2 : s.o;
   return with_workspace(workspace, workspace_bytes, B, H, Nk, d, st, [&](void* ws) {
-    return ajvp::launch_bf16_ex(q, k, v, tq, tk, tv, o, to, lse, tlse, B, H, Nq, Nk, d, scale,
-                                out_dtype == ATTN_JVP_OUT_BF16, ws, st);
+    return each_group(s, [&](int64_t s0, int n) {
+      return ajvp::launch_bf16_ex(shift(q, s0 * s.q), shift(k, s0 * s.k), shift(v, s0 * s.k),
+                                  shift(tq, s0 * s.q), shift(tk, s0 * s.k), shift(tv, s0 * s.k),
+                                  shift(o, s0 * os), shift(to, s0 * os), shift(lse, s0 * s.r),
+                                  shift(tlse, s0 * s.r), 1, n, Nq, Nk, d, scale, bf16,
+                                  shift(ws, s0 * s.img), st);
+    });
   });
 }
 
 size_t attn_jvp_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int nsplit) {
-  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128) || nsplit < 0) return 0;
-  return ajvp::splitkv_workspace_bytes(B, H, Nq, Nk, d, nsplit);
+  if (nsplit < 0 || check_sizes(B, H, Nq, Nk, d, 2) != ATTN_JVP_OK) return 0;
+  return splitkv_need(slices(B, H, Nq, Nk, d, 2), Nq, Nk, d, nsplit);
 }
 
 int attn_jvp_fwd_splitkv(const void* q, const void* k, const void* v, const void* tq,
@@ -242,10 +336,17 @@ int attn_jvp_fwd_splitkv(const void* q, const void* k, const void* v, const void
     if (t != nullptr && misaligned(t, 16)) return ATTN_JVP_EALIGN;
   if (tlse != nullptr && misaligned(tlse, 4)) return ATTN_JVP_EALIGN;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const size_t need = ajvp::splitkv_workspace_bytes(B, H, Nq, Nk, d, nsplit);
-  return with_workspace_n(workspace, workspace_bytes, need, st, [&](void* ws) {
-    return ajvp::launch_bf16_splitkv(q, k, v, tq, tk, tv, o, to, lse, tlse, B, H, Nq, Nk, d,
-                                     scale, nsplit, ws, st);
+  const Slices s = slices(B, H, Nq, Nk, d, 2);
+  return with_workspace_n(workspace, workspace_bytes, splitkv_need(s, Nq, Nk, d, nsplit), st,
+                          [&](void* ws) {
+    return each_group(s, [&](int64_t s0, int n) {
+      return ajvp::launch_bf16_splitkv(shift(q, s0 * s.q), shift(k, s0 * s.k),
+                                       shift(v, s0 * s.k), shift(tq, s0 * s.q),
+                                       shift(tk, s0 * s.k), shift(tv, s0 * s.k),
+                                       shift(o, s0 * s.o), shift(to, s0 * s.o),
+                                       shift(lse, s0 * s.r), shift(tlse, s0 * s.r), 1, n, Nq, Nk,
+                                       d, scale, nsplit, ws, st);
+    });
   });
 }
 
@@ -259,9 +360,14 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, float* o, floa
   if (rc != ATTN_JVP_OK) return rc;
   if (nsplit < 0) return ATTN_JVP_EINVAL;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const size_t need = ajvp::splitkv_workspace_bytes(B, H, Nq, Nk, d, nsplit);
-  return with_workspace_n(workspace, workspace_bytes, need, st, [&](void* ws) {
-    return ajvp::launch_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, nsplit, ws, st);
+  const Slices s = slices(B, H, Nq, Nk, d, 2);
+  return with_workspace_n(workspace, workspace_bytes, splitkv_need(s, Nq, Nk, d, nsplit), st,
+                          [&](void* ws) {
+    return each_group(s, [&](int64_t s0, int n) {
+      return ajvp::launch_fwd_splitkv(shift(q, s0 * s.q), shift(k, s0 * s.k), shift(v, s0 * s.k),
+                                      shift(o, s0 * s.o), shift(lse, s0 * s.r), 1, n, Nq, Nk, d,
+                                      scale, nsplit, ws, st);
+    });
   });
 }
 
@@ -276,9 +382,15 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (rc != ATTN_JVP_OK) return rc;
   if (bad_out_dtype(out_dtype)) return ATTN_JVP_EINVAL;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool bf16 = out_dtype == ATTN_JVP_OUT_BF16;
+  const Slices s = slices(B, H, Nq, Nk, d, 2);
+  const int64_t os = bf16 ? s.o / 2 : s.o;
   return with_workspace(workspace, workspace_bytes, B, H, Nk, d, st, [&](void* ws) {
-    return ajvp::launch_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale,
-                            out_dtype == ATTN_JVP_OUT_BF16, ws, st);
+    return each_group(s, [&](int64_t s0, int n) {
+      return ajvp::launch_fwd(shift(q, s0 * s.q), shift(k, s0 * s.k), shift(v, s0 * s.k),
+                              shift(o, s0 * os), shift(lse, s0 * s.r), 1, n, Nq, Nk, d, scale,
+                              bf16, shift(ws, s0 * s.img), st);
+    });
   });
 }
 
@@ -305,8 +417,8 @@ int attn_jvp_merge(const float* lse_parts, const float* o_parts, const float* to
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
-  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128)) return 0;
-  return ajvp::bwd_workspace_bytes(B, H, Nq, Nk, d);
+  if (check_sizes(B, H, Nq, Nk, d, 2) != ATTN_JVP_OK) return 0;
+  return bwd_need(slices(B, H, Nq, Nk, d, 2), Nq, Nk, d);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const float* o, const void* go,
@@ -319,31 +431,24 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || bad_scale(scale)) return ATTN_JVP_EINVAL;
   int rc = check_sizes(B, H, Nq, Nk, d, 2);
   if (rc != ATTN_JVP_OK) return rc;
-  // one (b, h) slice of each half of the workspace stays under 2^31 bytes
-  if (int64_t(ajvp::bwd_workspace_bytes(1, 1, Nq, Nk, d)) >= kMaxTensorBytes ||
-      int64_t(B) * H * Nk * d * 4 >= kMaxTensorBytes)
+  // the kernels address one (b, h) slice of the workspace's tile images at a time
+  if (int64_t(ajvp::bwd_workspace_bytes(1, 1, Nq, Nk, d)) >= kMaxTensorBytes)
     return ATTN_JVP_EUNSUPPORTED;
   const void* al16[8] = {q, k, v, o, go, gq, gk, gv};
   for (const void* p : al16)
     if (misaligned(p, 16)) return ATTN_JVP_EALIGN;
   if (misaligned(lse, 4)) return ATTN_JVP_EALIGN;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const size_t need_ws = ajvp::bwd_workspace_bytes(B, H, Nq, Nk, d);
-  auto launch = [&](void* ws) {
-    return ajvp::launch_bwd(q, k, v, o, go, lse, gq, gk, gv, B, H, Nq, Nk, d, scale, ws, st);
-  };
-  if (workspace != nullptr) {
-    if (workspace_bytes < need_ws) return ATTN_JVP_EINVAL;
-    if (misaligned(workspace, 256)) return ATTN_JVP_EALIGN;
-    return launch(workspace) == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
-  }
-  hipMemPool_t pool = nullptr;
-  if (device_pool(&pool) != hipSuccess) return ATTN_JVP_ELAUNCH;
-  void* ws = nullptr;
-  if (hipMallocFromPoolAsync(&ws, need_ws, pool, st) != hipSuccess) return ATTN_JVP_ELAUNCH;
-  const hipError_t e = launch(ws);
-  const hipError_t f = hipFreeAsync(ws, st);
-  return (e == hipSuccess && f == hipSuccess) ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+  const Slices s = slices(B, H, Nq, Nk, d, 2);
+  return with_workspace_n(workspace, workspace_bytes, bwd_need(s, Nq, Nk, d), st,
+                          [&](void* ws) {
+    return each_group(s, [&](int64_t s0, int n) {
+      return ajvp::launch_bwd(shift(q, s0 * s.q), shift(k, s0 * s.k), shift(v, s0 * s.k),
+                              shift(o, s0 * s.o), shift(go, s0 * s.q), shift(lse, s0 * s.r),
+                              shift(gq, s0 * s.o), shift(gk, s0 * s.ko), shift(gv, s0 * s.ko), 1,
+                              n, Nq, Nk, d, scale, ws, st);
+    });
+  });
 }
 
 int attn_jvp_fwd_f32(const float* q, const float* k, const float* v, const float* tq,
@@ -352,8 +457,13 @@ int attn_jvp_fwd_f32(const float* q, const float* k, const float* v, const float
   const void* in[6] = {q, k, v, tq, tk, tv};
   int rc = validate(in, 6, o, to, lse, B, H, Nq, Nk, d, scale, 4);
   if (rc != ATTN_JVP_OK) return rc;
-  hipError_t e = ajvp::launch_f32(q, k, v, tq, tk, tv, o, to, lse, B, H, Nq, Nk, d, scale,
-                                  reinterpret_cast<hipStream_t>(stream));
+  const Slices s = slices(B, H, Nq, Nk, d, 4);
+  const hipError_t e = each_group(s, [&](int64_t s0, int n) {
+    return ajvp::launch_f32(shift(q, s0 * s.q), shift(k, s0 * s.k), shift(v, s0 * s.k),
+                            shift(tq, s0 * s.q), shift(tk, s0 * s.k), shift(tv, s0 * s.k),
+                            shift(o, s0 * s.o), shift(to, s0 * s.o), shift(lse, s0 * s.r), 1, n,
+                            Nq, Nk, d, scale, reinterpret_cast<hipStream_t>(stream));
+  });
   return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
 }
 

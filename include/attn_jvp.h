@@ -24,6 +24,13 @@
  * address every tensor through buffer descriptors that span exactly that
  * tensor, so an access outside it reads zero or is dropped.
  *
+ * Sizes.  A descriptor takes 32-bit byte offsets, so one kernel launch covers
+ * at most 2^31 bytes of each tensor.  Whole tensors may be larger: a call
+ * whose tensors pass that runs as consecutive launches on `stream` over
+ * groups of whole (b, h) slices, each group's tensors under 2^31 bytes (every
+ * slice is independent and [B, H, N, d] keeps a group contiguous).  What stays
+ * bounded is one slice of each tensor (see ATTN_JVP_EUNSUPPORTED).
+ *
  * Precision.  attn_jvp_fwd takes bf16 inputs (uint16 storage holding IEEE
  * bfloat16 bit patterns); all products are formed on bf16/fp16 matrix cores
  * with fp32 accumulation, and O, dO and lse are written in fp32.  The second
@@ -47,9 +54,11 @@
  *   ATTN_JVP_EINVAL       a required pointer is NULL; B, H, Nq or Nk < 1;
  *                         `scale` is negative, NaN or infinite; the workspace
  *                         is NULL or too small
- *   ATTN_JVP_EUNSUPPORTED d is not 64 or 128, B*H exceeds 65535, a tensor
- *                         reaches 2^31 bytes, or one (b, h) slice of the bf16
- *                         path's workspace does (Nk beyond about 1.9 million)
+ *   ATTN_JVP_EUNSUPPORTED d is not 64 or 128; one (b, h) slice of a tensor
+ *                         reaches 2^31 bytes (counted as fp32: Nq*d*4 or
+ *                         Nk*d*4), or one slice of the bf16 path's tile images
+ *                         does (Nk beyond about 2 million at d = 128); B*H
+ *                         exceeds 2^31 - 1
  *   ATTN_JVP_EALIGN       a tensor pointer is not 16-byte aligned (workspace:
  *                         256-byte aligned)
  *   ATTN_JVP_ELAUNCH      the HIP runtime rejected a launch or an allocation
@@ -210,7 +219,10 @@ ATTN_JVP_API int attn_jvp_fwd_splitkv(const void *q, const void *k, const void *
                          attn_jvp_stream_t stream);
 
 /* Workspace bytes of attn_jvp_fwd_splitkv (tile images, then the partial
- * states when more than one range is used); 0 if a size is invalid. */
+ * states when more than one range is used); 0 if a size is invalid.  The
+ * range count is chosen per group of slices (a group whose partial O would
+ * pass 2^31 bytes uses fewer ranges), and the groups of a call past 2^31
+ * bytes per tensor reuse the workspace: it holds the larger group's need. */
 ATTN_JVP_API size_t attn_jvp_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d,
                                                      int nsplit);
 
@@ -278,8 +290,10 @@ ATTN_JVP_API int attn_jvp_merge(const float *lse_parts, const float *o_parts,
  * bf16 products with fp32 accumulation; P and the softmax gradient gS are
  * rounded to fp16 for the products with gO^T, Q^T and K^T.  Errors as
  * attn_jvp_fwd (EINVAL: a NULL pointer, sizes < 1, bad scale, short
- * workspace; EUNSUPPORTED: d, B*H, or a tensor / workspace slice of 2^31
- * bytes; EALIGN: 16-byte tensors, 4-byte lse, 256-byte workspace).
+ * workspace; EUNSUPPORTED: d, B*H, or one (b, h) slice of a tensor or of the
+ * workspace's tile images reaching 2^31 bytes; EALIGN: 16-byte tensors, 4-byte
+ * lse, 256-byte workspace).  Calls past 2^31 bytes per tensor run in groups of
+ * slices that reuse the workspace in stream order, as for split-KV.
  */
 ATTN_JVP_API int attn_bwd(const void *q, const void *k, const void *v,
              const float *o, const void *go, const float *lse,

@@ -116,18 +116,23 @@ def test_unsupported_head_dim(fn):
 
 @pytest.mark.parametrize("fn", FNS)
 def test_oversized_slice(fn):
-    # K (one slice) past 2^31 bytes: outside what 32-bit buffer offsets reach
+    # one slice of K past 2^31 bytes: outside what 32-bit buffer offsets reach
     assert _call(fn, Nk=1 << 24) == EUNSUPPORTED
-    # Q and O past 2^31 bytes over many slices of modest size
-    assert _call(fn, B=64, H=64, Nq=4096) == EUNSUPPORTED
-    # more (b, h) slices than the grid's y extent holds
-    assert _call(fn, B=256, H=256, Nq=1, Nk=1) == EUNSUPPORTED
+    # one slice of the fp32 outputs at 2^31 bytes (Nq d 4)
+    assert _call(fn, Nq=1 << 22) == EUNSUPPORTED
+    assert _call(fn, Nq=1 << 23, d=64) == EUNSUPPORTED
+    # more (b, h) slices than 2^31 - 1
     assert _call(fn, B=1 << 16, H=1 << 16, Nq=256) == EUNSUPPORTED
-    # the largest slice count passes the size checks (and then stops at the
-    # misaligned pointer, so nothing is launched)
+    # tensors past 2^31 bytes over many slices of modest size, and more slices
+    # than one launch takes (65535), pass the size checks: such calls run as
+    # launches over groups of slices.  They stop here at the misaligned
+    # pointer, so nothing is launched.
     p = [A + j * 0x100000 for j in range(9)]
     p[0] += 4
-    assert _call(fn, p, B=65535, H=1, Nq=1, Nk=1) == EALIGN
+    assert _call(fn, p, B=64, H=64, Nq=4096) == EALIGN
+    assert _call(fn, p, B=256, H=256, Nq=1, Nk=1) == EALIGN
+    assert _call(fn, p, B=(1 << 15) - 1, H=1 << 16, Nq=1, Nk=1) == EALIGN
+    assert _call(fn, p, Nq=(1 << 22) - 1) == EALIGN
 
 
 @pytest.mark.parametrize("fn", FNS)
@@ -173,7 +178,7 @@ def test_pack_kv_rejects_bad_arguments():
     assert _pack(ws_bytes=100) == EINVAL
     assert _pack(B=0) == EINVAL and _pack(Nk=0) == EINVAL
     assert _pack(d=96) == EUNSUPPORTED and _pack(Nk=1 << 24) == EUNSUPPORTED
-    assert _pack(B=1 << 16) == EUNSUPPORTED
+    assert _pack(B=1 << 16, H=1 << 16) == EUNSUPPORTED
     assert _pack(k=A + 4) == EALIGN and _pack(v=A + 0x100000 + 8) == EALIGN
     assert _pack(tk=A + 0x200000 + 2) == EALIGN and _pack(tv=A + 0x300000 + 8) == EALIGN
     assert _pack(ws=A + 0x1000000 + 16) == EALIGN
@@ -261,7 +266,7 @@ def test_attn_fwd_rejects_bad_arguments():
         p[i] = 0
         assert _fwd(p) == EINVAL, i
     assert _fwd(out_dtype=3) == EINVAL and _fwd(scale=-1.0) == EINVAL
-    assert _fwd(d=32) == EUNSUPPORTED and _fwd(B=1 << 16) == EUNSUPPORTED
+    assert _fwd(d=32) == EUNSUPPORTED and _fwd(B=1 << 16, H=1 << 16) == EUNSUPPORTED
     p = [A + j * 0x100000 for j in range(5)]
     p[3] += 4
     assert _fwd(p) == EALIGN
@@ -354,6 +359,30 @@ def test_splitkv_workspace_bytes():
     assert auto_count(1, 12, 256, 32760, 128) > 8         # 12 row tiles, 512 key tiles
     assert 1 < auto_count(1, 1, 10, 512, 64) <= 2         # 8 key tiles: ranges of >= 4
     assert ajvp.attn_jvp_splitkv_workspace_bytes(1, 1, 10, 512, 64, -1) == 0
+
+
+def test_grouped_workspace_bytes():
+    """Calls whose tensors pass 2^31 bytes run as launches over groups of whole
+    (b, h) slices (as many as keep one group's fp32 outputs under 2^31 bytes)
+    that reuse one workspace in stream order: the split-KV and backward
+    workspaces hold the larger of the two group sizes' needs, the tile-image
+    workspace keeps one region per slice."""
+    Nq, Nk, d = 32760, 100, 128
+    g = (2**31 - 1) // (Nq * d * 4)
+    assert g == 128
+    split = lambda B, H, n: ajvp.attn_jvp_splitkv_workspace_bytes(B, H, Nq, Nk, d, n)
+    bwd = lambda B, H: ajvp.attn_bwd_workspace_bytes(B, H, Nq, Nk, d)
+    for n in (0, 1, 2):
+        assert split(3, 50, n) == max(split(1, g, n), split(1, 150 - g, n)) > 0, n
+        assert split(1, 2 * g, n) == split(1, g, n), n
+    # two ranges: a 128-slice group's partial O would pass 2^31 bytes, so that
+    # group runs unsplit and the 22-slice group sets the size
+    assert split(1, g, 2) == split(1, g, 1) < split(1, 22, 2) == split(3, 50, 2)
+    assert bwd(3, 50) == max(bwd(1, g), bwd(1, 150 - g)) > 0
+    assert ajvp.attn_jvp_workspace_bytes(3, 50, Nk, d) == 150 * ajvp.attn_jvp_workspace_bytes(1, 1, Nk, d)
+    # one slice too large: no size
+    assert split(1, 1, 0) > 0 and ajvp.attn_jvp_splitkv_workspace_bytes(1, 1, 1 << 22, Nk, d, 0) == 0
+    assert ajvp.attn_bwd_workspace_bytes(1, 1, 1 << 22, Nk, d) == 0
 
 
 def test_fwd_splitkv_rejects_bad_arguments():
