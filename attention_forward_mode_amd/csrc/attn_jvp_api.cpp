@@ -403,17 +403,25 @@ int attn_jvp_merge(const float* lse_parts, const float* o_parts, const float* to
   if (!tan && tlse != nullptr) return ATTN_JVP_EINVAL;
   if (P < 1 || R < 1) return ATTN_JVP_EINVAL;
   if (d != 64 && d != 128) return ATTN_JVP_EUNSUPPORTED;
-  if (P > kMaxMergeParts || int64_t(P) * R * d * 4 >= kMaxTensorBytes)
-    return ATTN_JVP_EUNSUPPORTED;
+  if (P > kMaxMergeParts) return ATTN_JVP_EUNSUPPORTED;
   const void* al16[4] = {o_parts, to_parts, o, to};
   for (const void* p : al16)
     if (p != nullptr && misaligned(p, 16)) return ATTN_JVP_EALIGN;
   const void* al4[4] = {lse_parts, tlse_parts, lse, tlse};
   for (const void* p : al4)
     if (p != nullptr && misaligned(p, 4)) return ATTN_JVP_EALIGN;
-  const hipError_t e = ajvp::launch_merge(lse_parts, o_parts, to_parts, tlse_parts, P, R, d, lse,
-                                          o, to, tlse, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+  // chunks of rows, each under 2^31 bytes of one part's (or the output's) O
+  const int64_t rows = (kMaxTensorBytes - 1) / (int64_t(d) * 4);
+  for (int64_t r0 = 0; r0 < R; r0 += rows) {
+    const int n = static_cast<int>(R - r0 < rows ? R - r0 : rows);
+    const int64_t m = r0 * d;
+    const hipError_t e = ajvp::launch_merge(
+        lse_parts + r0, o_parts + m, shift(to_parts, m * 4), shift(tlse_parts, r0 * 4), P, n, d,
+        shift(lse, r0 * 4), o + m, shift(to, m * 4), shift(tlse, r0 * 4),
+        reinterpret_cast<hipStream_t>(stream), R);
+    if (e != hipSuccess) return ATTN_JVP_ELAUNCH;
+  }
+  return ATTN_JVP_OK;
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d) {

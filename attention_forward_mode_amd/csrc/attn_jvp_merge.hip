@@ -20,19 +20,18 @@ namespace merge_path {
 
 constexpr int kThreads = 256;
 
-// One thread per (row, 4 consecutive columns).  Parts are strided by
-// R (lse, tlse) or R*d (o, to) elements.
+// One thread per (row, 4 consecutive columns) of R rows.  Part p of lse_p,
+// tlse_p starts `stride` rows after part p - 1 (of o_p, to_p, stride * d
+// elements), so a call can cover a chunk of the rows of larger parts; every
+// part gets a descriptor of its own over the chunk's R rows.
 __global__ __launch_bounds__(kThreads) void merge_kernel(
     const float* __restrict__ lse_p, const float* __restrict__ o_p,
     const float* __restrict__ to_p, const float* __restrict__ tlse_p, int P, int R, int d,
-    float* __restrict__ lse, float* __restrict__ o, float* __restrict__ to,
-    float* __restrict__ tlse, uint32_t row_bytes_p, uint32_t mat_bytes_p) {
+    int64_t stride, float* __restrict__ lse, float* __restrict__ o, float* __restrict__ to,
+    float* __restrict__ tlse) {
   const bool tan = to_p != nullptr;
-  const auto rl = make_rsrc(lse_p, row_bytes_p);
-  const auto ro = make_rsrc(o_p, mat_bytes_p);
-  const auto rto = make_rsrc(to_p, tan ? mat_bytes_p : 0u);
-  const auto rtl = make_rsrc(tlse_p, tan ? row_bytes_p : 0u);
   const uint32_t row_bytes = (uint32_t)R * 4, mat_bytes = (uint32_t)R * (uint32_t)d * 4;
+  const int64_t mat_stride = stride * d;
   const auto wl = make_rsrc(lse, row_bytes);
   const auto wo = make_rsrc(o, mat_bytes);
   const auto wto = make_rsrc(to, tan ? mat_bytes : 0u);
@@ -44,30 +43,31 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     const uint32_t row = (uint32_t)(i / chunks), c4 = (uint32_t)(i % chunks);
     float m = -INFINITY;
     for (int p = 0; p < P; ++p)
-      m = fmaxf(m, buf_load4f(rl, ((uint32_t)p * R + row) * 4));
+      m = fmaxf(m, buf_load4f(make_rsrc(lse_p + p * stride, row_bytes), row * 4));
     float wsum = 0.f, mu = 0.f;
     f32x4 ov = {0.f, 0.f, 0.f, 0.f}, hv = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t off = (row * (uint32_t)d + 4 * c4) * 4;
     for (int p = 0; p < P; ++p) {
-      const float w = __expf(buf_load4f(rl, ((uint32_t)p * R + row) * 4) - m);
+      const float w = __expf(buf_load4f(make_rsrc(lse_p + p * stride, row_bytes), row * 4) - m);
       wsum += w;
-      const uint32_t off = (((uint32_t)p * R + row) * (uint32_t)d + 4 * c4) * 4;
-      const f32x4 op = __builtin_bit_cast(f32x4, buf_load16(ro, off));
+      const f32x4 op =
+          __builtin_bit_cast(f32x4, buf_load16(make_rsrc(o_p + p * mat_stride, mat_bytes), off));
       ov += w * op;
       if (tan) {
-        const float mp = buf_load4f(rtl, ((uint32_t)p * R + row) * 4);
-        const f32x4 tp = __builtin_bit_cast(f32x4, buf_load16(rto, off));
+        const float mp = buf_load4f(make_rsrc(tlse_p + p * stride, row_bytes), row * 4);
+        const f32x4 tp = __builtin_bit_cast(
+            f32x4, buf_load16(make_rsrc(to_p + p * mat_stride, mat_bytes), off));
         mu += w * mp;
         hv += w * (tp + mp * op);
       }
     }
     const float inv = 1.0f / wsum;
     ov *= inv;
-    const uint32_t woff = (row * (uint32_t)d + 4 * c4) * 4;
-    buf_store16(wo, woff, __builtin_bit_cast(u32x4, ov));
+    buf_store16(wo, off, __builtin_bit_cast(u32x4, ov));
     if (tan) {
       mu *= inv;
       const f32x4 dv = hv * inv - mu * ov;
-      buf_store16(wto, woff, __builtin_bit_cast(u32x4, dv));
+      buf_store16(wto, off, __builtin_bit_cast(u32x4, dv));
     }
     if (c4 == 0) {
       if (lse != nullptr) buf_store4(wl, row * 4, m + __logf(wsum));
@@ -80,14 +80,13 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
 
 hipError_t launch_merge(const float* lse_p, const float* o_p, const float* to_p,
                         const float* tlse_p, int P, int R, int d, float* lse, float* o,
-                        float* to, float* tlse, hipStream_t stream) {
+                        float* to, float* tlse, hipStream_t stream, int64_t stride) {
   using namespace merge_path;
   const int64_t n = (int64_t)R * (d / 4);
   const int64_t want = (n + kThreads - 1) / kThreads;
   const int blocks = (int)(want < 65536 ? want : 65536);
   hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(kThreads), 0, stream, lse_p, o_p, to_p,
-                     tlse_p, P, R, d, lse, o, to, tlse, (uint32_t)((size_t)P * R * 4),
-                     (uint32_t)((size_t)P * R * d * 4));
+                     tlse_p, P, R, d, stride > 0 ? stride : (int64_t)R, lse, o, to, tlse);
   return hipGetLastError();
 }
 

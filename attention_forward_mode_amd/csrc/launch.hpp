@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace ajvp {
 
@@ -52,10 +53,12 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int H, int Nq, int Nk, int d, float scale, bool out_bf16, void* workspace,
                       hipStream_t stream);
 
-// Merge of P partial results over disjoint key subsets (rows R, head dim d).
+// Merge of P partial results over disjoint key subsets (rows R, head dim d;
+// R * d * 4 under 2^31 bytes).  Part p starts `stride` rows after part p - 1
+// (0: stride R, the parts back to back).
 hipError_t launch_merge(const float* lse_p, const float* o_p, const float* to_p,
                         const float* tlse_p, int P, int R, int d, float* lse, float* o,
-                        float* to, float* tlse, hipStream_t stream);
+                        float* to, float* tlse, hipStream_t stream, int64_t stride = 0);
 
 // Backward pass (gradients of a loss through O): workspace bytes and launch.
 size_t bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d);

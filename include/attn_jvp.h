@@ -264,10 +264,11 @@ ATTN_JVP_API int attn_fwd(const void *q, const void *k, const void *v,
  * tlse = sum_p a_p tlse_p,  dO = sum_p a_p (dO_p + tlse_p O_p) - tlse O.
  * to_parts, tlse_parts and to are either all given (the JVP state) or all NULL
  * (forward only; tlse must then be NULL too); lse may be NULL.  d = 64 or 128,
- * 1 <= P <= 1024, each array under 2^31 bytes.  A row whose parts all have
+ * 1 <= P <= 1024; arrays of any size (rows past 2^31 bytes of one part's O run
+ * as consecutive launches over chunks of rows).  A row whose parts all have
  * lse = -inf yields NaN.  Errors: EINVAL (NULL inputs, inconsistent tangent
- * arguments, P or R < 1), EUNSUPPORTED (d, P or sizes), EALIGN (16-byte for
- * o/to arrays, 4-byte for lse/tlse arrays), ELAUNCH.  Allocates nothing.
+ * arguments, P or R < 1), EUNSUPPORTED (d or P), EALIGN (16-byte for o/to
+ * arrays, 4-byte for lse/tlse arrays), ELAUNCH.  Allocates nothing.
  */
 ATTN_JVP_API int attn_jvp_merge(const float *lse_parts, const float *o_parts,
                    const float *to_parts, const float *tlse_parts,

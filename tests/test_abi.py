@@ -286,7 +286,10 @@ def test_merge_rejects_bad_arguments():
     assert _merge(p) == EINVAL
     assert _merge(P=0) == EINVAL and _merge(R=0) == EINVAL
     assert _merge(d=96) == EUNSUPPORTED and _merge(P=2048) == EUNSUPPORTED
-    assert _merge(P=1024, R=1 << 20) == EUNSUPPORTED  # o_parts past 2^31 bytes
+    # o_parts past 2^31 bytes: accepted (chunks of rows); stops at the misaligned pointer
+    p = [A + j * 0x100000 for j in range(8)]
+    p[1] += 4
+    assert _merge(p, P=1024, R=1 << 20) == EALIGN
     for i in (1, 2, 5, 6):
         p = [A + j * 0x100000 for j in range(8)]
         p[i] += 8

@@ -162,3 +162,48 @@ def test_f32_past_2gib():
     torch.cuda.synchronize()
     ref_o, ref_do, ref_l, _ = _oracle_jvp(x)
     check("f32 >2GiB", (_host(o), _host(to), _host(lse)), (ref_o, ref_do, ref_l), fp32=True)
+
+
+@pytest.mark.parametrize("heads,cuts", [
+    (138, [64]),                  # R = 4.52M rows: one part's O is 2.3 GB, merged in two row chunks
+    (40, [20, 84, 85, 185]),      # 5 parts of 20, 64, 1, 100, 7 keys: parts 3.4 GB in all
+])
+def test_merge_past_2gib(heads, cuts):
+    # the attention of all keys equals the merge of the attentions of a
+    # partition of the keys; every part's state comes from attn_jvp_fwd_ex on
+    # its keys, the whole from the oracle
+    Nk = {138: 128, 40: 192}[heads]
+    shape_q, shape_k = (1, heads, NQ, D), (1, heads, Nk, D)
+    x = {"q": _draw(shape_q, 1.0, 21, torch.bfloat16), "k": _draw(shape_k, 1.0, 22, torch.bfloat16),
+         "v": _draw(shape_k, 1.0, 23, torch.bfloat16), "dq": _draw(shape_q, 0.1, 24, torch.bfloat16),
+         "dk": _draw(shape_k, 0.1, 25, torch.bfloat16), "dv": _draw(shape_k, 0.1, 26, torch.bfloat16)}
+    bounds = [0, *cuts, Nk]
+    P = len(bounds) - 1
+    lse_p = torch.empty((P, 1, heads, NQ), dtype=torch.float32, device="cuda:0")
+    tlse_p = torch.empty_like(lse_p)
+    o_p = torch.empty((P, 1, heads, NQ, D), dtype=torch.float32, device="cuda:0")
+    to_p = torch.empty_like(o_p)
+    assert o_p.numel() * 4 >= 1 << 31
+    for p in range(P):
+        a, b = bounds[p], bounds[p + 1]
+        kv = {n: x[n][:, :, a:b].contiguous() for n in ("k", "v", "dk", "dv")}
+        print(f"  launch attn_jvp_fwd_ex part {p}: keys {a}..{b} H={heads}", flush=True)
+        o, to, lse, mu = ajvp.attn_jvp_fwd_ex(x["q"], kv["k"], kv["v"], x["dq"], kv["dk"], kv["dv"],
+                                              scale=SCALE)
+        o_p[p].copy_(o)
+        to_p[p].copy_(to)
+        lse_p[p].copy_(lse)
+        tlse_p[p].copy_(mu)
+        del o, to, lse, mu, kv
+    print(f"  launch attn_jvp_merge P={P} R={heads * NQ} d={D}", flush=True)
+    lse, o, to, mu = ajvp.attn_jvp_merge(lse_p, o_p, to_p, tlse_p)
+    torch.cuda.synchronize()
+    del o_p, to_p
+    idx = sorted({0, (4194303 // NQ) % heads, heads // 2, heads - 1})
+    host = lambda t: t.reshape(heads, *t.shape[2:])[idx].cpu().unsqueeze(0)
+    h = {n: host(x[n]) for n in x}
+    ref_o, ref_do, ref_l, ref_mu = oracle.attention_jvp(h["q"], h["k"], h["v"], h["dq"], h["dk"],
+                                                        h["dv"], SCALE, with_dlse=True)
+    check(f"merge P={P} >2GiB", (host(o), host(to), host(lse)), (ref_o, ref_do, ref_l), fp32=False)
+    m = metrics(host(mu).double().numpy(), ref_mu)
+    assert m["max_abs"] <= 2e-2 and m["rel_frob"] <= 1e-2, m
