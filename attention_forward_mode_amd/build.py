@@ -1,4 +1,6 @@
-"""Build libattn_jvp.so in-tree: HIP kernels for gfx950 plus the C ABI.
+"""Build libattn_jvp.so in-tree: HIP kernels for gfx950 plus the C ABI; and
+libmfma_probe.so, the matrix-core throughput probe the benchmark reports
+beside the published peak (include/mfma_probe.h).
 
     python -m attention_forward_mode_amd.build        # or __graft_entry__.build()
 
@@ -19,11 +21,13 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn_jvp.so")
+PROBE_LIB = os.path.join(PKG, "libmfma_probe.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["attn_jvp_bf16.hip", "attn_jvp_f32.hip", "attn_jvp_merge.hip", "attn_bwd.hip"]
 CXX_SOURCES = ["attn_jvp_api.cpp"]
+PROBE_SOURCE = "mfma_probe.hip"
 
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -44,7 +48,8 @@ def _run(cmd, verbose):
 
 
 def build(verbose=False, save_temps=False):
-    """Compile every source and link libattn_jvp.so; always rebuilds."""
+    """Compile every source and link libattn_jvp.so and libmfma_probe.so;
+    always rebuilds."""
     hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
     os.makedirs(BUILD, exist_ok=True)
     objs = []
@@ -61,6 +66,10 @@ def build(verbose=False, save_temps=False):
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs,
           f"-L{ROCM}/lib", "-lamdhip64"], verbose)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc, *HIPCC_FLAGS, "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", tmp,
+          f"-L{ROCM}/lib", "-lamdhip64"], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

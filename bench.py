@@ -20,6 +20,11 @@ bf16 inputs, fp32 outputs).  Prints ONE JSON line:
             the kernel source changed since it was taken.
   cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample of
             the same workload (query rows of head 0), same FLOP count.
+  mfma_loop  the bf16 matrix-core rate this board sustains under a load of
+            nothing but matrix products (libmfma_probe.so, same occupancy as
+            the fused kernel: two waves per SIMD), timed after the steps, and
+            the clock it implies (rate / (256 CU x 4096 flop/clk)); beside it
+            the fused kernel's rate as a fraction of that sustained rate.
 
 --calib-copy runs only a plain device copy of known size (the calibration
 kernel for the FETCH_SIZE / WRITE_SIZE counters).
@@ -195,6 +200,42 @@ def bench_variant(args, ajvp, w, g, x, scale):
     print(json.dumps(res), flush=True)
 
 
+def mfma_loop(dev, stream, launches=5):
+    """Rate of the matrix-core probe (include/mfma_probe.h): 512 workgroups of
+    4 waves, 131072 iterations of 4 bf16 32x32x16 products per wave, ~15 ms per
+    launch; HIP events on the launch stream.  None if the probe is not built."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "attention_forward_mode_amd", "libmfma_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mfma_probe_launch.restype = ctypes.c_int
+    lib.mfma_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    wgs, iters = 512, 131072
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    st = ctypes.c_void_p(stream.cuda_stream)
+
+    def launch():
+        rc = lib.mfma_probe_launch(wgs, iters, ctypes.c_void_p(sink.data_ptr()), st)
+        if rc != 0:
+            raise RuntimeError(f"mfma_probe_launch failed ({rc})")
+
+    launch()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
+    ev[0].record(stream)
+    for i in range(launches):
+        launch()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(launches)) / launches
+    tf = wgs * 4 * iters * 131072.0 / (ms / 1e3) / 1e12
+    return {"tflops": round(tf, 1), "clock_ghz_implied": round(tf / 1048.576, 3),
+            "ms_per_launch": round(ms, 3), "launches": launches}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,6 +350,10 @@ def main():
         },
         "kernel_source_sha256": kernel_source_hash(),
     }
+    loop = mfma_loop(dev, stream)
+    if loop is not None:
+        loop["kernel_frac_of_loop"] = round(kern_tflops / loop["tflops"], 4)
+    res["mfma_loop"] = loop
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(x, scale)
     print(json.dumps(res), flush=True)

@@ -83,6 +83,19 @@ def _call(fn, ptrs=None, B=1, H=1, Nq=4, Nk=4, d=128, scale=0.1, ws=None, ws_byt
     return getattr(L, fn)(*args)
 
 
+def test_mfma_probe_library():
+    """The matrix-core probe beside the library (include/mfma_probe.h, timed by
+    bench.py) loads, exports its one entry point and rejects bad arguments
+    before launching."""
+    L = ctypes.CDLL(os.path.join(ROOT, "attention_forward_mode_amd", "libmfma_probe.so"))
+    f = L.mfma_probe_launch
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(1, 1, None, None) == -1
+    assert f(0, 1, ctypes.c_void_p(A), None) == -1
+    assert f(1, 0, ctypes.c_void_p(A), None) == -1
+
+
 FNS = ["attn_jvp_fwd", "attn_jvp_fwd_ws", "attn_jvp_fwd_f32"]
 
 
