@@ -18,6 +18,9 @@ bf16 inputs, fp32 outputs).  Prints ONE JSON line:
             of every timed step.  'traffic' is the measured HBM bytes per
             launch from the committed rocprofv3 counter summary, or null when
             the kernel source changed since it was taken.
+  hbm_gbs_algorithmic / hbm_gbs_measured_kernel  the algorithmic bytes over the
+            step time, and the measured bytes ('traffic') over the fused
+            kernel's time.
   cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample of
             the same workload (query rows of head 0), same FLOP count.
   mfma_loop  the bf16 matrix-core rate this board sustains under a load of
@@ -318,6 +321,7 @@ def main():
     fl = flops(B, H, Nq, Nk, d)
     tflops = fl / (ms / 1e3) / 1e12
     kern_tflops = fl / (kern_ms / 1e3) / 1e12
+    traffic = measured_traffic()
     alg_bytes = (2 * Nq + 4 * Nk) * d * 2 * B * H + (2 * Nq * d + Nq) * 4 * B * H
     res = {
         "metric": METRIC,
@@ -328,6 +332,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "ms_per_step_min": round(min(per), 4),
+        "ms_per_step_median": round(sorted(per)[len(per) // 2], 4),
         "wall_ms_timed_region": round(wall_ms, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -338,6 +343,8 @@ def main():
                    "d": d, "scale": scale, "outputs": "fp32 O, dO, lse"},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "hbm_gbs_algorithmic": round(alg_bytes / (ms / 1e3) / 1e9, 1),
+        "hbm_gbs_measured_kernel": (round(traffic / (kern_ms / 1e3) / 1e9, 1)
+                                    if traffic is not None else None),
         "roofline": {
             "kernel": f"attn_jvp_bf16_kernel<{d}, 0, false>",
             "bound": "mfma",
@@ -345,7 +352,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(),
+            "traffic": traffic,
             "kernel_ms_avg": round(kern_ms, 4),
             "pack_kv_ms_avg": round(sum(pack_ms) / len(pack_ms), 4),
         },
