@@ -324,7 +324,8 @@ def main():
     traffic = measured_traffic()
     alg_bytes = (2 * Nq + 4 * Nk) * d * 2 * B * H + (2 * Nq * d + Nq) * 4 * B * H
     res = {
-        "metric": METRIC,
+        "metric": (METRIC if args.workload == "video_1p3b"
+                   else f"attn+JVP TFLOP/s and % bf16 MFMA peak at 1 GPU ({args.workload})"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
