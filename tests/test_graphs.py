@@ -90,3 +90,32 @@ def test_forward_and_backward_graph_replays():
     graph = _capture(step)
     outs = tuple(state["fwd"]) + tuple(state["bwd"])
     _replays_match(graph, outs, (o, lse) + tuple(want))
+
+
+def test_splitkv_graph_replays():
+    # few queries against many keys: key ranges on separate workgroups, then
+    # the merge kernel, all in the captured graph (caller workspace)
+    x, s = make_inputs("image_dit", Nq=100, Nk=5000, heads=[0, 1])
+    g = to_device(x)
+    B, H, Nq, d = g["q"].shape
+    Nk = g["k"].shape[2]
+    nb = max(ajvp.attn_jvp_splitkv_workspace_bytes(B, H, Nq, Nk, d, 0),
+             ajvp.attn_jvp_splitkv_workspace_bytes(B, H, Nq, Nk, d, 7))
+    assert nb > ajvp.attn_jvp_workspace_bytes(B, H, Nk, d)  # partial states: more than one range
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    args = [g[n] for n in NAMES]
+    want = ajvp.attn_jvp_fwd_splitkv(*args, scale=s)
+    want_f = ajvp.attn_fwd_splitkv(g["q"], g["k"], g["v"], scale=s, nsplit=7)
+    torch.cuda.synchronize()
+    print(f"  capture attn_jvp_fwd_splitkv + attn_fwd_splitkv q{tuple(g['q'].shape)} "
+          f"k{tuple(g['k'].shape)}", flush=True)
+    state = {}
+
+    def step():
+        state["jvp"] = ajvp.attn_jvp_fwd_splitkv(*args, scale=s, workspace=ws)
+        state["fwd"] = ajvp.attn_fwd_splitkv(g["q"], g["k"], g["v"], scale=s, nsplit=7,
+                                             workspace=ws)
+
+    graph = _capture(step)
+    outs = tuple(state["jvp"]) + tuple(state["fwd"])
+    _replays_match(graph, outs, tuple(want) + tuple(want_f))
