@@ -510,6 +510,115 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
   jvp_epilogue<D, kOutBf16>(st, obh, row, Nq, g, o, to, lse, tlse, ext);
 }
 
+// ---- short key ranges: 128-row workgroups, one LDS stage, two per CU ----
+// With few key tiles per work item (cross-attention to a short text, or a
+// short split-KV range) the 256-row kernel spends a large share of its time
+// loading Q, dQ and storing O, dO, and with one workgroup per CU nothing runs
+// beside those memory phases.  Here a workgroup holds 4 waves (128 rows) and
+// one 64 KiB stage, so two fit on a CU (registers: 2 x 4 waves x 256 = two
+// waves per SIMD, as before; LDS: 2 x 64 KiB) and one computes while the other
+// loads, stores or waits for its next tile.  Per row the arithmetic is that of
+// the 256-row kernel (same blocks, same key order), so the results are the
+// same bit for bit.
+constexpr int kShortWaves = 4;
+constexpr int kShortThreads = 64 * kShortWaves;
+constexpr int kShortBR = kShortWaves * kRowsPerWave;  // query rows per workgroup
+// Work items of at most this many key tiles take the short kernel.  Measured
+// at H = 12, Nq = 32760 against the 256-row kernel: 64 keys 146 vs 171 us, 256
+// keys 220 vs 245, 512 keys 337 vs 369, 1024 keys 551 vs 567; 2048 keys 1034
+// vs 1021 and B H = 32, N = 4096 750 vs 701 (there the doubled tile stream per
+// row costs more than the overlap gains).
+constexpr int kShortMaxTiles = 16;
+
+template <int D, int kMode, bool kOutBf16>
+__global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ tq,
+    const char* __restrict__ img, void* __restrict__ o, void* __restrict__ to,
+    float* __restrict__ lse, float* __restrict__ tlse, int Nq, int Nk, int ntiles, int nqt,
+    int nbh, int tps, Extents ext, float scale, float c_log2) {
+  using M = Mode<kMode>;
+  using G = Geo<D, M::kKV>;
+  __shared__ __attribute__((aligned(1024))) char smem[G::kImgBytes];
+
+  // work item: as in attn_jvp_bf16_kernel, with row tiles of kShortBR rows
+  const uint32_t wg = blockIdx.x, nwg = gridDim.x;
+  const uint32_t xcd = wg % kXcds, slot = wg / kXcds, per = nwg / kXcds, extra = nwg % kXcds;
+  const uint32_t work = xcd < extra ? xcd * (per + 1) + slot
+                                    : extra * (per + 1) + (xcd - extra) * per + slot;
+  const int qt = (int)(work % (uint32_t)nqt);
+  const uint32_t obh = work / (uint32_t)nqt;
+  const uint32_t bh = obh % (uint32_t)nbh;
+  const int t0 = (int)(obh / (uint32_t)nbh) * tps;
+  const int t1 = t0 + tps < ntiles ? t0 + tps : ntiles;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int row = qt * kShortBR + wave * kRowsPerWave + l32;
+  const bool row_ok = row < Nq;
+
+  const auto rq = make_rsrc(q, ext.q_bytes);
+  const auto rtq = make_rsrc(tq, tq != nullptr ? ext.q_bytes : 0u);
+  const uint32_t slice_bytes = (uint32_t)ntiles * G::kImgBytes;
+  const auto rimg = make_rsrc(img + (size_t)bh * slice_bytes, slice_bytes);
+
+  // Copy of tile image kt into the stage: this wave's quarter, 1 KiB per
+  // instruction, lane l moving bytes 16 l .. 16 l + 15 of each KiB.
+  constexpr int kPer = G::kImgBytes / (kShortWaves * kDmaBytes);
+  const uint32_t wave_part = (uint32_t)wave * kPer * kDmaBytes;
+  auto copy_one = [&](int kt, char* stage, int j) {
+    const uint32_t src = (uint32_t)kt * G::kImgBytes + wave_part + j * kDmaBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rimg, (lds_ptr_t)(stage + wave_part + j * kDmaBytes),
+                                             16, lane * 16, src, 0, 0);
+  };
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) copy_one(t0, smem, j);
+
+  u32x4 qf[G::kKS], dqf[G::kKS];
+  const uint32_t qrow = row_ok ? (bh * (uint32_t)Nq + row) * D * 2 : 0x80000000u;
+#pragma unroll
+  for (int ks = 0; ks < G::kKS; ++ks) {
+    const uint32_t off = qrow + (16 * ks + 8 * g) * 2;
+    qf[ks] = buf_load16(rq, off);
+    dqf[ks] = buf_load16(rtq, off);
+  }
+
+  RowState<D> st;
+#pragma unroll
+  for (int cb = 0; cb < G::kCB; ++cb) {
+    st.accA[cb] = f32x16{};
+    st.accG[cb] = f32x16{};
+  }
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.u = 0.f;
+
+  // Tile kt: wait for its copy (every wave's share) and make it visible, compute
+  // both blocks, then a barrier retires every read of the stage before the
+  // copy of tile kt + 1 overwrites it.
+  auto none = [](int) {};
+  auto tile_ready = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  const int kLast = t1 - 1;
+  for (int kt = t0; kt < kLast; ++kt) {
+    tile_ready();
+    jvp_block<D, kMode, false>(st, smem, 0, qf, dqf, l32, g, 0, Nk, c_log2, scale, none);
+    jvp_block<D, kMode, false>(st, smem, 1, qf, dqf, l32, g, 0, Nk, c_log2, scale, none);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) copy_one(kt + 1, smem, j);
+  }
+  tile_ready();
+  {
+    const int kl = kLast * kBC;
+    jvp_block<D, kMode, true>(st, smem, 0, qf, dqf, l32, g, kl, Nk, c_log2, scale, none);
+    jvp_block<D, kMode, true>(st, smem, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, scale, none);
+  }
+
+  jvp_epilogue<D, kOutBf16>(st, obh, row, Nq, g, o, to, lse, tlse, ext);
+}
+
 // ---- forward attention alone (O, lse) ----
 // RB = 2: each wave holds 64 query rows (two 32-row blocks), so every K and
 // V^T fragment it reads from LDS feeds two matrix products, and a workgroup of
@@ -758,7 +867,6 @@ hipError_t launch_main_d(const void* q, const void* tq, const void* ws, void* o,
                          float* lse, float* tlse, int B, int H, int Nq, int Nk, float scale,
                          int nsplit, hipStream_t stream) {
   const int ntiles = (Nk + kBC - 1) / kBC;
-  const int nqt = (Nq + kBR - 1) / kBR;
   const int bh = B * H;
   const int tps = (ntiles + nsplit - 1) / nsplit;
   const int ns = (ntiles + tps - 1) / tps;  // no empty range
@@ -766,6 +874,15 @@ hipError_t launch_main_d(const void* q, const void* tq, const void* ws, void* o,
   ext.q_bytes = (uint32_t)((size_t)bh * Nq * D * 2);
   ext.o_bytes = (uint32_t)((size_t)ns * bh * Nq * D * (kOutBf16 ? 2 : 4));
   ext.lse_bytes = (uint32_t)((size_t)ns * bh * Nq * 4);
+  if (tps <= kShortMaxTiles) {
+    const int nqt = (Nq + kShortBR - 1) / kShortBR;
+    hipLaunchKernelGGL((attn_jvp_bf16_short_kernel<D, kMode, kOutBf16>), dim3(nqt * bh * ns),
+                       dim3(kShortThreads), 0, stream, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(tq), static_cast<const char*>(ws), o, to,
+                       lse, tlse, Nq, Nk, ntiles, nqt, bh, tps, ext, scale, scale * kLog2e);
+    return hipGetLastError();
+  }
+  const int nqt = (Nq + kBR - 1) / kBR;
   hipLaunchKernelGGL((attn_jvp_bf16_kernel<D, kMode, kOutBf16>), dim3(nqt * bh * ns),
                      dim3(kThreads), 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(tq), static_cast<const char*>(ws), o, to, lse,

@@ -79,6 +79,17 @@ def measured_traffic():
         return None
 
 
+# Work items of at most this many 64-key tiles run the library's 128-row
+# short-key kernel (kShortMaxTiles in attn_jvp_bf16.hip); the name is reported.
+SHORT_MAX_TILES = 16
+
+
+def jvp_kernel_name(Nk, d):
+    if -(-Nk // 64) <= SHORT_MAX_TILES:
+        return f"attn_jvp_bf16_short_kernel<{d}, 0, false>"
+    return f"attn_jvp_bf16_kernel<{d}, 0, false>"
+
+
 def flops(B, H, Nq, Nk, d):
     return 12.0 * B * H * Nq * Nk * d
 
@@ -195,8 +206,8 @@ def bench_variant(args, ajvp, w, g, x, scale):
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"kernel": {"bwd": "pack_q + pack_k + bwd_kv + bwd_q (one call)",
                                 "fwd": "pack_kv + attn_fwd_bf16_kernel (one call, pack included)"}
-                               .get(args.mode, "pack_kv + attn_jvp_bf16_kernel (one call, pack "
-                                               "included)"),
+                               .get(args.mode, f"pack_kv + {jvp_kernel_name(Nk, d).split('<')[0]} "
+                                               "(one call, pack included)"),
                      "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
@@ -347,7 +358,7 @@ def main():
         "hbm_gbs_measured_kernel": (round(traffic / (kern_ms / 1e3) / 1e9, 1)
                                     if traffic is not None else None),
         "roofline": {
-            "kernel": f"attn_jvp_bf16_kernel<{d}, 0, false>",
+            "kernel": jvp_kernel_name(Nk, d),
             "bound": "mfma",
             "achieved": round(kern_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
