@@ -978,13 +978,19 @@ hipError_t launch_fwd_rb(const void* q, const void* ws, void* o, float* lse, int
 
 // 512-row workgroups, unless even the 256-row ones fit the chip's 256 CUs
 // one per CU (then twice as many CUs work; measured at Nk = 32760, H = 12:
-// Nq = 4096 1446 -> 994 us, Nq = 8192 with 512 rows 1534 us vs 1730).  ns
-// key-tile ranges (1: the plain pass).
+// Nq = 4096 1446 -> 994 us, Nq = 8192 with 512 rows 1534 us vs 1730) or a
+// work item has at most kShortMaxTiles key tiles.  ns key-tile ranges (1: the
+// plain pass).
 template <int D, bool kOutBf16>
 hipError_t launch_fwd_d(const void* q, const void* ws, void* o, float* lse, int B, int H, int Nq,
                         int Nk, float scale, int ns, hipStream_t stream) {
   const long tiles256 = (long)(Nq + fwd_rows<1>() - 1) / fwd_rows<1>() * B * H * ns;
-  if (tiles256 > 256)
+  const int ntiles = (Nk + kBC - 1) / kBC, tps = (ntiles + ns - 1) / ns;
+  // few key tiles per work item: two workgroups per CU overlap one's query
+  // and output traffic with the other's products, as in the short-key JVP
+  // kernel (H = 12, Nq = 32760: 512 keys 148 vs 164 us, 1024 keys 231 vs 244;
+  // 2048 keys 402 vs 395)
+  if (tiles256 > 256 && tps > kShortMaxTiles)
     return launch_fwd_rb<D, 2, kOutBf16>(q, ws, o, lse, B, H, Nq, Nk, scale, ns, stream);
   return launch_fwd_rb<D, 1, kOutBf16>(q, ws, o, lse, B, H, Nq, Nk, scale, ns, stream);
 }
