@@ -88,7 +88,9 @@ int check_sizes(int B, int H, int Nq, int Nk, int d, int esize) {
   return ATTN_JVP_OK;
 }
 
-bool bad_scale(float scale) { return !(scale >= 0.0f) || std::isinf(scale); }
+// Any finite scale is valid: the definition holds for either sign (s < 0
+// reverses the order of the logits); NaN and +-Inf are rejected.
+bool bad_scale(float scale) { return !std::isfinite(scale); }
 
 // Checks of the forward entry points: null pointers, sizes, scale, then
 // alignment (16 bytes for tensors, 4 for lse).  `in` holds n input pointers.

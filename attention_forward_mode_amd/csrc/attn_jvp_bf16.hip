@@ -7,15 +7,19 @@
 //   dS = s (dQ K^T + Q dK^T),  mu = rowsum(P * dS),  lse = ln rowsum exp(s Q K^T),
 //   and mu is also the tangent of lse.
 //
-// Two kernels per call:
-//  1. pack_kv: K, dK, V, dV -> one "tile image" per 64 keys in the workspace,
+// Three kernels per call:
+//  1. range_stats (range.hpp): per (b, h) the largest finite |V| and |dV|
+//     (partial maxima over chunks of keys), from which the pack takes the
+//     power-of-two exponents that scale V and dV into fp16's upper range.
+//  2. pack_kv: K, dK, V, dV -> one "tile image" per 64 keys in the workspace,
 //     byte for byte the LDS layout the fused kernel computes from: K and dK
-//     (bf16), then V^T and dV^T (fp16), each stored as the sequence of
-//     matrix-core operand fragments the waves read (1 KiB per fragment, lane l
-//     at bytes 16 l .. 16 l + 15), zero past Nk.  HBM bound, under 1% of the
-//     fused kernel's time at N = 32760.  fp16 instead of bf16 for the second
-//     contraction keeps P and P*dS at 11 significant bits.
-//  2. attn_jvp_bf16: one workgroup = 8 waves x 32 query rows of one (b, h),
+//     (bf16), then V^T 2^eV and dV^T 2^edV (fp16), each stored as the sequence
+//     of matrix-core operand fragments the waves read (1 KiB per fragment, lane
+//     l at bytes 16 l .. 16 l + 15), zero past Nk; and the slice's largest key
+//     norms |k_j|, |dk_j|.  HBM bound, about 1% of the fused kernel's time at
+//     N = 32760 together with the stats.  fp16 instead of bf16 for the
+//     second contraction keeps P and P*dS at 11 significant bits.
+//  3. attn_jvp_bf16: one workgroup = 8 waves x 32 query rows of one (b, h),
 //     two waves per SIMD.  Per 64-key tile the waves copy the next tile image
 //     from the workspace straight into LDS (buffer loads with the LDS-direct
 //     bit, 1 KiB per instruction, no registers in between; double buffered),
@@ -25,8 +29,14 @@
 //     online softmax in the accumulator layout (each lane owns one query row,
 //     so row state is per lane), and
 //        A^T += V^T P^T,  G^T += V^T (s P dS)^T + dV^T P^T  (fp16 MFMA)
-//     with P, s*P*dS rounded to fp16.  The epilogue forms O = A / l,
-//     mu = u / l (u = rowsum s P dS), dO = G / l - mu O and lse.
+//     with P, s*P*dS rounded to fp16.  s*P*dS is formed as P dS (s 2^t): each
+//     wave takes t from a bound of |s dS| over its rows (|s| (|dq_i| max|k_j|
+//     + |q_i| max|dk_j|)), so that it stays below 4000 and |s P dS 2^t| below
+//     64000; G then holds 2^(eV + t) times its value (dV is packed at
+//     2^(eV + t) when the head's t fits every wave; a wave whose bound needs a
+//     smaller t scales its dV^T fragments by the difference instead).  The
+//     epilogue forms O = A 2^-eV / l, mu = u 2^-t / l (u = rowsum s P dS 2^t),
+//     dO = G 2^-(eV + t) / l - mu O and lse.
 //  While one wave of a SIMD runs its softmax on the vector ALU, the other
 //  keeps the matrix core busy; every wave fits in 256 registers (128
 //  accumulators, 64 for the Q and dQ operands, 64 for the rest).
@@ -48,6 +58,7 @@
 
 #include "cdna4.hpp"
 #include "launch.hpp"
+#include "range.hpp"
 
 namespace ajvp {
 namespace bf16_path {
@@ -96,6 +107,16 @@ static_assert(Geo<128, true>::kImgBytes == 65536 && Geo<64, true>::kImgBytes == 
                   Geo<128, true>::kImgUsed == Geo<128, true>::kImgBytes,
               "tile image sizes");
 
+// One (b, h) slice of the workspace: the ntiles tile images, then the header
+// of range.hpp (kHdrBytes): record = {int eV, int edV, uint flags}, norm
+// maxima = {max_j |k_j|, max_j |dk_j|}, the range pass's partial maxima of
+// |V| and |dV|.
+constexpr uint32_t kDvZero = 1u;  // flags: dV has no finite nonzero value (or no dV at all)
+template <int D, bool kKV>
+__host__ __device__ constexpr uint32_t slice_bytes(int ntiles) {
+  return (uint32_t)ntiles * Geo<D, kKV>::kImgBytes + kHdrBytes;
+}
+
 // Key held at position `pos` (0..63) of a packed V^T row.  Positions
 // 16G + 8g + e hold the keys that the S^T accumulator of lane half g puts in
 // slots 8t + e of block G/2, t = G%2: keys 16G + 4g + e (e < 4) and
@@ -106,7 +127,11 @@ __device__ inline int packed_key(int pos) {
 }
 
 // One tile image: blockIdx.x = 64-key tile, blockIdx.y = (b, h) slice.  A NULL
-// dk or dv gets an empty descriptor, so its part of the image is zero.
+// dk or dv gets an empty descriptor, so its part of the image is zero.  V and
+// dV are written as fp16(v 2^eV), fp16(dv 2^edV) with the slice's exponents
+// (fp16_exponent of range_stats' maxima, which every wave reduces itself);
+// the workgroup of tile 0 writes them to the slice header, and every tile
+// raises the slice's largest key norms to its own.
 template <int D, bool kKV>
 __device__ __attribute__((always_inline)) inline void pack_kv_body(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -115,47 +140,89 @@ __device__ __attribute__((always_inline)) inline void pack_kv_body(
   using G = Geo<D, kKV>;
   constexpr int kT = G::kNT;
   __shared__ _Float16 sv[kT][kBC][D + 2];
+  __shared__ double snorm[2][kPackThreads / 64];
   const int tile = blockIdx.x;
   const uint32_t bh = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // Every global access goes through a buffer descriptor spanning the whole
   // tensor: an offset outside it is dropped (stores) or reads zero (loads).
   const auto rk = make_rsrc(k, kv_bytes);
   const auto rdk = make_rsrc(dk, dk != nullptr ? kv_bytes : 0u);
   const auto rv = make_rsrc(v, kv_bytes);
   const auto rdv = make_rsrc(dv, dv != nullptr ? kv_bytes : 0u);
-  // the workspace descriptor spans this (b, h) slice's images only
-  const uint32_t slice_bytes = (uint32_t)ntiles * G::kImgBytes;
-  const auto rws = make_rsrc(ws + (size_t)bh * slice_bytes, slice_bytes);
+  // the workspace descriptor spans this (b, h) slice's images and header only
+  const uint32_t sb = slice_bytes<D, kKV>(ntiles);
+  const uint32_t hdr = (uint32_t)ntiles * G::kImgBytes;
+  const auto rws = make_rsrc(ws + (size_t)bh * sb, sb);
   const int key0 = tile * kBC;
   const uint32_t img = (uint32_t)tile * G::kImgBytes;
   constexpr int kChunksPerRow = D / 8;  // 16-byte chunks of one input row
   constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
+
+  // the slice's exponents, from the partial maxima of range_stats
+  uint32_t mv, mdv;
+  slice_maxima(rws, hdr, ntiles, lane, mv, mdv);
+  const int ev = fp16_exponent(mv);
+  const int edv = kKV ? fp16_exponent(mdv) : 0;
+
   // K, dK: 16-byte chunk col of key row r goes to lane (r % 32) + 32 (col % 2)
-  // of fragment (r / 32) kKS + col / 2; keys >= Nk are zero.
+  // of fragment (r / 32) kKS + col / 2; keys >= Nk are zero.  Each key's sum
+  // of squares (fp64) is summed over the kChunksPerRow consecutive lanes that
+  // hold its row; the tile's largest goes to the header.
   constexpr int kKChunks = kBC * kChunksPerRow;
-  for (int c = threadIdx.x; c < kT * kKChunks; c += kPackThreads) {
-    const int t = c / kKChunks, rem = c % kKChunks;
-    const int r = rem / kChunksPerRow, col = rem % kChunksPerRow;
-    const int key = key0 + r;
-    u32x4 x = kZero;
-    if (key < Nk) x = buf_load16(t == 0 ? rk : rdk, ((bh * (uint32_t)Nk + key) * D + 8 * col) * 2);
-    const int frag = (r >> 5) * G::kKS + (col >> 1), ln = (r & 31) + 32 * (col & 1);
-    buf_store16(rws, img + t * G::kOffdK + frag * kDmaBytes + ln * 16, x);
+  static_assert(kKChunks % kPackThreads == 0, "one tensor per pass of the loop");
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    double kss = 0.0;
+    if (t < kT) {
+      for (int c = threadIdx.x; c < kKChunks; c += kPackThreads) {
+        const int r = c / kChunksPerRow, col = c % kChunksPerRow;
+        const int key = key0 + r;
+        u32x4 x = kZero;
+        if (key < Nk)
+          x = buf_load16(t == 0 ? rk : rdk, ((bh * (uint32_t)Nk + key) * D + 8 * col) * 2);
+        const int frag = (r >> 5) * G::kKS + (col >> 1), ln = (r & 31) + 32 * (col & 1);
+        buf_store16(rws, img + t * G::kOffdK + frag * kDmaBytes + ln * 16, x);
+        double ss = sumsq8(x);
+#pragma unroll
+        for (int m = 1; m < kChunksPerRow; m <<= 1) ss += __shfl_xor(ss, m);
+        kss = __builtin_fmax(kss, ss);
+      }
+    }
+    kss = wave_max_f64(kss);
+    if (lane == 0) snorm[t][wave] = kss;
   }
-  // V, dV: to fp16 in LDS, then written transposed as operand fragments.
+  // V, dV: scaled to fp16 in LDS, then written transposed as operand fragments.
   constexpr int kIn = kBC * kChunksPerRow;
   for (int c = threadIdx.x; c < kT * kIn; c += kPackThreads) {
     const int t = c / kIn, rem = c % kIn, r = rem / kChunksPerRow, col = (rem % kChunksPerRow) * 8;
     const int key = key0 + r;
+    const int e_t = t == 0 ? ev : edv;
     u32x4 x = kZero;
     if (key < Nk) x = buf_load16(t == 0 ? rv : rdv, ((bh * (uint32_t)Nk + key) * D + col) * 2);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t bits = (x[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-      sv[t][r][col + e] = (_Float16)__builtin_bit_cast(float, bits << 16);
+      sv[t][r][col + e] = (_Float16)__builtin_amdgcn_ldexpf(__builtin_bit_cast(float, bits << 16), e_t);
     }
   }
   __syncthreads();
+  if (threadIdx.x == 0) {
+    double nk = snorm[0][0], ndk = snorm[1][0];
+    for (int i = 1; i < kPackThreads / 64; ++i) {
+      nk = __builtin_fmax(nk, snorm[0][i]);
+      ndk = __builtin_fmax(ndk, snorm[1][i]);
+    }
+    const float fk = round_up_f32(__builtin_sqrt(nk));
+    const float fdk = kKV ? round_up_f32(__builtin_sqrt(ndk)) : 0.f;
+    uint32_t* nmax = reinterpret_cast<uint32_t*>(ws + (size_t)bh * sb + hdr + kHdrNorms);
+    atomicMax(nmax, __builtin_bit_cast(uint32_t, fk));
+    atomicMax(nmax + 1, __builtin_bit_cast(uint32_t, fdk));
+    if (tile == 0) {
+      const uint32_t flags = (!kKV || mdv == 0) ? kDvZero : 0u;
+      buf_store16(rws, hdr + kHdrRecord, u32x4{(uint32_t)ev, (uint32_t)edv, flags, 0u});
+    }
+  }
   constexpr int kVChunks = G::kVTile / 16;  // = 64 lanes x fragments
   for (int c = threadIdx.x; c < kT * kVChunks; c += kPackThreads) {
     const int t = c / kVChunks, rem = c % kVChunks, frag = rem >> 6, ln = rem & 63;
@@ -192,7 +259,10 @@ __device__ __attribute__((always_inline)) inline int slot_key(int r, int g) {
 // them and adds the block's P V products with the V^T and dV^T fragments at
 // vbase, dvbase (fragment f of a part at base + f KiB, the tile image's
 // layout).  kMask: the block may hold keys >= Nk, which get p = 0 and
-// contribute nothing to u.  issue(slot) is called at the start of each step
+// contribute nothing to u.  kScaleDV: the dV^T fragments are multiplied by
+// dv_mul (two equal fp16 powers of two) after their read, for a wave whose
+// tangent exponent is below the one dV was packed for.  `scale` is s 2^t, the
+// wave's scale of s P dS.  issue(slot) is called at the start of each step
 // (slots 0..kKS-1: the S/dS steps, then kKS.. the P V steps).
 // Online-softmax order: the accumulators hold sums normalised to the running
 // max m; a raised max rescales them by alpha = 2^(m_old - m_new) before this
@@ -221,10 +291,10 @@ __device__ __attribute__((always_inline)) inline void qk_phase(
   }
 }
 
-template <int D, int kMode, bool kMask, typename Issue>
+template <int D, int kMode, bool kMask, bool kScaleDV, typename Issue>
 __device__ __attribute__((always_inline)) inline void sm_pv_phase(
     RowState<D>& st, f32x16 s, f32x16 ds, const char* vbase, const char* dvbase, int lane16,
-    int g, int key0, int Nk, float c_log2, float scale, Issue issue) {
+    int g, int key0, int Nk, float c_log2, float scale, uint32_t dv_mul, Issue issue) {
   using M = Mode<kMode>;
   using G = Geo<D, M::kKV>;
   // running max (NaN-propagating maximum, combined across the half-waves)
@@ -303,24 +373,29 @@ __device__ __attribute__((always_inline)) inline void sm_pv_phase(
     }
     st.accA[cb] = mma_f16(vf[step & 1], p[t], st.accA[cb]);
     st.accG[cb] = mma_f16(vf[step & 1], pd[t], st.accG[cb]);
-    if constexpr (M::kKV) st.accG[cb] = mma_f16(dvf[step & 1], p[t], st.accG[cb]);
+    if constexpr (M::kKV) {
+      u32x4 dvx = dvf[step & 1];
+      if constexpr (kScaleDV) dvx = mul_f16x8(dvx, dv_mul);
+      st.accG[cb] = mma_f16(dvx, p[t], st.accG[cb]);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // One 32-key block (block `kb` of the 64-key tile image in `stage`): both
 // phases back to back.
-template <int D, int kMode, bool kMask, typename Issue>
+template <int D, int kMode, bool kMask, bool kScaleDV, typename Issue>
 __device__ __attribute__((always_inline)) inline void jvp_block(
     RowState<D>& st, const char* stage, int kb, const u32x4* qf, const u32x4* dqf, int l32,
-    int g, int key0, int Nk, float c_log2, float scale, Issue issue) {
+    int g, int key0, int Nk, float c_log2, float scale, uint32_t dv_mul, Issue issue) {
   using G = Geo<D, Mode<kMode>::kKV>;
   const int lane16 = 16 * l32 + 512 * g;  // this lane's 16 bytes of a fragment
   const int kf0 = kb * G::kKS * kDmaBytes, vf0 = 2 * kb * G::kCB * kDmaBytes;
   f32x16 s, ds;
   qk_phase<D, kMode>(s, ds, stage + kf0, stage + G::kOffdK + kf0, qf, dqf, lane16, issue);
-  sm_pv_phase<D, kMode, kMask>(st, s, ds, stage + G::kOffV + vf0, stage + G::kOffdV + vf0, lane16,
-                               g, key0, Nk, c_log2, scale, issue);
+  sm_pv_phase<D, kMode, kMask, kScaleDV>(st, s, ds, stage + G::kOffV + vf0,
+                                         stage + G::kOffdV + vf0, lane16, g, key0, Nk, c_log2,
+                                         scale, dv_mul, issue);
 }
 
 // One full tile: the copy of the next tile image into `next` is spread over
@@ -329,17 +404,18 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
 // computed from `cur`.  The two stage pointers are restrict-qualified (they
 // name disjoint halves of the LDS), which tells the compiler that reads of
 // `cur` need not wait for the copy into `next`.
-template <int D, int kMode, typename Copy>
+template <int D, int kMode, bool kScaleDV, typename Copy>
 __device__ __attribute__((always_inline)) inline void tile_step(
     char* __restrict__ next, const char* __restrict__ cur, Copy copy, RowState<D>& st,
-    const u32x4* qf, const u32x4* dqf, int l32, int g, int Nk, float c_log2, float scale) {
+    const u32x4* qf, const u32x4* dqf, int l32, int g, int Nk, float c_log2, float scale,
+    uint32_t dv_mul) {
   using G = Geo<D, Mode<kMode>::kKV>;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
-    jvp_block<D, kMode, false>(st, cur, kb, qf, dqf, l32, g, 0, Nk, c_log2, scale,
-                               [&](int slot) {
-                                 if (kb == 0 && slot < G::kDmaPerWave) copy(next, slot);
-                               });
+    jvp_block<D, kMode, false, kScaleDV>(st, cur, kb, qf, dqf, l32, g, 0, Nk, c_log2, scale,
+                                         dv_mul, [&](int slot) {
+                                           if (kb == 0 && slot < G::kDmaPerWave) copy(next, slot);
+                                         });
 }
 
 // Sizes of the whole tensors (bytes) the kernel may touch; each global access
@@ -364,16 +440,19 @@ __device__ __attribute__((always_inline)) inline void store4(__amdgpu_buffer_rsr
   }
 }
 
-// Epilogue of one wave: O = A / l, mu = u / l, dO = G / l - mu O, lse and
-// tlse = mu for this lane's query row of output slice obh (rows past Nq are
-// not stored).
+// Epilogue of one wave: O = A 2^-ea / l, mu = u 2^-eu / l,
+// dO = G 2^-eg / l - mu O, lse and tlse = mu for this lane's query row of
+// output slice obh (rows past Nq are not stored).  The accumulators hold A,
+// G and u scaled by 2^ea, 2^eg and 2^eu (the fp16 exponents of V and of the
+// tangent terms); multiplying 1/l by a power of two is exact.
 template <int D, bool kOutBf16>
 __device__ __attribute__((always_inline)) inline void jvp_epilogue(
     const RowState<D>& st, uint32_t obh, int row, int Nq, int g, void* o, void* to, float* lse,
-    float* tlse, const Extents& ext) {
+    float* tlse, const Extents& ext, int ea, int eg, int eu) {
   const float l = halves_sum(st.l);
   const float inv_l = 1.0f / l;
-  const float mu = halves_sum(st.u) * inv_l;
+  const float fa = __builtin_amdgcn_ldexpf(inv_l, -ea), fg = __builtin_amdgcn_ldexpf(inv_l, -eg);
+  const float mu = halves_sum(st.u) * __builtin_amdgcn_ldexpf(inv_l, -eu);
   if (row < Nq) {
     const uint32_t orow = (obh * (uint32_t)Nq + row) * D;  // first element of the row
     const auto ro = make_rsrc(o, ext.o_bytes);
@@ -386,9 +465,9 @@ __device__ __attribute__((always_inline)) inline void jvp_epilogue(
         f32x4 ov, tv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float a = st.accA[cb][4 * qq + e] * inv_l;
+          const float a = st.accA[cb][4 * qq + e] * fa;
           ov[e] = a;
-          tv[e] = st.accG[cb][4 * qq + e] * inv_l - mu * a;
+          tv[e] = st.accG[cb][4 * qq + e] * fg - mu * a;
         }
         store4<kOutBf16>(ro, orow + c0, ov);
         store4<kOutBf16>(rto, orow + c0, tv);
@@ -400,6 +479,73 @@ __device__ __attribute__((always_inline)) inline void jvp_epilogue(
       if (tlse != nullptr) buf_store4(make_rsrc(tlse, ext.lse_bytes), off, mu);
     }
   }
+}
+
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
+// A wave's fp16 exponents: eV of the slice (header record), and the tangent
+// exponent t of s P dS, from the bound |s dS_ij| <= |s| (|dq_i| Mk + |q_i| Mdk)
+// (Cauchy-Schwarz) over the wave's rows i (row norms from its Q and dQ
+// fragments, fp64) and all keys of the slice (Mk, Mdk: the largest key norms,
+// from the header).
+// With dV present, t is the slice's edV - eV (dV was packed at 2^(eV + t))
+// unless the bound needs a smaller one; then `slow` is set and dv_mul = 2^(t -
+// edV + eV) rescales the dV^T fragments.  Without dV (frozen keys, or dV = 0)
+// any t is consistent and the bound alone sets it.
+struct WaveScale {
+  int ev, t;
+  float s_t;        // scale 2^t
+  uint32_t dv_mul;  // two fp16 copies of 2^(t - edV + eV)
+  bool slow;
+};
+
+template <int D, bool kKV>
+__device__ __attribute__((always_inline)) inline WaveScale wave_scale(
+    __amdgpu_buffer_rsrc_t rimg, uint32_t hdr, const u32x4* qf, const u32x4* dqf, float scale) {
+  const u32x4 rec = buf_load16(rimg, hdr + kHdrRecord);
+  const uint32_t mk_bits = __builtin_amdgcn_raw_buffer_load_b32(rimg, (int)(hdr + kHdrNorms), 0, 0);
+  const uint32_t mdk_bits =
+      __builtin_amdgcn_raw_buffer_load_b32(rimg, (int)(hdr + kHdrNorms + 4), 0, 0);
+  const float mk = __builtin_bit_cast(float, mk_bits), mdk = __builtin_bit_cast(float, mdk_bits);
+  double nq = 0.0, ndq = 0.0;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    if constexpr (kKV) nq += sumsq8(qf[ks]);
+    ndq += sumsq8(dqf[ks]);
+  }
+  double b = __builtin_sqrt(halves_sum_f64(ndq)) * (double)mk;
+  if constexpr (kKV) b += __builtin_sqrt(halves_sum_f64(nq)) * (double)mdk;
+  b *= __builtin_fabs((double)scale);
+  // A row (or key) with an Inf or NaN gives a non-finite bound; its outputs
+  // are non-finite whatever t is, so it does not take part in the wave's choice.
+  b = wave_max_f64(__builtin_isfinite(b) ? b : 0.0);
+  const int ev = __builtin_amdgcn_readfirstlane((int)rec[0]);
+  const int edv = __builtin_amdgcn_readfirstlane((int)rec[1]);
+  const uint32_t flags = __builtin_amdgcn_readfirstlane(rec[2]);
+  WaveScale w;
+  w.ev = ev;
+  w.slow = false;
+  w.dv_mul = 0x3c003c00u;  // 1.0, 1.0
+  int t;
+  if (!kKV || (flags & kDvZero)) {
+    t = product_exponent(b);
+  } else {
+    const int th = edv - ev;
+    const bool slow = __builtin_ldexp(b, th) > kProdSafe;  // false for NaN
+    t = slow ? product_exponent(b) : th;
+    w.slow = __builtin_amdgcn_readfirstlane((int)slow) != 0;
+    const _Float16 m = (_Float16)__builtin_amdgcn_ldexpf(1.0f, t - th);
+    w.dv_mul = (uint32_t)__builtin_bit_cast(uint16_t, m) * 0x10001u;
+  }
+  w.t = __builtin_amdgcn_readfirstlane(t);
+  w.dv_mul = __builtin_amdgcn_readfirstlane(w.dv_mul);
+  w.s_t = __builtin_bit_cast(
+      float, __builtin_amdgcn_readfirstlane(
+                 __builtin_bit_cast(int, __builtin_amdgcn_ldexpf(scale, w.t))));
+  return w;
 }
 
 // o, to: [B, H, Nq, D] in fp32 (kOutBf16 false) or bf16; lse, tlse: [B, H, Nq]
@@ -443,9 +589,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
   // Buffer descriptors over whole tensors (see Extents); a NULL tq reads zeros.
   const auto rq = make_rsrc(q, ext.q_bytes);
   const auto rtq = make_rsrc(tq, tq != nullptr ? ext.q_bytes : 0u);
-  // the workspace descriptor spans this (b, h) slice's tile images only
-  const uint32_t slice_bytes = (uint32_t)ntiles * G::kImgBytes;
-  const auto rimg = make_rsrc(img + (size_t)bh * slice_bytes, slice_bytes);
+  // the workspace descriptor spans this (b, h) slice's tile images and header
+  const uint32_t sb = slice_bytes<D, M::kKV>(ntiles);
+  const auto rimg = make_rsrc(img + (size_t)bh * sb, sb);
+  const uint32_t hdr = (uint32_t)ntiles * G::kImgBytes;
 
   // Copy of tile image kt into a stage: this wave's kDmaPerWave consecutive
   // KiB, lane l moving bytes 16 l .. 16 l + 15 of each (LDS address = the
@@ -470,6 +617,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
     dqf[ks] = buf_load16(rtq, off);
   }
 
+  const WaveScale sc = wave_scale<D, M::kKV>(rimg, hdr, qf, dqf, scale);
+
   RowState<D> st;
 #pragma unroll
   for (int cb = 0; cb < G::kCB; ++cb) {
@@ -483,31 +632,40 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
   // Tile kt is computed from stage (kt - t0) % 2 while tile kt + 1 is copied
   // into the other stage; the wait for the copies and the barrier at the end
   // of each tile make tile kt + 1 visible to every wave and retire every read
-  // of the stage the next copy overwrites.
+  // of the stage the next copy overwrites.  Both forms of the loop (with and
+  // without the dV^T rescale) run the same barriers.
   const int kLast = t1 - 1;
   auto finish_tile = [&]() {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  finish_tile();
-  for (int kt = t0; kt < kLast; ++kt) {
-    const int sc = (kt - t0) & 1;
-    tile_step<D, kMode>(smem + (sc ^ 1) * G::kImgBytes, smem + sc * G::kImgBytes,
-                        [&](char* next, int j) { copy_one(kt + 1, next, j); }, st, qf, dqf, l32,
-                        g, Nk, c_log2, scale);
+  auto key_loop = [&](auto scale_dv) {
+    constexpr bool kS = decltype(scale_dv)::value;
     finish_tile();
-  }
-  // last tile of the range: keys past Nk are masked (the tile image holds
-  // zeros there; in a range that ends before the last tile nothing is masked)
-  {
+    for (int kt = t0; kt < kLast; ++kt) {
+      const int cs = (kt - t0) & 1;
+      tile_step<D, kMode, kS>(smem + (cs ^ 1) * G::kImgBytes, smem + cs * G::kImgBytes,
+                              [&](char* next, int j) { copy_one(kt + 1, next, j); }, st, qf, dqf,
+                              l32, g, Nk, c_log2, sc.s_t, sc.dv_mul);
+      finish_tile();
+    }
+    // last tile of the range: keys past Nk are masked (the tile image holds
+    // zeros there; in a range that ends before the last tile nothing is masked)
     const char* cur = smem + ((kLast - t0) & 1) * G::kImgBytes;
     const int kl = kLast * kBC;
     auto none = [](int) {};
-    jvp_block<D, kMode, true>(st, cur, 0, qf, dqf, l32, g, kl, Nk, c_log2, scale, none);
-    jvp_block<D, kMode, true>(st, cur, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, scale, none);
-  }
+    jvp_block<D, kMode, true, kS>(st, cur, 0, qf, dqf, l32, g, kl, Nk, c_log2, sc.s_t,
+                                  sc.dv_mul, none);
+    jvp_block<D, kMode, true, kS>(st, cur, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, sc.s_t,
+                                  sc.dv_mul, none);
+  };
+  if (M::kKV && sc.slow)
+    key_loop(Flag<M::kKV>{});
+  else
+    key_loop(Flag<false>{});
 
-  jvp_epilogue<D, kOutBf16>(st, obh, row, Nq, g, o, to, lse, tlse, ext);
+  jvp_epilogue<D, kOutBf16>(st, obh, row, Nq, g, o, to, lse, tlse, ext, sc.ev, sc.ev + sc.t,
+                            sc.t);
 }
 
 // ---- short key ranges: 128-row workgroups, one LDS stage, two per CU ----
@@ -558,8 +716,9 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
 
   const auto rq = make_rsrc(q, ext.q_bytes);
   const auto rtq = make_rsrc(tq, tq != nullptr ? ext.q_bytes : 0u);
-  const uint32_t slice_bytes = (uint32_t)ntiles * G::kImgBytes;
-  const auto rimg = make_rsrc(img + (size_t)bh * slice_bytes, slice_bytes);
+  const uint32_t sb = slice_bytes<D, M::kKV>(ntiles);
+  const auto rimg = make_rsrc(img + (size_t)bh * sb, sb);
+  const uint32_t hdr = (uint32_t)ntiles * G::kImgBytes;
 
   // Copy of tile image kt into the stage: this wave's quarter, 1 KiB per
   // instruction, lane l moving bytes 16 l .. 16 l + 15 of each KiB.
@@ -582,6 +741,8 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
     dqf[ks] = buf_load16(rtq, off);
   }
 
+  const WaveScale sc = wave_scale<D, M::kKV>(rimg, hdr, qf, dqf, scale);
+
   RowState<D> st;
 #pragma unroll
   for (int cb = 0; cb < G::kCB; ++cb) {
@@ -594,29 +755,40 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
 
   // Tile kt: wait for its copy (every wave's share) and make it visible, compute
   // both blocks, then a barrier retires every read of the stage before the
-  // copy of tile kt + 1 overwrites it.
+  // copy of tile kt + 1 overwrites it.  Both forms of the loop (with and
+  // without the dV^T rescale) run the same barriers.
   auto none = [](int) {};
   auto tile_ready = [&]() {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   const int kLast = t1 - 1;
-  for (int kt = t0; kt < kLast; ++kt) {
-    tile_ready();
-    jvp_block<D, kMode, false>(st, smem, 0, qf, dqf, l32, g, 0, Nk, c_log2, scale, none);
-    jvp_block<D, kMode, false>(st, smem, 1, qf, dqf, l32, g, 0, Nk, c_log2, scale, none);
-    __syncthreads();
+  auto key_loop = [&](auto scale_dv) {
+    constexpr bool kS = decltype(scale_dv)::value;
+    for (int kt = t0; kt < kLast; ++kt) {
+      tile_ready();
+      jvp_block<D, kMode, false, kS>(st, smem, 0, qf, dqf, l32, g, 0, Nk, c_log2, sc.s_t,
+                                     sc.dv_mul, none);
+      jvp_block<D, kMode, false, kS>(st, smem, 1, qf, dqf, l32, g, 0, Nk, c_log2, sc.s_t,
+                                     sc.dv_mul, none);
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) copy_one(kt + 1, smem, j);
-  }
-  tile_ready();
-  {
+      for (int j = 0; j < kPer; ++j) copy_one(kt + 1, smem, j);
+    }
+    tile_ready();
     const int kl = kLast * kBC;
-    jvp_block<D, kMode, true>(st, smem, 0, qf, dqf, l32, g, kl, Nk, c_log2, scale, none);
-    jvp_block<D, kMode, true>(st, smem, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, scale, none);
-  }
+    jvp_block<D, kMode, true, kS>(st, smem, 0, qf, dqf, l32, g, kl, Nk, c_log2, sc.s_t,
+                                  sc.dv_mul, none);
+    jvp_block<D, kMode, true, kS>(st, smem, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, sc.s_t,
+                                  sc.dv_mul, none);
+  };
+  if (M::kKV && sc.slow)
+    key_loop(Flag<M::kKV>{});
+  else
+    key_loop(Flag<false>{});
 
-  jvp_epilogue<D, kOutBf16>(st, obh, row, Nq, g, o, to, lse, tlse, ext);
+  jvp_epilogue<D, kOutBf16>(st, obh, row, Nq, g, o, to, lse, tlse, ext, sc.ev, sc.ev + sc.t,
+                            sc.t);
 }
 
 // ---- forward attention alone (O, lse) ----
@@ -768,8 +940,10 @@ __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kerne
   const int row0 = qt * fwd_rows<RB>() + wave * 32 * RB + l32;  // block rb: row0 + 32 rb
 
   const auto rq = make_rsrc(q, ext.q_bytes);
-  const uint32_t slice_bytes = (uint32_t)ntiles * G::kImgBytes;
-  const auto rimg = make_rsrc(img + (size_t)bh * slice_bytes, slice_bytes);
+  const uint32_t sb = slice_bytes<D, false>(ntiles);
+  const auto rimg = make_rsrc(img + (size_t)bh * sb, sb);
+  // V's fp16 exponent (slice header): the accumulators hold A 2^eV
+  const u32x4 rec = buf_load16(rimg, (uint32_t)ntiles * G::kImgBytes + kHdrRecord);
   const uint32_t wave_part = (uint32_t)wave * G::kDmaPerWave * kDmaBytes;
   auto copy_one = [&](int kt, char* stage, int j) {
     const uint32_t src = (uint32_t)kt * G::kImgBytes + wave_part + j * kDmaBytes;
@@ -818,11 +992,12 @@ __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kerne
   }
 
   const auto ro = make_rsrc(o, ext.o_bytes);
+  const int ev = __builtin_amdgcn_readfirstlane((int)rec[0]);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int row = row0 + 32 * rb;
     const float l = halves_sum(st.l[rb]);
-    const float inv_l = 1.0f / l;
+    const float inv_l = __builtin_amdgcn_ldexpf(1.0f / l, -ev);
     if (row < Nq) {
       const uint32_t orow = (obh * (uint32_t)Nq + row) * D;
 #pragma unroll
@@ -855,6 +1030,10 @@ hipError_t launch_pack_d(const void* k, const void* v, const void* tk, const voi
   const int ntiles = (Nk + kBC - 1) / kBC;
   const int bh = B * H;
   const uint32_t kv_bytes = (uint32_t)((size_t)bh * Nk * D * 2);
+  const hipError_t e = launch_range_stats<D>(v, kKV ? tv : nullptr, ws, bh, Nk,
+                                             slice_bytes<D, kKV>(ntiles),
+                                             (uint32_t)ntiles * Geo<D, kKV>::kImgBytes, stream);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((pack_kv_kernel<D, kKV>), dim3(ntiles, bh), dim3(kPackThreads), 0, stream,
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      static_cast<const uint16_t*>(tk), static_cast<const uint16_t*>(tv),
@@ -919,9 +1098,11 @@ hipError_t launch_pack(bool kv_tangents, const void* k, const void* v, const voi
 using namespace bf16_path;
 
 size_t bf16_workspace_bytes(int B, int H, int Nk, int d) {
+  // tile images and header of every slice, in the full (dK, dV) layout; the
+  // modes without dK, dV lay out smaller slices in the same space
   const size_t ntiles = ((size_t)Nk + kBC - 1) / kBC;
   const size_t img = d == 128 ? Geo<128, true>::kImgBytes : Geo<64, true>::kImgBytes;
-  return (size_t)B * H * ntiles * img;
+  return (size_t)B * H * (ntiles * img + kHdrBytes);
 }
 
 hipError_t launch_pack_kv(const void* k, const void* v, const void* tk, const void* tv, int B,

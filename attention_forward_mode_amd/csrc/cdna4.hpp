@@ -86,6 +86,17 @@ __device__ inline uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// Eight fp16 values times the fp16 pair in m (both halves equal), rounded to
+// nearest even (packed fp16 multiplies).  Note: every __builtin_bit_cast here
+// takes a whole vector or a scalar value; applied to an element of an
+// ext_vector_type variable (x[i] as an lvalue) this compiler reads element 0
+// whatever i is, so an element is first copied to a scalar.
+__device__ inline u32x4 mul_f16x8(u32x4 x, uint32_t m) {
+  const f16x2 mm = __builtin_bit_cast(f16x2, m);
+  const f16x8 s = {mm[0], mm[0], mm[0], mm[0], mm[0], mm[0], mm[0], mm[0]};
+  return __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, x) * s);
+}
+
 // acc + h.x + h.y for a register of two fp16 (products with 1.0 are exact;
 // the sum is formed in fp32).
 __device__ inline float add_f16x2(uint32_t h, float acc) {

@@ -1,0 +1,227 @@
+// range.hpp -- power-of-two scalings that keep the fp16 operands of the
+// matrix-core products inside fp16's range (gfx950 device helpers).
+//
+// The second contraction of the forward pass (P and s P dS against V and dV)
+// and the products of the backward pass run on fp16 operands, which hold 11
+// significant bits but only magnitudes from 2^-24 to 65504; bf16 inputs span
+// 2^-133 .. 3.4e38.  Multiplying an operand by a power of two is exact in
+// binary floating point (short of overflow and underflow), so each operand
+// family is scaled by 2^e into fp16's upper range and the result is scaled
+// back by 2^-e in fp32: the products, sums and roundings in between are those
+// of the unscaled values, moved by whole binades.
+//   - a tensor of the inputs (V, dV; Q, gO, K in the backward pass) gets one
+//     exponent per (b, h) slice from its largest finite magnitude, found by a
+//     reduction pass before the pack;
+//   - a per-element product formed in the kernel (s P dS; the backward's
+//     softmax gradient) gets its exponent from an upper bound of its
+//     magnitude (Cauchy-Schwarz on row norms) computed before the key loop.
+// Non-finite inputs are left out of the maxima, so they stay Inf or NaN in
+// fp16 and propagate through the products as they would unscaled.
+#pragma once
+
+#include "cdna4.hpp"
+
+namespace ajvp {
+
+// Largest finite |x| among the eight bf16 values of a 16-byte chunk, as bf16
+// magnitude bits (the bit patterns of non-negative bf16 values order like
+// their values; exponent field 0xff = Inf or NaN is left out).
+__device__ inline uint32_t finite_absmax8(u32x4 x) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = x[w] & 0x7fffu, hi = (x[w] >> 16) & 0x7fffu;
+    m = lo < 0x7f80u && lo > m ? lo : m;
+    m = hi < 0x7f80u && hi > m ? hi : m;
+  }
+  return m;
+}
+
+// The exponent e that puts a largest magnitude given as bf16 bits into
+// [2^14, 2^15) after multiplying by 2^e (below fp16's 65504, so every scaled
+// value of the tensor converts without overflow); 0 when the tensor is zero.
+__device__ inline int fp16_exponent(uint32_t absbits) {
+  if (absbits == 0) return 0;
+  int e;
+  __builtin_frexpf(__builtin_bit_cast(float, absbits << 16), &e);  // max = f 2^e, f in [0.5, 1)
+  return 15 - e;
+}
+
+// Bound on |s P dS| or |gS| after scaling, with P <= 2^4 (the forward pass's
+// lazy rescale keeps p <= 16): 16 * 4000 = 64000 < 65504, the largest fp16.
+constexpr double kProdSafe = 4000.0;
+
+// The largest t with bound * 2^t <= kProdSafe, clamped to [-150, 100] (a bound
+// of 0 or NaN gives 0, an infinite one -150).
+__device__ inline int product_exponent(double bound) {
+  if (!(bound > 0.0)) return 0;
+  if (bound > 1.0e300) return -150;
+  int e;
+  __builtin_frexp(kProdSafe / bound, &e);  // = f 2^e, f in [0.5, 1): floor(log2) = e - 1
+  const int t = e - 1;
+  return t < -150 ? -150 : (t > 100 ? 100 : t);
+}
+
+// Sum of squares of the eight bf16 values of a 16-byte chunk, in fp64 (exact
+// products; no overflow for any finite bf16).
+__device__ inline double sumsq8(u32x4 x) {
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const double lo = (double)__builtin_bit_cast(float, x[w] << 16);
+    const double hi = (double)__builtin_bit_cast(float, x[w] & 0xffff0000u);
+    s = __builtin_fma(lo, lo, s);
+    s = __builtin_fma(hi, hi, s);
+  }
+  return s;
+}
+
+// fp64 value of lane l and lane l ^ 32 summed, in every lane.
+__device__ inline double halves_sum_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  const double x0 = __builtin_bit_cast(double, ((uint64_t)(uint32_t)b[0] << 32) | (uint32_t)a[0]);
+  const double x1 = __builtin_bit_cast(double, ((uint64_t)(uint32_t)b[1] << 32) | (uint32_t)a[1]);
+  return x0 + x1;
+}
+
+// Maximum over the 64 lanes of a wave (NaN lanes are ignored: fmax).
+__device__ inline double wave_max_f64(double x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = __shfl_xor((uint32_t)u, m), hi = __shfl_xor((uint32_t)(u >> 32), m);
+    x = __builtin_fmax(x, __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo));
+  }
+  return x;
+}
+__device__ inline uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const uint32_t y = __shfl_xor(x, m);
+    x = y > x ? y : x;
+  }
+  return x;
+}
+__device__ inline float wave_max_f32(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = __builtin_fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+// fp32 value not below the fp64 x (x >= 0): rounded to nearest, then raised by
+// 2^-20 relative, more than the rounding can have taken off.
+__device__ inline float round_up_f32(double x) { return (float)(x * (1.0 + 0x1p-20)); }
+
+// ---- the per-slice header of a packed workspace -------------------------------
+// Each (b, h) slice of a packed workspace (tile images of 64 rows of one
+// side, keys or queries) ends with a header of kHdrBytes:
+//   +kHdrRecord  the slice's fp16 exponents (int, up to four) and flags
+//   +kHdrNorms   two fp32 maxima of row norms (rounded up), raised by the
+//                pack's workgroups with integer atomics (the bit patterns of
+//                non-negative floats order like their values) after the
+//                range pass has zeroed them
+//   +kHdrStats   the range pass's partial maxima, per chunk of rows: uint max
+//                finite |x| and |y| as bf16 magnitude bits
+constexpr int kHdrRecord = 0;
+constexpr int kHdrNorms = 16;
+constexpr int kHdrStats = 256;
+constexpr int kStatChunks = 64;
+constexpr int kHdrBytes = 1024;
+static_assert(kHdrStats + 8 * kStatChunks <= kHdrBytes, "header layout");
+constexpr int kStatThreads = 256;
+
+__host__ __device__ constexpr int stat_chunks(int ntiles) {
+  return ntiles < kStatChunks ? ntiles : kStatChunks;
+}
+
+// Largest finite |x| and |y| (y NULL: 0) over one chunk of rows (blockIdx.x;
+// the ntiles 64-row tiles are cut into stat_chunks(ntiles) contiguous chunks)
+// of slice blockIdx.y of [slices, N, D] bf16 tensors of in_bytes bytes,
+// written to the header of that slice (at ws + slice * slice_bytes + hdr).
+// Chunk 0 also zeroes the header's norm words.
+template <int D>
+__global__ __launch_bounds__(kStatThreads) void range_stats_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ y, char* __restrict__ ws,
+    int N, int ntiles, uint32_t in_bytes, uint32_t slice_bytes, uint32_t hdr) {
+  const int nch = stat_chunks(ntiles), c = blockIdx.x;
+  const uint32_t bh = blockIdx.y;
+  const int tpc = (ntiles + nch - 1) / nch;
+  const int r0 = c * tpc * 64, r1 = r0 + tpc * 64 < N ? r0 + tpc * 64 : N;
+  const auto rws = make_rsrc(ws + (size_t)bh * slice_bytes, slice_bytes);
+  const auto rx = make_rsrc(x, in_bytes);
+  const auto ry = make_rsrc(y, y != nullptr ? in_bytes : 0u);
+  uint32_t mx = 0, my = 0;
+  if (r1 > r0) {
+    const uint32_t base = (bh * (uint32_t)N + r0) * D * 2, n = (uint32_t)(r1 - r0) * D * 2;
+    constexpr uint32_t kStep = kStatThreads * 16;
+    uint32_t off = threadIdx.x * 16;
+    for (; off + 3 * kStep < n; off += 4 * kStep) {  // four loads in flight per tensor
+      u32x4 a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = buf_load16(rx, base + off + u * kStep);
+        b[u] = buf_load16(ry, base + off + u * kStep);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t ma = finite_absmax8(a[u]), mb = finite_absmax8(b[u]);
+        mx = ma > mx ? ma : mx;
+        my = mb > my ? mb : my;
+      }
+    }
+    for (; off < n; off += kStep) {
+      const uint32_t ma = finite_absmax8(buf_load16(rx, base + off));
+      const uint32_t mb = finite_absmax8(buf_load16(ry, base + off));
+      mx = ma > mx ? ma : mx;
+      my = mb > my ? mb : my;
+    }
+  }
+  mx = wave_max_u32(mx);
+  my = wave_max_u32(my);
+  __shared__ uint32_t sm[2][kStatThreads / 64];
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm[0][w] = mx;
+    sm[1][w] = my;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < kStatThreads / 64; ++i) {
+      mx = sm[0][i] > mx ? sm[0][i] : mx;
+      my = sm[1][i] > my ? sm[1][i] : my;
+    }
+    buf_store8(rws, hdr + kHdrStats + 8 * c, u32x2{mx, my});
+    if (c == 0) buf_store8(rws, hdr + kHdrNorms, u32x2{0u, 0u});
+  }
+}
+
+template <int D>
+inline hipError_t launch_range_stats(const void* x, const void* y, void* ws, int slices, int N,
+                                     uint32_t slice_bytes, uint32_t hdr, hipStream_t stream) {
+  const int ntiles = (N + 63) / 64;
+  hipLaunchKernelGGL((range_stats_kernel<D>), dim3(stat_chunks(ntiles), slices),
+                     dim3(kStatThreads), 0, stream, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(y), static_cast<char*>(ws), N, ntiles,
+                     (uint32_t)((size_t)slices * N * D * 2), slice_bytes, hdr);
+  return hipGetLastError();
+}
+
+// The range pass's maxima of one slice, reduced by one wave from its partial
+// maxima: every lane returns max |x| and max |y| as bf16 magnitude bits.
+__device__ inline void slice_maxima(__amdgpu_buffer_rsrc_t rws, uint32_t hdr, int ntiles,
+                                    int lane, uint32_t& mx, uint32_t& my) {
+  mx = 0;
+  my = 0;
+  if (lane < stat_chunks(ntiles)) {
+    const int o = (int)(hdr + kHdrStats + 8 * lane);
+    mx = __builtin_amdgcn_raw_buffer_load_b32(rws, o, 0, 0);
+    my = __builtin_amdgcn_raw_buffer_load_b32(rws, o + 4, 0, 0);
+  }
+  mx = wave_max_u32(mx);
+  my = wave_max_u32(my);
+}
+
+}  // namespace ajvp

@@ -34,12 +34,21 @@
  * Precision.  attn_jvp_fwd takes bf16 inputs (uint16 storage holding IEEE
  * bfloat16 bit patterns); all products are formed on bf16/fp16 matrix cores
  * with fp32 accumulation, and O, dO and lse are written in fp32.  The second
- * contraction (P and P*dS against V and dV) runs on fp16 operands: V and dV
- * are converted exactly (bf16 -> fp16 is exact for 2^-14 <= |x| < 65504; smaller
- * magnitudes round to fp16 subnormals), P and P*dS are rounded to nearest.
- * An input outside fp16 range, or |scale * dS| beyond about 4000, overflows to
- * a non-finite output rather than a wrong finite one.  attn_jvp_fwd_f32 takes
- * fp32 inputs and computes in fp32 throughout.  NaN/Inf inputs propagate.
+ * contraction (P and s P dS against V and dV) runs on fp16 operands, kept
+ * inside fp16's range by powers of two that are undone exactly in fp32: V and
+ * dV are multiplied by 2^e per (b, h) slice, e chosen from the slice's largest
+ * finite |V| (|dV|), so the conversion is exact apart from magnitudes below
+ * 2^-29 of that largest one; s P dS is multiplied by 2^t per group of 32 query
+ * rows, t chosen from an upper bound of |s dS| (Cauchy-Schwarz on the norms of
+ * the rows of Q, dQ and the keys of K, dK), then rounded to nearest like P.
+ * So every finite bf16 input is in range; what bounds the domain is fp32
+ * itself: the logits s q.k, s dS and the results must be finite in fp32.
+ * Scaling (V, dV) by a power of two scales O and dO by it exactly, and so does
+ * scaling every tangent for dO and the tangent of lse.  attn_jvp_fwd_f32 takes
+ * fp32 inputs and computes in fp32 throughout.  NaN and Inf inputs propagate:
+ * an output is NaN or Inf where the exact result is (e.g. a NaN in row i of Q
+ * or dQ reaches row i of the outputs only, a NaN in column c of V or dV column
+ * c of O and dO).
  *
  * Ownership and streams.  All tensor pointers are DEVICE pointers owned by the
  * caller, on the current HIP device.  Outputs must not alias inputs or each
@@ -52,8 +61,8 @@
  * Errors.  Argument errors are detected before anything is launched and leave
  * every output untouched:
  *   ATTN_JVP_EINVAL       a required pointer is NULL; B, H, Nq or Nk < 1;
- *                         `scale` is negative, NaN or infinite; the workspace
- *                         is NULL or too small
+ *                         `scale` is NaN or infinite; the workspace is NULL
+ *                         or too small
  *   ATTN_JVP_EUNSUPPORTED d is not 64 or 128; one (b, h) slice of a tensor
  *                         reaches 2^31 bytes (counted as fp32: Nq*d*4 or
  *                         Nk*d*4), or one slice of the bf16 path's tile images
@@ -102,7 +111,7 @@ typedef struct ihipStream_t *attn_jvp_stream_t;
  *   lse         output row log-sum-exp, fp32 [B, H, Nq]; may be NULL (not written)
  *   B, H        batch and head counts; Nq, Nk query and key lengths (any >= 1;
  *               Nq != Nk is cross-attention); d = 64 or 128
- *   scale       softmax scale s >= 0 (typically 1/sqrt(d))
+ *   scale       softmax scale s, any finite value (typically 1/sqrt(d))
  *   stream      HIP stream for every launch
  * Allocates a workspace of attn_jvp_workspace_bytes(B, H, Nk, d) bytes from a
  * library-owned stream-ordered pool and frees it stream-ordered.
@@ -115,12 +124,13 @@ ATTN_JVP_API int attn_jvp_fwd(const void *q, const void *k, const void *v,
                  attn_jvp_stream_t stream);
 
 /*
- * Bytes of workspace the bf16 path needs for these sizes: one 64-key tile
- * image per (b, h) and key tile, holding K and dK (bf16) and V^T and dV^T
- * (fp16) as the sequence of matrix-core operand fragments the fused kernel
- * reads, laid out byte for byte as it holds them in LDS (64 KiB per tile at
- * d = 128, 32 KiB at d = 64); 0 if a size is invalid.  Same operation as
- * attn_jvp_fwd.
+ * Bytes of workspace the bf16 path needs for these sizes: per (b, h), one
+ * 64-key tile image per key tile, holding K and dK (bf16) and V^T and dV^T
+ * (fp16, scaled by the slice's powers of two) as the sequence of matrix-core
+ * operand fragments the fused kernel reads, laid out byte for byte as it holds
+ * them in LDS (64 KiB per tile at d = 128, 32 KiB at d = 64), then a 1 KiB
+ * header (the powers of two, the partial maxima they come from and the largest
+ * key norms); 0 if a size is invalid.  Same operation as attn_jvp_fwd.
  */
 ATTN_JVP_API size_t attn_jvp_workspace_bytes(int B, int H, int Nk, int d);
 

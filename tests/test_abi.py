@@ -53,15 +53,18 @@ def test_strerror():
 
 
 def test_workspace_bytes():
-    # one tile image per (b, h) and 64-key tile: K, dK (64 x d bf16) and V^T,
-    # dV^T (d x 64 fp16), unpadded operand fragments, a whole number of 8 KiB
+    # per (b, h): one tile image per 64-key tile (K, dK as 64 x d bf16 and V^T,
+    # dV^T as d x 64 fp16, unpadded operand fragments, a whole number of
+    # 8 KiB), then a 1 KiB header (the fp16 exponents, the largest key norms
+    # and the range pass's partial maxima)
     def img(d):
         used = 2 * 64 * d * 2 + 2 * d * 64 * 2
         return -(-used // 8192) * 8192
+    hdr = 1024
     assert img(128) == 64 * 1024 and img(64) == 32 * 1024
-    assert ajvp.attn_jvp_workspace_bytes(1, 1, 1, 128) == img(128)
-    assert ajvp.attn_jvp_workspace_bytes(1, 12, 32760, 128) == 12 * 512 * img(128)
-    assert ajvp.attn_jvp_workspace_bytes(2, 3, 65, 64) == 6 * 2 * img(64)
+    assert ajvp.attn_jvp_workspace_bytes(1, 1, 1, 128) == img(128) + hdr
+    assert ajvp.attn_jvp_workspace_bytes(1, 12, 32760, 128) == 12 * (512 * img(128) + hdr)
+    assert ajvp.attn_jvp_workspace_bytes(2, 3, 65, 64) == 6 * (2 * img(64) + hdr)
     assert ajvp.attn_jvp_workspace_bytes(0, 1, 1, 128) == 0
     assert ajvp.attn_jvp_workspace_bytes(1, 1, 1, 96) == 0
 
@@ -115,7 +118,8 @@ def test_bad_sizes(fn):
 
 @pytest.mark.parametrize("fn", FNS)
 def test_bad_scale(fn):
-    for s in (float("nan"), float("inf"), -float("inf"), -0.5):
+    # any finite scale is valid (a negative one too); NaN and +-Inf are not
+    for s in (float("nan"), float("inf"), -float("inf")):
         assert _call(fn, scale=s) == EINVAL, s
 
 
@@ -203,7 +207,7 @@ def test_fwd_packed_rejects_bad_arguments():
         p[i] = 0
         assert _packed(p) == EINVAL, i
     assert _packed(ws=0) == EINVAL and _packed(ws_bytes=100) == EINVAL
-    assert _packed(scale=-1.0) == EINVAL and _packed(scale=float("nan")) == EINVAL
+    assert _packed(scale=float("inf")) == EINVAL and _packed(scale=float("nan")) == EINVAL
     assert _packed(Nq=0) == EINVAL
     assert _packed(d=64 + 1) == EUNSUPPORTED and _packed(Nk=1 << 24) == EUNSUPPORTED
     for i in range(4):
@@ -278,7 +282,7 @@ def test_attn_fwd_rejects_bad_arguments():
         p = [A + j * 0x100000 for j in range(5)]
         p[i] = 0
         assert _fwd(p) == EINVAL, i
-    assert _fwd(out_dtype=3) == EINVAL and _fwd(scale=-1.0) == EINVAL
+    assert _fwd(out_dtype=3) == EINVAL and _fwd(scale=-float("inf")) == EINVAL
     assert _fwd(d=32) == EUNSUPPORTED and _fwd(B=1 << 16, H=1 << 16) == EUNSUPPORTED
     p = [A + j * 0x100000 for j in range(5)]
     p[3] += 4
