@@ -8,24 +8,35 @@
 // (rCM record LIT-783 in the Anthology of the SOTA: the student is trained
 // through the attention output, "Key takeaways", "JVP at production scale".)
 //
-// Four kernels per call, all on one stream:
+// Kernels per call, all on one stream:
+//  0. range_stats (range.hpp), twice: per (b, h) the largest finite |Q|, |gO|
+//     and |K|, from which the packs take per-slice powers of two 2^eQ, 2^eG,
+//     2^eK that put Q^T, gO^T and K^T into fp16's upper range.
 //  1. pack_q: per 64 queries, a tile image of Q and gO rows (bf16, padded),
-//     Q^T and gO^T (fp16, [d][64 queries] in matrix-core operand order), and
-//     per query lse (+inf past Nq) and D = <gO_i, O_i> (fp32, from O).
-//  2. pack_k: per 64 keys, a tile image of K and V rows (bf16) and K^T (fp16).
+//     Q^T 2^eQ and gO^T 2^eG (fp16, [d][64 queries] in matrix-core operand
+//     order), and per query lse (+inf past Nq) and D = <gO_i, O_i> (fp32, from
+//     O); the slice's largest |gO_i| and |D_i| go to its header.
+//  2. pack_k: per 64 keys, a tile image of K and V rows (bf16) and K^T 2^eK
+//     (fp16); the slice's largest |v_j| goes to its header.
 //  3. bwd_kv: one workgroup = 8 waves x 32 keys (K, V fragments held in
 //     registers); it streams the query tiles (direct-to-LDS copies, double
 //     buffered) and per 32-query block forms S = Q K^T and gP = gO V^T (bf16
-//     MFMA), P = exp(S - lse), gS = P (gP - D) (rounded to fp16 pairs), and
-//     accumulates gV^T += gO^T P and gK^T += Q^T gS (fp16 MFMA).
+//     MFMA), P = exp(S - lse), gS 2^t = P 2^t (gP - D) (rounded to fp16
+//     pairs), and accumulates gV^T += gO^T P and gK^T += Q^T gS (fp16 MFMA).
 //  4. bwd_q: one workgroup = 8 waves x 32 queries (Q, gO fragments held in
 //     registers); it streams the key tiles and per 32-key block forms
-//     S^T = K Q^T, gP^T = V gO^T, P^T, gS^T, and accumulates gQ^T += K^T gS^T.
+//     S^T = K Q^T, gP^T = V gO^T, P^T, gS^T 2^t, and accumulates
+//     gQ^T += K^T gS^T.
+// The tangent-free analogue of the forward's s P dS scaling: with P <= 1,
+// |gS_ij| <= |gO_i| |v_j| + |D_i| (Cauchy-Schwarz), and each wave takes t
+// from that bound over its keys (bwd_kv) or its queries (bwd_q) so that gS 2^t
+// stays below 4000; the stores undo 2^t and the image exponents exactly.
 // Every access to global memory is a buffer access range-checked against its
 // tensor (or one (b, h) slice of the workspace).  Products: 8 (bwd_kv) + 6
 // (bwd_q) Nq x Nk x d contractions' worth of flops, S and gP formed twice.
 #include "cdna4.hpp"
 #include "launch.hpp"
+#include "range.hpp"
 
 namespace ajvp {
 namespace bwd_path {
@@ -76,9 +87,23 @@ __device__ __attribute__((always_inline)) inline int slot_row(int r, int g) {
   return 8 * (r >> 2) + 4 * g + (r & 3);
 }
 
+// Bytes of one (b, h) slice of the query-side (kQuery) or key-side workspace:
+// its tile images, then the header of range.hpp.  Query side: record =
+// {eQ, eG}, norm maxima = {max_i |gO_i|, max_i |D_i|}; key side: record =
+// {eK}, norm maxima = {max_j |v_j|, 0}.
+template <int D, bool kQuery>
+__host__ __device__ constexpr uint32_t slice_bytes(int ntiles) {
+  using G = Img<D, 2, kQuery ? 2 : 1, kQuery ? 2 * kTile * 4 : 0>;
+  return (uint32_t)ntiles * G::kBytes + kHdrBytes;
+}
+
 // One tile image (blockIdx.x = tile, blockIdx.y = (b, h)).  Rows past N are
 // zero; with kQuery, the extras are lse (+inf past N) and D = <gO_i, O_i>,
 // 32 floats per 32-row block in slot order (lane half g, slot r at 16 g + r).
+// The transposed tiles hold t0 2^e0 and t1 2^e1 in fp16, e0, e1 from the
+// range pass's maxima of t0, t1 (which every wave reduces itself); the
+// workgroup of tile 0 writes them to the slice header, and every tile raises
+// the header's maxima of |r1 row| and (kQuery) |D| to its own.
 template <int D, bool kQuery>
 __device__ __attribute__((always_inline)) inline void pack_body(
     const uint16_t* __restrict__ r0, const uint16_t* __restrict__ r1,
@@ -89,18 +114,24 @@ __device__ __attribute__((always_inline)) inline void pack_body(
   constexpr int NT = kQuery ? 2 : 1;
   __shared__ _Float16 sv[NT][kTile][D + 2];
   __shared__ float sd[kTile];
+  __shared__ double sn[kTile];
   const int tile = blockIdx.x;
   const uint32_t bh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
   const auto rr0 = make_rsrc(r0, in_bytes);
   const auto rr1 = make_rsrc(r1, in_bytes);
   const auto rt0 = make_rsrc(t0, in_bytes);
   const auto rt1 = make_rsrc(t1, kQuery ? in_bytes : 0u);
-  const uint32_t slice = (uint32_t)ntiles * G::kBytes;
+  const uint32_t slice = slice_bytes<D, kQuery>(ntiles);
+  const uint32_t hdr = (uint32_t)ntiles * G::kBytes;
   const auto rws = make_rsrc(ws + (size_t)bh * slice, slice);
   const int row0 = tile * kTile;
   const uint32_t img = (uint32_t)tile * G::kBytes;
   constexpr int kC = D / 8;
   constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
+  uint32_t m0, m1;
+  slice_maxima(rws, hdr, ntiles, lane, m0, m1);
+  const int e0 = fp16_exponent(m0), e1 = kQuery ? fp16_exponent(m1) : 0;
   constexpr int kRChunks = kTile * (kC + 1);
   for (int c = threadIdx.x; c < 2 * kRChunks; c += kPackThreads) {
     const int t = c / kRChunks, rem = c % kRChunks, r = rem / (kC + 1), col = rem % (kC + 1);
@@ -112,39 +143,62 @@ __device__ __attribute__((always_inline)) inline void pack_body(
   constexpr int kIn = kTile * kC;
   for (int c = threadIdx.x; c < NT * kIn; c += kPackThreads) {
     const int t = c / kIn, rem = c % kIn, r = rem / kC, col = (rem % kC) * 8;
+    const int e_t = t == 0 ? e0 : e1;
     u32x4 x = kZero;
     if (row0 + r < N)
       x = buf_load16(t == 0 ? rt0 : rt1, ((bh * (uint32_t)N + row0 + r) * D + col) * 2);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t bits = (x[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-      sv[t][r][col + e] = (_Float16)__builtin_bit_cast(float, bits << 16);
+      sv[t][r][col + e] = (_Float16)__builtin_amdgcn_ldexpf(__builtin_bit_cast(float, bits << 16), e_t);
     }
   }
-  if constexpr (kQuery) {
-    // D_i = <gO_i, O_i>: four threads per row, fp32 sums of bf16 gO times fp32 O
-    const auto ro = make_rsrc(o, in_bytes * 2);
-    for (int c = threadIdx.x; c < kTile * 4; c += kPackThreads) {
-      const int r = c / 4, part = c % 4;
-      float acc = 0.f;
-      if (row0 + r < N) {
-        for (int j = part * (D / 4); j < (part + 1) * (D / 4); j += 4) {
-          const uint32_t e = (bh * (uint32_t)N + row0 + r) * D + j;
-          const f32x4 ov = __builtin_bit_cast(f32x4, buf_load16(ro, e * 4));
-          const u32x2 gw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rt1, (int)(e * 2), 0, 0));
+  {
+    // Per row of r1 (gO or V), four threads: the squared norm (fp64) and, with
+    // kQuery, D_i = <gO_i, O_i> (fp32 sums of bf16 gO times fp32 O).
+    static_assert(kTile * 4 == kPackThreads, "one row quarter per thread");
+    const auto ro = make_rsrc(o, kQuery ? in_bytes * 2 : 0u);
+    const int r = threadIdx.x / 4, part = threadIdx.x % 4;
+    float acc = 0.f;
+    double ss = 0.0;
+    if (row0 + r < N) {
+      for (int j = part * (D / 4); j < (part + 1) * (D / 4); j += 4) {
+        const uint32_t e = (bh * (uint32_t)N + row0 + r) * D + j;
+        const u32x2 gw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr1, (int)(e * 2), 0, 0));
+        f32x4 ov = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (kQuery) ov = __builtin_bit_cast(f32x4, buf_load16(ro, e * 4));
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t bits = (gw[q >> 1] >> (16 * (q & 1))) & 0xffffu;
-            acc += __builtin_bit_cast(float, bits << 16) * ov[q];
-          }
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t bits = (gw[q >> 1] >> (16 * (q & 1))) & 0xffffu;
+          const float gv = __builtin_bit_cast(float, bits << 16);
+          if constexpr (kQuery) acc += gv * ov[q];
+          ss = __builtin_fma((double)gv, (double)gv, ss);
         }
       }
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      if (part == 0) sd[r] = acc;
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    if (part == 0) {
+      sd[r] = acc;
+      sn[r] = ss;
     }
   }
   __syncthreads();
+  if (threadIdx.x < 64) {
+    // the tile's largest row norm of r1 and |D| (NaN rows left out: fmax)
+    double nmax = sn[threadIdx.x];
+    float dmax = __builtin_fabsf(sd[threadIdx.x]);
+    nmax = wave_max_f64(nmax);
+    dmax = wave_max_f32(dmax);
+    if (threadIdx.x == 0) {
+      raise_norms(ws + (size_t)bh * slice + hdr, tile, round_up_f32(__builtin_sqrt(nmax)),
+                  kQuery ? dmax : 0.f);
+      if (tile == 0)
+        buf_store16(rws, hdr + kHdrRecord, u32x4{(uint32_t)e0, (uint32_t)e1, 0u, 0u});
+    }
+  }
   for (int c = threadIdx.x; c < NT * D * 9; c += kPackThreads) {
     const int t = c / (D * 9), rem = c % (D * 9), col = rem / 9, p = rem % 9;
     u32x4 x = kZero;
@@ -229,12 +283,13 @@ __device__ __attribute__((always_inline)) inline void load_frags(__amdgpu_buffer
 }
 
 // Store a [D][32] accumulator (4 blocks of 32x32; lane: column l32) as rows
-// of a [N, D] fp32 tensor, times `mul`.
+// of a [N, D] fp32 tensor, times mul 2^-e (the accumulators hold their sums
+// scaled by 2^e; the power of two is applied exactly, after the multiply).
 template <int D>
 __device__ __attribute__((always_inline)) inline void store_rows(__amdgpu_buffer_rsrc_t r,
                                                                  uint32_t row_elem,
                                                                  const f32x16* acc, int g,
-                                                                 float mul) {
+                                                                 float mul, int e) {
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -242,16 +297,36 @@ __device__ __attribute__((always_inline)) inline void store_rows(__amdgpu_buffer
       const int c0 = 32 * cb + 8 * qq + 4 * g;
       f32x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[cb][4 * qq + e] * mul;
+      for (int k = 0; k < 4; ++k) v[k] = __builtin_amdgcn_ldexpf(acc[cb][4 * qq + k] * mul, -e);
       buf_store16(r, (row_elem + c0) * 4, __builtin_bit_cast(u32x4, v));
     }
+}
+
+// The wave's exponent t for gS 2^t from per-lane bounds of |gS| (rows or keys
+// whose bound is not finite hold Inf or NaN inputs and do not take part),
+// capped so that the operand scaled by 2^t (norm `norm` per lane) stays
+// finite in bf16.
+__device__ __attribute__((always_inline)) inline int gs_exponent(double bound, double norm) {
+  const int t = product_exponent(wave_max_f64(__builtin_isfinite(bound) ? bound : 0.0));
+  const int cap = cap_exponent(wave_max_f64(__builtin_isfinite(norm) ? norm : 0.0));
+  return __builtin_amdgcn_readfirstlane(t < cap ? t : cap);
+}
+
+// The row norm of 32 rows held as B-operand fragments (lane: row l32, d-slice
+// g), in fp64, in every lane of the row.
+template <int D>
+__device__ __attribute__((always_inline)) inline double frag_row_norm(const u32x4* f) {
+  double ss = 0.0;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) ss += sumsq8(f[ks]);
+  return __builtin_sqrt(halves_sum_f64(ss));
 }
 
 // ---- bwd_kv: gK, gV for 256 keys per workgroup --------------------------------
 template <int D, bool kMaskQ>
 __device__ __attribute__((always_inline)) inline void kv_block(
     const char* stage, int qb, const u32x4* kf, const u32x4* vf, int l32, int g,
-    f32x16* gk, f32x16* gv, float c_log2) {
+    f32x16* gk, f32x16* gv, float c_log2, float gs_mul) {
   using G = QImg<D>;
   const char* sQ = stage;
   const char* sGO = stage + G::kRTile;
@@ -270,7 +345,8 @@ __device__ __attribute__((always_inline)) inline void kv_block(
     __builtin_amdgcn_sched_barrier(0);
   }
   // P = 2^(S c - lse log2 e) (queries past Nq have lse = +inf, so P = 0 there),
-  // gS = P (gP - D); both rounded to fp16 pairs straight into B operands.
+  // gS 2^t = P (gP 2^t - D 2^t), gP 2^t from the wave's V fragments scaled by
+  // 2^t; both rounded to fp16 pairs straight into B operands.
   u32x4 pb[2], sb[2];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
@@ -281,7 +357,7 @@ __device__ __attribute__((always_inline)) inline void kv_block(
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * q4 + e;
       pp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l4[e]));
-      gs[e] = pp[e] * (gp[r] - d4[e]);
+      gs[e] = pp[e] * __builtin_fmaf(-d4[e], gs_mul, gp[r]);
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -315,11 +391,11 @@ template <int D>
 __device__ __attribute__((always_inline)) inline void kv_tile(
     char* __restrict__ next, const char* __restrict__ cur, __amdgpu_buffer_rsrc_t rimg,
     uint32_t wave_part, int lane, int t_next, bool copy, const u32x4* kf, const u32x4* vf,
-    int l32, int g, f32x16* gk, f32x16* gv, float c_log2) {
+    int l32, int g, f32x16* gk, f32x16* gv, float c_log2, float gs_mul) {
   using G = QImg<D>;
   if (copy) copy_image<G::kDmaPerWave, G::kBytes>(rimg, next, wave_part, lane, t_next);
-  kv_block<D, false>(cur, 0, kf, vf, l32, g, gk, gv, c_log2);
-  kv_block<D, false>(cur, 1, kf, vf, l32, g, gk, gv, c_log2);
+  kv_block<D, false>(cur, 0, kf, vf, l32, g, gk, gv, c_log2, gs_mul);
+  kv_block<D, false>(cur, 1, kf, vf, l32, g, gk, gv, c_log2, gs_mul);
 }
 
 template <int D>
@@ -342,7 +418,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_kernel(
   const int l32 = lane & 31, g = lane >> 5;
   const int key = kt * kRows + wave * 32 + l32;
   const bool key_ok = key < Nk;
-  const uint32_t slice = (uint32_t)nqtiles * G::kBytes;
+  const uint32_t slice = slice_bytes<D, true>(nqtiles);
+  const uint32_t hdr = (uint32_t)nqtiles * G::kBytes;
   const auto rimg = make_rsrc(qimg + (size_t)bh * slice, slice);
   const uint32_t wave_part = (uint32_t)wave * G::kDmaPerWave * kDmaBytes;
   copy_image<G::kDmaPerWave, G::kBytes>(rimg, smem, wave_part, lane, t0);
@@ -350,6 +427,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_kernel(
   const uint32_t krow = (bh * (uint32_t)Nk + key) * D * 2;
   load_frags<D>(make_rsrc(k, sz.k_bytes), krow, key_ok, g, kf);
   load_frags<D>(make_rsrc(v, sz.k_bytes), krow, key_ok, g, vf);
+  // the query side's exponents eQ (Q^T) and eG (gO^T) and maxima of |gO_i|,
+  // |D_i|; t from |gS_ij| <= max|gO_i| |v_j| + max|D_i| over this wave's keys
+  const u32x4 rec = buf_load16(rimg, hdr + kHdrRecord);
+  float mg, md;
+  slice_norms(rimg, hdr, nqtiles, lane, mg, md);
+  const int eq = __builtin_amdgcn_readfirstlane((int)rec[0]);
+  const int eg = __builtin_amdgcn_readfirstlane((int)rec[1]);
+  const double vn = frag_row_norm<D>(vf);
+  const int t = gs_exponent((double)mg * vn + (double)md, vn);
+  const float gs_mul = __builtin_amdgcn_ldexpf(1.0f, t);
+#pragma unroll
+  for (int ks = 0; ks < G::kKS; ++ks) vf[ks] = scale_bf16x8(vf[ks], t);
   f32x16 acc_k[G::kCB], acc_v[G::kCB];
 #pragma unroll
   for (int cb = 0; cb < G::kCB; ++cb) {
@@ -360,17 +449,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_kernel(
   __syncthreads();
   // the copy into the other stage starts once every wave has left the tile
   // that last read it (the barrier at the end of each tile)
-  for (int t = t0; t < t1; ++t) {
-    const int i = t - t0;
+  for (int qt = t0; qt < t1; ++qt) {
+    const int i = qt - t0;
     kv_tile<D>(smem + ((i + 1) & 1) * G::kBytes, smem + (i & 1) * G::kBytes, rimg, wave_part,
-               lane, t + 1, t + 1 < t1, kf, vf, l32, g, acc_k, acc_v, c_log2);
+               lane, qt + 1, qt + 1 < t1, kf, vf, l32, g, acc_k, acc_v, c_log2, gs_mul);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   if (key_ok) {
     const uint32_t row = (bh * (uint32_t)Nk + key) * D;
-    store_rows<D>(make_rsrc(gk + part, sz.ok_bytes), row, acc_k, g, scale);
-    store_rows<D>(make_rsrc(gv + part, sz.ok_bytes), row, acc_v, g, 1.0f);
+    store_rows<D>(make_rsrc(gk + part, sz.ok_bytes), row, acc_k, g, scale, eq + t);
+    store_rows<D>(make_rsrc(gv + part, sz.ok_bytes), row, acc_v, g, 1.0f, eg);
   }
 }
 
@@ -394,7 +483,8 @@ __device__ __attribute__((always_inline)) inline void q_block(
     gp = mma_bf16(va, gof[ks], ks == 0 ? f32x16{} : gp);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // gS^T = P^T (gP^T - D), P^T = 2^(S^T c - lse log2 e); keys past Nk: 0
+  // gS^T 2^t = P^T (gP^T 2^t - D 2^t), P^T = 2^(S^T c - lse log2 e), gP^T 2^t
+  // from the wave's gO fragments scaled by 2^t; keys past Nk: 0
   u32x4 sb[2];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -454,7 +544,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
   const int l32 = lane & 31, g = lane >> 5;
   const int row = qt * kRows + wave * 32 + l32;
   const bool row_ok = row < Nq;
-  const uint32_t slice = (uint32_t)nktiles * G::kBytes;
+  const uint32_t slice = slice_bytes<D, false>(nktiles);
+  const uint32_t khdr = (uint32_t)nktiles * G::kBytes;
   const auto rimg = make_rsrc(kimg + (size_t)bh * slice, slice);
   const uint32_t wave_part = (uint32_t)wave * G::kDmaPerWave * kDmaBytes;
   copy_image<G::kDmaPerWave, G::kBytes>(rimg, smem, wave_part, lane, k0);
@@ -465,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
   // this row's lse and D, from the query image's extras (written by pack_q)
   float lse2 = 0.f, dq = 0.f;
   {
-    const uint32_t qslice = (uint32_t)nqtiles * GQ::kBytes;
+    const uint32_t qslice = slice_bytes<D, true>(nqtiles);
     const auto rq = make_rsrc(qimg + (size_t)bh * qslice, qslice);
     const int in_tile = row % kTile, blk = in_tile / 32, r32 = in_tile % 32;
     // slot of row r32 within its block: r32 = 8(r/4) + 4 gg + r%4
@@ -474,16 +565,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     lse2 = buf_load4f(rq, x);
     dq = buf_load4f(rq, x + 128);
   }
+  // the key side's exponent eK (K^T) and max |v_j|; t from
+  // |gS_ij| <= |gO_i| max|v_j| + |D_i| over this wave's rows
+  const int ek = __builtin_amdgcn_readfirstlane((int)buf_load16(rimg, khdr + kHdrRecord)[0]);
+  float mv, unused;
+  slice_norms(rimg, khdr, nktiles, lane, mv, unused);
+  const double gn = frag_row_norm<D>(gof);
+  const int t = gs_exponent(gn * (double)mv + __builtin_fabs((double)dq), gn);
+#pragma unroll
+  for (int ks = 0; ks < G::kKS; ++ks) gof[ks] = scale_bf16x8(gof[ks], t);
+  dq = __builtin_amdgcn_ldexpf(dq, t);  // D_i 2^t
   f32x16 acc[G::kCB];
 #pragma unroll
   for (int cb = 0; cb < G::kCB; ++cb) acc[cb] = f32x16{};
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int kLast = k1 - 1;
-  for (int t = k0; t < kLast; ++t) {
-    const int i = t - k0;
+  for (int kt = k0; kt < kLast; ++kt) {
+    const int i = kt - k0;
     q_tile<D>(smem + ((i + 1) & 1) * G::kBytes, smem + (i & 1) * G::kBytes, rimg, wave_part,
-              lane, t + 1, qf, gof, l32, g, acc, c_log2, lse2, dq, Nk);
+              lane, kt + 1, qf, gof, l32, g, acc, c_log2, lse2, dq, Nk);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -501,7 +602,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
   }
   if (row_ok)
     store_rows<D>(make_rsrc(gq + part, sz.oq_bytes), (bh * (uint32_t)Nq + row) * D, acc, g,
-                  scale);
+                  scale, ek + t);
 }
 
 // out[i] = sum_s parts[s n + i], i < n (n a multiple of 4); fp32
@@ -542,8 +643,8 @@ Plan plan(int B, int H, int Nq, int Nk) {
   const size_t kbytes = bh * Nk * D * 4, qbytes = bh * Nq * D * 4;
   p.split_kv = pick_split(p.nkw * (int)bh, p.nqt, kbytes);
   p.split_q = pick_split(p.nqw * (int)bh, p.nkt, qbytes);
-  p.qimg = bh * p.nqt * QImg<D>::kBytes;
-  p.kimg = bh * p.nkt * KImg<D>::kBytes;
+  p.qimg = bh * slice_bytes<D, true>(p.nqt);
+  p.kimg = bh * slice_bytes<D, false>(p.nkt);
   p.pkv = p.split_kv > 1 ? 2 * (size_t)p.split_kv * kbytes : 0;
   p.pq = p.split_q > 1 ? (size_t)p.split_q * qbytes : 0;
   return p;
@@ -561,6 +662,12 @@ hipError_t launch_d(const void* q, const void* k, const void* v, const float* o,
   float* pkv = reinterpret_cast<float*>(kimg + p.kimg);
   float* pq = reinterpret_cast<float*>(kimg + p.kimg + p.pkv);
   const uint32_t qb = (uint32_t)((size_t)bh * Nq * D * 2), kb = (uint32_t)((size_t)bh * Nk * D * 2);
+  hipError_t e = launch_range_stats<D>(q, go, qimg, bh, Nq, slice_bytes<D, true>(nqt),
+                                       (uint32_t)nqt * QImg<D>::kBytes, stream);
+  if (e != hipSuccess) return e;
+  e = launch_range_stats<D>(k, nullptr, kimg, bh, Nk, slice_bytes<D, false>(nkt),
+                            (uint32_t)nkt * KImg<D>::kBytes, stream);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((pack_kernel<D, true>), dim3(nqt, bh), dim3(kPackThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(go),
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(go), o, lse,

@@ -108,9 +108,8 @@ static_assert(Geo<128, true>::kImgBytes == 65536 && Geo<64, true>::kImgBytes == 
               "tile image sizes");
 
 // One (b, h) slice of the workspace: the ntiles tile images, then the header
-// of range.hpp (kHdrBytes): record = {int eV, int edV, uint flags}, norm
-// maxima = {max_j |k_j|, max_j |dk_j|}, the range pass's partial maxima of
-// |V| and |dV|.
+// of range.hpp (kHdrBytes): record = {int eV, int edV, uint flags}, the range
+// pass's partial maxima of |V| and |dV|, norm slots = {max |k_j|, max |dk_j|}.
 constexpr uint32_t kDvZero = 1u;  // flags: dV has no finite nonzero value (or no dV at all)
 template <int D, bool kKV>
 __host__ __device__ constexpr uint32_t slice_bytes(int ntiles) {
@@ -215,9 +214,7 @@ __device__ __attribute__((always_inline)) inline void pack_kv_body(
     }
     const float fk = round_up_f32(__builtin_sqrt(nk));
     const float fdk = kKV ? round_up_f32(__builtin_sqrt(ndk)) : 0.f;
-    uint32_t* nmax = reinterpret_cast<uint32_t*>(ws + (size_t)bh * sb + hdr + kHdrNorms);
-    atomicMax(nmax, __builtin_bit_cast(uint32_t, fk));
-    atomicMax(nmax + 1, __builtin_bit_cast(uint32_t, fdk));
+    raise_norms(ws + (size_t)bh * sb + hdr, tile, fk, fdk);
     if (tile == 0) {
       const uint32_t flags = (!kKV || mdv == 0) ? kDvZero : 0u;
       buf_store16(rws, hdr + kHdrRecord, u32x4{(uint32_t)ev, (uint32_t)edv, flags, 0u});
@@ -504,12 +501,11 @@ struct WaveScale {
 
 template <int D, bool kKV>
 __device__ __attribute__((always_inline)) inline WaveScale wave_scale(
-    __amdgpu_buffer_rsrc_t rimg, uint32_t hdr, const u32x4* qf, const u32x4* dqf, float scale) {
+    __amdgpu_buffer_rsrc_t rimg, uint32_t hdr, int ntiles, const u32x4* qf, const u32x4* dqf,
+    float scale, int lane) {
   const u32x4 rec = buf_load16(rimg, hdr + kHdrRecord);
-  const uint32_t mk_bits = __builtin_amdgcn_raw_buffer_load_b32(rimg, (int)(hdr + kHdrNorms), 0, 0);
-  const uint32_t mdk_bits =
-      __builtin_amdgcn_raw_buffer_load_b32(rimg, (int)(hdr + kHdrNorms + 4), 0, 0);
-  const float mk = __builtin_bit_cast(float, mk_bits), mdk = __builtin_bit_cast(float, mdk_bits);
+  float mk, mdk;
+  slice_norms(rimg, hdr, ntiles, lane, mk, mdk);
   double nq = 0.0, ndq = 0.0;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
@@ -617,7 +613,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
     dqf[ks] = buf_load16(rtq, off);
   }
 
-  const WaveScale sc = wave_scale<D, M::kKV>(rimg, hdr, qf, dqf, scale);
+  const WaveScale sc = wave_scale<D, M::kKV>(rimg, hdr, ntiles, qf, dqf, scale, lane);
 
   RowState<D> st;
 #pragma unroll
@@ -741,7 +737,7 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
     dqf[ks] = buf_load16(rtq, off);
   }
 
-  const WaveScale sc = wave_scale<D, M::kKV>(rimg, hdr, qf, dqf, scale);
+  const WaveScale sc = wave_scale<D, M::kKV>(rimg, hdr, ntiles, qf, dqf, scale, lane);
 
   RowState<D> st;
 #pragma unroll

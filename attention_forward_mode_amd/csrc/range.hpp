@@ -111,6 +111,31 @@ __device__ inline float wave_max_f32(float x) {
   return x;
 }
 
+// Eight bf16 values times 2^t (exact while the results stay normal; rounded
+// to nearest even below that).
+__device__ inline u32x4 scale_bf16x8(u32x4 x, int t) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t v = x[w];
+    const float lo = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, v << 16), t);
+    const float hi = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, v & 0xffff0000u), t);
+    const uint32_t blo = __builtin_bit_cast(uint16_t, (__bf16)lo);
+    const uint32_t bhi = __builtin_bit_cast(uint16_t, (__bf16)hi);
+    r[w] = blo | (bhi << 16);
+  }
+  return r;
+}
+
+// The largest t with x 2^t <= 2^120 (x > 0 finite; otherwise 1000, no limit):
+// a cap on a scaling exponent that keeps bf16 values and their sums finite.
+__device__ inline int cap_exponent(double x) {
+  if (!(x > 0.0) || !__builtin_isfinite(x)) return 1000;
+  int e;
+  __builtin_frexp(x, &e);  // x = f 2^e, f in [0.5, 1): x 2^(120 - e) < 2^120
+  return 120 - e;
+}
+
 // fp32 value not below the fp64 x (x >= 0): rounded to nearest, then raised by
 // 2^-20 relative, more than the rounding can have taken off.
 __device__ inline float round_up_f32(double x) { return (float)(x * (1.0 + 0x1p-20)); }
@@ -119,18 +144,23 @@ __device__ inline float round_up_f32(double x) { return (float)(x * (1.0 + 0x1p-
 // Each (b, h) slice of a packed workspace (tile images of 64 rows of one
 // side, keys or queries) ends with a header of kHdrBytes:
 //   +kHdrRecord  the slice's fp16 exponents (int, up to four) and flags
-//   +kHdrNorms   two fp32 maxima of row norms (rounded up), raised by the
-//                pack's workgroups with integer atomics (the bit patterns of
-//                non-negative floats order like their values) after the
-//                range pass has zeroed them
 //   +kHdrStats   the range pass's partial maxima, per chunk of rows: uint max
 //                finite |x| and |y| as bf16 magnitude bits
+//   +kHdrNorms   kNormSlots pairs of fp32 maxima of row norms (rounded up):
+//                the pack's workgroup of tile i raises pair i % kNormSlots with
+//                integer atomics (the bit patterns of non-negative floats
+//                order like their values; spreading the tiles over slots keeps
+//                the atomics on one address few), after the range pass has
+//                zeroed them; a consumer takes the maximum over the slots
 constexpr int kHdrRecord = 0;
-constexpr int kHdrNorms = 16;
 constexpr int kHdrStats = 256;
 constexpr int kStatChunks = 64;
-constexpr int kHdrBytes = 1024;
-static_assert(kHdrStats + 8 * kStatChunks <= kHdrBytes, "header layout");
+constexpr int kHdrNorms = 1024;
+constexpr int kNormSlots = 64;
+constexpr int kHdrBytes = 2048;
+static_assert(kHdrStats + 8 * kStatChunks <= kHdrNorms &&
+                  kHdrNorms + 8 * kNormSlots <= kHdrBytes,
+              "header layout");
 constexpr int kStatThreads = 256;
 
 __host__ __device__ constexpr int stat_chunks(int ntiles) {
@@ -194,8 +224,10 @@ __global__ __launch_bounds__(kStatThreads) void range_stats_kernel(
       my = sm[1][i] > my ? sm[1][i] : my;
     }
     buf_store8(rws, hdr + kHdrStats + 8 * c, u32x2{mx, my});
-    if (c == 0) buf_store8(rws, hdr + kHdrNorms, u32x2{0u, 0u});
   }
+  // the norm slots the pack raises with atomics start at 0
+  if (c == 0 && threadIdx.x < kNormSlots)
+    buf_store8(rws, hdr + kHdrNorms + 8 * threadIdx.x, u32x2{0u, 0u});
 }
 
 template <int D>
@@ -207,6 +239,28 @@ inline hipError_t launch_range_stats(const void* x, const void* y, void* ws, int
                      static_cast<const uint16_t*>(y), static_cast<char*>(ws), N, ntiles,
                      (uint32_t)((size_t)slices * N * D * 2), slice_bytes, hdr);
   return hipGetLastError();
+}
+
+// Raise norm slot tile % kNormSlots of the slice header at `hdr_ptr` to
+// (a, b) (non-negative fp32, as bits).
+__device__ inline void raise_norms(char* hdr_ptr, int tile, float a, float b) {
+  uint32_t* slot = reinterpret_cast<uint32_t*>(hdr_ptr + kHdrNorms) + 2 * (tile % kNormSlots);
+  atomicMax(slot, __builtin_bit_cast(uint32_t, a));
+  atomicMax(slot + 1, __builtin_bit_cast(uint32_t, b));
+}
+
+// The two norm maxima of a slice (over its slots), in every lane of a wave.
+__device__ inline void slice_norms(__amdgpu_buffer_rsrc_t rws, uint32_t hdr, int ntiles,
+                                   int lane, float& a, float& b) {
+  a = 0.f;
+  b = 0.f;
+  if (lane < (ntiles < kNormSlots ? ntiles : kNormSlots)) {
+    const int o = (int)(hdr + kHdrNorms + 8 * lane);
+    a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rws, o, 0, 0));
+    b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rws, o + 4, 0, 0));
+  }
+  a = wave_max_f32(a);
+  b = wave_max_f32(b);
 }
 
 // The range pass's maxima of one slice, reduced by one wave from its partial

@@ -128,7 +128,7 @@ ATTN_JVP_API int attn_jvp_fwd(const void *q, const void *k, const void *v,
  * 64-key tile image per key tile, holding K and dK (bf16) and V^T and dV^T
  * (fp16, scaled by the slice's powers of two) as the sequence of matrix-core
  * operand fragments the fused kernel reads, laid out byte for byte as it holds
- * them in LDS (64 KiB per tile at d = 128, 32 KiB at d = 64), then a 1 KiB
+ * them in LDS (64 KiB per tile at d = 128, 32 KiB at d = 64), then a 2 KiB
  * header (the powers of two, the partial maxima they come from and the largest
  * key norms); 0 if a size is invalid.  Same operation as attn_jvp_fwd.
  */

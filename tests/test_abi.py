@@ -55,12 +55,12 @@ def test_strerror():
 def test_workspace_bytes():
     # per (b, h): one tile image per 64-key tile (K, dK as 64 x d bf16 and V^T,
     # dV^T as d x 64 fp16, unpadded operand fragments, a whole number of
-    # 8 KiB), then a 1 KiB header (the fp16 exponents, the largest key norms
-    # and the range pass's partial maxima)
+    # 8 KiB), then a 2 KiB header (the fp16 exponents, the range pass's
+    # partial maxima and the largest key norms)
     def img(d):
         used = 2 * 64 * d * 2 + 2 * d * 64 * 2
         return -(-used // 8192) * 8192
-    hdr = 1024
+    hdr = 2048
     assert img(128) == 64 * 1024 and img(64) == 32 * 1024
     assert ajvp.attn_jvp_workspace_bytes(1, 1, 1, 128) == img(128) + hdr
     assert ajvp.attn_jvp_workspace_bytes(1, 12, 32760, 128) == 12 * (512 * img(128) + hdr)

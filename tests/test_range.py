@@ -203,3 +203,86 @@ def test_nonfinite_inputs_propagate(value, Nk):
             if (~bad_r).any():
                 m = metrics(gt[~bad_r], rf[~bad_r])
                 assert m["max_abs"] <= 2e-2 and m["rel_frob"] <= 1e-2, (name, oname, m)
+
+
+# ---- the backward pass ------------------------------------------------------------
+# Its fp16 operands are Q^T, gO^T and K^T (per-slice powers of two from their
+# largest magnitudes), P (<= 1) and the softmax gradient gS (a per-wave power of
+# two from |gS_ij| <= |gO_i| |v_j| + |D_i|).  Gate as tests/test_backward.py:
+# relative Frobenius error <= 1e-2, max-abs <= 2e-2 of the largest reference
+# magnitude.
+
+def _bwd(x, scale=S128):
+    g = {n: t.cuda() for n, t in x.items()}
+    print(f"  launch attn_fwd + attn_bwd q{tuple(g['q'].shape)} k{tuple(g['k'].shape)}",
+          flush=True)
+    o, lse = ajvp.attn_fwd(g["q"], g["k"], g["v"], scale=scale)
+    out = ajvp.attn_bwd(g["q"], g["k"], g["v"], o, g["dq"], lse, scale=scale)
+    torch.cuda.synchronize()
+    return [t.cpu() for t in out]
+
+
+def _bwd_gate(label, got, want):
+    for name, a, b in zip(("gQ", "gK", "gV"), got, want):
+        a = a.double().numpy()
+        m = metrics(a, b)
+        print(f"[{label}] {name}: rel-Frobenius {m['rel_frob']:.3e} max-abs/max|ref| "
+              f"{m['max_rel']:.3e} max|ref| {np.abs(b).max():.3e}", flush=True)
+        assert np.isfinite(a).all(), (label, name)
+        assert m["rel_frob"] <= 1e-2 and m["max_rel"] <= 2e-2, (label, name, m)
+
+
+@pytest.mark.parametrize("Nk", [200, 700])
+def test_backward_scaling_is_exact(Nk):
+    """gO -> 2^k gO gives 2^k (gQ, gK, gV); V -> 2^k V (O with it) gives
+    2^k (gQ, gK) and the same gV (gS = P (gO V^T - <gO, O>) is linear in V,
+    gV = P^T gO does not involve it), bit for bit.  The cotangent gO is the
+    dq draw."""
+    x = _rand(2, 300, Nk, seed=31 + Nk)
+    base = _bwd(x)
+    for k in (24, -30):
+        y = dict(x, dq=_pow2(x["dq"], k))
+        got = _bwd(y)
+        for a, b in zip(got, base):
+            assert torch.equal(a, b * 2.0 ** k), k
+        y = dict(x, v=_pow2(x["v"], k))
+        gq, gk, gv = _bwd(y)
+        assert torch.equal(gq, base[0] * 2.0 ** k), k
+        assert torch.equal(gk, base[1] * 2.0 ** k), k
+        assert torch.equal(gv, base[2]), k
+
+
+BWD_CASES = {
+    # sigmas of (q, k, v, gO = dq); dk, dv unused
+    "V_1e6": (1.0, 1.0, 2e5, 0.1),
+    "gO_1e5": (1.0, 1.0, 1.0, 2e4),
+    "Q_1e5_K_1e-5": (2e4, 2e-5, 1.0, 0.1),
+    "K_1e5_Q_1e-5": (2e-5, 2e4, 1.0, 0.1),
+    "tiny_V_gO": (1.0, 1.0, 1e-6, 1e-7),
+}
+
+
+@pytest.mark.parametrize("case", list(BWD_CASES))
+def test_backward_out_of_fp16_range_vs_oracle(case):
+    sq, sk, sv, sg = BWD_CASES[case]
+    x = _rand(2, 300, 700, seed=list(BWD_CASES).index(case), sig=(sq, sk, sv, sg, 0.1, 0.1))
+    want = oracle.attention_vjp(x["q"], x["k"], x["v"], x["dq"], S128)
+    _bwd_gate(f"bwd {case}", _bwd(x), want)
+
+
+def test_backward_nonfinite_inputs_propagate():
+    """A NaN in gO row i or in V: the gradients are non-finite exactly where
+    the oracle's are."""
+    base = _rand(1, 130, 200, seed=41)
+    for name in ("dq", "v", "q"):
+        x = {n: t.clone() for n, t in base.items()}
+        x[name][0, 0, 17, 5] = float("nan")
+        got = _bwd(x)
+        with np.errstate(all="ignore"):
+            want = oracle.attention_vjp(x["q"], x["k"], x["v"], x["dq"], S128)
+        for gname, a, b in zip(("gQ", "gK", "gV"), got, want):
+            a = a.double().numpy()
+            bad_a, bad_b = ~np.isfinite(a), ~np.isfinite(b)
+            print(f"  NaN in {name}: {gname} {bad_a.sum()} non-finite (oracle {bad_b.sum()})",
+                  flush=True)
+            assert (bad_a == bad_b).all(), (name, gname)
