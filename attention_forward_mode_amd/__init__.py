@@ -16,6 +16,9 @@ device memory and the current stream.  The names mirror the C entry points:
         -> (lse, o, to, tlse): combine results over disjoint key subsets
     attn_bwd(q, k, v, o, go, lse) -> (gq, gk, gv)
         the backward pass: gradients of a loss through O
+    attn_jvp_fwd_noalloc(q, k, v, tq, tk, tv, ...) -> (o, to, lse)
+        attn_jvp_fwd without any allocation in the library (its tile images in
+        a fixed device buffer of NOALLOC_BYTES per GPU)
     attn_jvp_fwd_f32(...)  the same with fp32 inputs
     attn_jvp_workspace_bytes(B, H, Nk, d)
     attn_jvp_strerror(status)
@@ -34,7 +37,7 @@ import os
 
 import torch
 
-__all__ = ["attn_jvp_fwd", "attn_jvp_pack_kv", "attn_jvp_fwd_packed", "attn_jvp_fwd_ex", "attn_fwd",
+__all__ = ["attn_jvp_fwd", "attn_jvp_fwd_noalloc", "NOALLOC_BYTES", "attn_jvp_pack_kv", "attn_jvp_fwd_packed", "attn_jvp_fwd_ex", "attn_fwd",
            "attn_jvp_merge", "attn_bwd", "attn_bwd_workspace_bytes", "attn_jvp_fwd_f32",
            "attn_jvp_workspace_bytes",
            "attn_jvp_strerror", "AttnJvpError", "LIB_PATH", "lib"]
@@ -60,6 +63,8 @@ def lib():
     _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_jvp_fwd.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _vp]
     L.attn_jvp_fwd.restype = _i
+    L.attn_jvp_fwd_noalloc.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _vp]
+    L.attn_jvp_fwd_noalloc.restype = _i
     L.attn_jvp_fwd_ws.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _vp, _sz, _vp]
     L.attn_jvp_fwd_ws.restype = _i
     L.attn_jvp_pack_kv.argtypes = [_vp] * 4 + [_i] * 4 + [_vp, _sz, _vp]
@@ -93,6 +98,7 @@ def lib():
 
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, ELAUNCH = 0, -1, -2, -3, -4
+NOALLOC_BYTES = 128 << 20  # the device buffer of attn_jvp_fwd_noalloc (ATTN_JVP_NOALLOC_BYTES)
 OUT_F32, OUT_BF16 = 0, 1
 
 
@@ -229,6 +235,24 @@ def attn_jvp_fwd(q, k, v, tq, tk, tv, scale=None, lse=True, out=None, workspace=
         rc = lib().attn_jvp_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
                                  _ptr(o), _ptr(to), _ptr(lse_t), B, H, Nq, Nk, d, s,
                                  _ptr(workspace), _nbytes(workspace), stream)
+    if rc != OK:
+        raise AttnJvpError(rc)
+    return o, to, lse_t
+
+
+def attn_jvp_fwd_noalloc(q, k, v, tq, tk, tv, scale=None, lse=True, out=None):
+    """attn_jvp_fwd through the entry point that allocates nothing: the library
+    keeps the tile images in its fixed device buffer (calls that overlap on one
+    GPU race on it).  ``out`` may pass preallocated (o, to, lse); otherwise torch
+    allocates the outputs here, in the binding.  Returns (o, to, lse)."""
+    B, H, Nq, Nk, d = _check(q, k, v, tq, tk, tv, torch.bfloat16)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o, to, lse_t = _outputs(q, B, H, Nq, d, lse, out)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    with torch.cuda.device(q.device):
+        rc = lib().attn_jvp_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                                        _ptr(o), _ptr(to), _ptr(lse_t), B, H, Nq, Nk, d, s,
+                                        stream)
     if rc != OK:
         raise AttnJvpError(rc)
     return o, to, lse_t

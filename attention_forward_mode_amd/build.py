@@ -25,7 +25,8 @@ PROBE_LIB = os.path.join(PKG, "libmfma_probe.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["attn_jvp_bf16.hip", "attn_jvp_f32.hip", "attn_jvp_merge.hip", "attn_bwd.hip"]
+HIP_SOURCES = ["attn_jvp_bf16.hip", "attn_jvp_f32.hip", "attn_jvp_merge.hip", "attn_bwd.hip",
+               "attn_jvp_noalloc.hip"]
 CXX_SOURCES = ["attn_jvp_api.cpp"]
 PROBE_SOURCE = "mfma_probe.hip"
 

@@ -291,6 +291,31 @@ int attn_jvp_fwd(const void* q, const void* k, const void* v, const void* tq, co
   });
 }
 
+int attn_jvp_fwd_noalloc(const void* q, const void* k, const void* v, const void* tq,
+                         const void* tk, const void* tv, float* o, float* to, float* lse, int B,
+                         int H, int Nq, int Nk, int d, float scale, attn_jvp_stream_t stream) {
+  const void* in[6] = {q, k, v, tq, tk, tv};
+  int rc = validate(in, 6, o, to, lse, B, H, Nq, Nk, d, scale, 2);
+  if (rc != ATTN_JVP_OK) return rc;
+  // groups of whole slices whose tile images fit the library's device buffer;
+  // one slice must fit on its own
+  const size_t cap = ajvp::scratch_bytes();
+  Slices s = slices(B, H, Nq, Nk, d, 2);
+  if (size_t(s.img) > cap) return ATTN_JVP_EUNSUPPORTED;
+  const int64_t fit = int64_t(cap / size_t(s.img));
+  if (s.g > fit) s.g = fit;
+  void* ws = nullptr;
+  if (ajvp::scratch_buffer(&ws) != hipSuccess) return ATTN_JVP_ELAUNCH;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = each_group(s, [&](int64_t s0, int n) {
+    return ajvp::launch_bf16(shift(q, s0 * s.q), shift(k, s0 * s.k), shift(v, s0 * s.k),
+                             shift(tq, s0 * s.q), shift(tk, s0 * s.k), shift(tv, s0 * s.k),
+                             shift(o, s0 * s.o), shift(to, s0 * s.o), shift(lse, s0 * s.r), 1, n,
+                             Nq, Nk, d, scale, ws, st);
+  });
+  return e == hipSuccess ? ATTN_JVP_OK : ATTN_JVP_ELAUNCH;
+}
+
 int attn_jvp_fwd_ex(const void* q, const void* k, const void* v, const void* tq, const void* tk,
                     const void* tv, void* o, void* to, float* lse, float* tlse, int B, int H,
                     int Nq, int Nk, int d, float scale, int out_dtype, void* workspace,

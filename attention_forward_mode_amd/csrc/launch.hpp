@@ -66,6 +66,11 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const float* 
                       const float* lse, float* gq, float* gk, float* gv, int B, int H, int Nq,
                       int Nk, int d, float scale, void* workspace, hipStream_t stream);
 
+// The device buffer of attn_jvp_fwd_noalloc (attn_jvp_noalloc.hip): its size,
+// and its address on the current device (looked up once per device).
+size_t scratch_bytes();
+hipError_t scratch_buffer(void** out);
+
 hipError_t launch_f32(const float* q, const float* k, const float* v, const float* tq,
                       const float* tk, const float* tv, float* o, float* to, float* lse,
                       int B, int H, int Nq, int Nk, int d, float scale, hipStream_t stream);

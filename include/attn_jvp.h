@@ -124,6 +124,26 @@ ATTN_JVP_API int attn_jvp_fwd(const void *q, const void *k, const void *v,
                  attn_jvp_stream_t stream);
 
 /*
+ * attn_jvp_fwd for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * semantics and results (bit for bit) as attn_jvp_fwd; it calls no allocator.
+ * The tile images live in a device buffer of ATTN_JVP_NOALLOC_BYTES that the
+ * library holds on every GPU it runs on, from its first call there until the
+ * process ends; a call whose images pass that size runs as consecutive
+ * launches over groups of (b, h) slices that fit.  ATTN_JVP_EUNSUPPORTED if
+ * the images of one slice do not fit (Nk beyond 131008 at d = 128, 262080
+ * at d = 64); otherwise errors as attn_jvp_fwd.  Every call on one GPU uses
+ * the same buffer: calls that may overlap on one GPU (other streams, other
+ * threads) race and give wrong results; calls in one stream are ordered.
+ */
+#define ATTN_JVP_NOALLOC_BYTES ((size_t)128 << 20)
+ATTN_JVP_API int attn_jvp_fwd_noalloc(const void *q, const void *k, const void *v,
+                         const void *tq, const void *tk, const void *tv,
+                         float *o, float *to, float *lse,
+                         int B, int H, int Nq, int Nk, int d, float scale,
+                         attn_jvp_stream_t stream);
+
+/*
  * Bytes of workspace the bf16 path needs for these sizes: per (b, h), one
  * 64-key tile image per key tile, holding K and dK (bf16) and V^T and dV^T
  * (fp16, scaled by the slice's powers of two) as the sequence of matrix-core

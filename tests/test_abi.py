@@ -422,3 +422,27 @@ def test_fwd_splitkv_rejects_bad_arguments():
     assert call(p) == EALIGN
     nb = ajvp.attn_jvp_splitkv_workspace_bytes(1, 1, 4, 4, 128, 0)
     assert call(ws=A + 0x3000000, ws_bytes=nb - 1) == EINVAL
+
+
+def test_noalloc_validation():
+    """attn_jvp_fwd_noalloc validates like attn_jvp_fwd and rejects, before any
+    launch, a call whose single (b, h) slice of tile images exceeds its fixed
+    device buffer (fake, never-dereferenced pointers)."""
+    L = ajvp.lib()
+    p = [ctypes.c_void_p(A + i * 0x100000) for i in range(9)]
+    f = L.attn_jvp_fwd_noalloc
+    s = ctypes.c_float(0.1)
+    # 2048 key tiles x 64 KiB + the slice header > 128 MiB
+    assert f(*p, 1, 1, 4, 131072, 128, s, None) == EUNSUPPORTED
+    assert f(*p, 1, 1, 4, 4 * 131072, 64, s, None) == EUNSUPPORTED
+    assert f(*p, 1, 1, 4, 4, 96, s, None) == EUNSUPPORTED
+    assert f(*p, 0, 1, 4, 4, 128, s, None) == EINVAL
+    assert f(*p, 1, 1, 4, 4, 128, ctypes.c_float(float("nan")), None) == EINVAL
+    for i in range(8):
+        q = list(p)
+        q[i] = ctypes.c_void_p(0)
+        assert f(*q, 1, 1, 4, 4, 128, s, None) == EINVAL, i
+    q = list(p)
+    q[2] = ctypes.c_void_p(A + 8)
+    assert f(*q, 1, 1, 4, 4, 128, s, None) == EALIGN
+    assert ajvp.NOALLOC_BYTES == 128 << 20
