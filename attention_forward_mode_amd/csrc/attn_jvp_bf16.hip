@@ -55,6 +55,7 @@
 // key tiles per work item and write partial states (split-KV for few query
 // rows), which the merge kernel of attn_jvp_merge.hip combines.
 #include <cmath>
+#include <cstdlib>
 
 #include "cdna4.hpp"
 #include "launch.hpp"
@@ -1037,6 +1038,17 @@ hipError_t launch_pack_d(const void* k, const void* v, const void* tk, const voi
   return hipGetLastError();
 }
 
+// ATTN_JVP_TILE in the environment (read on every call) overrides the choice
+// of kernel form, for tuning sweeps and for the tests that compare the forms:
+// 128 or 256 query rows per workgroup of the JVP kernels (the short-key and
+// the 256-row kernel), 256 or 512 of the forward kernel (one or two 32-row
+// blocks per wave).  Every form computes each row with the same products in
+// the same order, so the results do not change.
+int tile_override() {
+  const char* e = std::getenv("ATTN_JVP_TILE");
+  return e != nullptr ? std::atoi(e) : 0;
+}
+
 template <int D, int kMode, bool kOutBf16>
 hipError_t launch_main_d(const void* q, const void* tq, const void* ws, void* o, void* to,
                          float* lse, float* tlse, int B, int H, int Nq, int Nk, float scale,
@@ -1049,7 +1061,8 @@ hipError_t launch_main_d(const void* q, const void* tq, const void* ws, void* o,
   ext.q_bytes = (uint32_t)((size_t)bh * Nq * D * 2);
   ext.o_bytes = (uint32_t)((size_t)ns * bh * Nq * D * (kOutBf16 ? 2 : 4));
   ext.lse_bytes = (uint32_t)((size_t)ns * bh * Nq * 4);
-  if (tps <= kShortMaxTiles) {
+  const int tile = tile_override();
+  if (tile == kShortBR || (tile != kBR && tps <= kShortMaxTiles)) {
     const int nqt = (Nq + kShortBR - 1) / kShortBR;
     hipLaunchKernelGGL((attn_jvp_bf16_short_kernel<D, kMode, kOutBf16>), dim3(nqt * bh * ns),
                        dim3(kShortThreads), 0, stream, static_cast<const uint16_t*>(q),
@@ -1167,7 +1180,8 @@ hipError_t launch_fwd_d(const void* q, const void* ws, void* o, float* lse, int 
   // and output traffic with the other's products, as in the short-key JVP
   // kernel (H = 12, Nq = 32760: 512 keys 148 vs 164 us, 1024 keys 231 vs 244;
   // 2048 keys 402 vs 395)
-  if (tiles256 > 256 && tps > kShortMaxTiles)
+  const int tile = tile_override();
+  if (tile == fwd_rows<2>() || (tile != fwd_rows<1>() && tiles256 > 256 && tps > kShortMaxTiles))
     return launch_fwd_rb<D, 2, kOutBf16>(q, ws, o, lse, B, H, Nq, Nk, scale, ns, stream);
   return launch_fwd_rb<D, 1, kOutBf16>(q, ws, o, lse, B, H, Nq, Nk, scale, ns, stream);
 }

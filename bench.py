@@ -18,11 +18,12 @@ bf16 inputs, fp32 outputs).  Prints ONE JSON line:
             of every timed step.  'traffic' is the measured HBM bytes per
             launch from the committed rocprofv3 counter summary, or null when
             the kernel source changed since it was taken.
-  hbm_gbs_algorithmic / hbm_gbs_measured_kernel  the algorithmic bytes over the
-            step time, and the measured bytes ('traffic') over the fused
-            kernel's time.
+  hbm_gbs_algorithmic  the algorithmic bytes (six inputs, fp32 O, dO and lse)
+            over the step time.
   cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample of
-            the same workload (query rows of head 0), same FLOP count.
+            the same workload (query rows of up to four heads, ~15 s), same FLOP count:
+            a process pool with one worker per core in os.sched_getaffinity(0)
+            and one BLAS thread per worker; "cores" is that worker count.
   mfma_loop  the bf16 matrix-core rate this board sustains under a load of
             nothing but matrix products (libmfma_probe.so, same occupancy as
             the fused kernel: two waves per SIMD), timed after the steps, and
@@ -94,35 +95,88 @@ def flops(B, H, Nq, Nk, d):
     return 12.0 * B * H * Nq * Nk * d
 
 
-def cpu_baseline(x, scale, budget_s=12.0, chunk=256):
-    """Time the fp64 oracle on query rows of head 0 until ~budget_s elapses."""
+# ---- the CPU baseline: the fp64 oracle on the host's cores ----
+# A process pool over chunks of query rows of up to four heads, one worker per core in
+# os.sched_getaffinity(0), each with one BLAS thread.  The workers are forked
+# before anything touches the GPU (so they hold no GPU state) and receive the
+# inputs as numpy arrays (they never call torch); they run after the GPU
+# timing, until a deadline.
+_CPU = {}
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+
+    _CPU["blas"] = threadpool_limits(limits=1)
+
+
+def _cpu_worker(task):
+    """Oracle rows of the sampled heads, `chunk` at a time, from work item
+    `first` of the list of (head, row chunk) items in steps of `step`, until
+    `deadline`; returns (rows done, start, end) in wall-clock seconds."""
     import numpy as np
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                            if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        blas_threads = 1
-    Nq, Nk, d = x["q"].shape[2], x["k"].shape[2], x["q"].shape[3]
-    rows_done, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s and rows_done < Nq:
-        rows = np.arange(rows_done, min(Nq, rows_done + chunk))
-        oracle.attention_jvp_rows(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], scale, 0, 0, rows)
-        rows_done += len(rows)
-    dt = time.perf_counter() - t0
-    return {
-        "value": round(flops(1, 1, rows_done, Nk, d) / dt / 1e12, 6),
-        "unit": "TFLOP/s",
-        "cores": int(blas_threads),
-        "kind": "oracle",
-        "sample": f"query rows 0..{rows_done - 1} of head 0 against all {Nk} keys "
-                  f"({rows_done}/{Nq * x['q'].shape[0] * x['q'].shape[1]} rows of the workload), "
-                  f"fp64 NumPy, {dt:.1f} s wall; exp is single-threaded, BLAS uses "
-                  f"{blas_threads} threads",
-    }
+    first, step, deadline, chunk = task
+    x, scale = _CPU["x"], _CPU["scale"]
+    heads, Nq = x["q"].shape[1], x["q"].shape[2]
+    per_head = -(-Nq // chunk)
+    t0, done = time.time(), 0
+    for item in range(first, heads * per_head, step):
+        if time.time() >= deadline:
+            break
+        h, a = item // per_head, (item % per_head) * chunk
+        rows = np.arange(a, min(Nq, a + chunk))
+        oracle.attention_jvp_rows(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], scale, 0, h,
+                                  rows)
+        done += len(rows)
+    return done, t0, time.time()
+
+
+class CpuBaseline:
+    """Create before the GPU is used; run() after the GPU timing."""
+
+    def __init__(self, workload):
+        import multiprocessing
+
+        import torch
+
+        from workloads import make_inputs
+
+        from workloads import WORKLOADS
+
+        self.heads = min(WORKLOADS[workload].H, 4)  # the sample's heads (batch 0)
+        x, scale = make_inputs(workload, heads=range(self.heads), device="cpu")
+        x = {n: t[:1] for n, t in x.items()}
+        _CPU["x"] = {n: t.to(torch.float32).numpy() for n, t in x.items()}
+        _CPU["scale"] = scale
+        self.Nq, self.d = x["q"].shape[2], x["q"].shape[3]
+        self.Nk = x["k"].shape[2]
+        self.cores = len(os.sched_getaffinity(0))
+        self.pool = multiprocessing.get_context("fork").Pool(self.cores,
+                                                             initializer=_cpu_worker_init)
+
+    def run(self, heads_total, budget_s=15.0, chunk=64):
+        n, Nq = self.cores, self.Nq
+        deadline = time.time() + budget_s
+        tasks = [(i, n, deadline, chunk) for i in range(n)]
+        res = self.pool.map(_cpu_worker, tasks)
+        self.pool.close()
+        self.pool.join()
+        rows = sum(r[0] for r in res)
+        wall = max(r[2] for r in res) - min(r[1] for r in res)
+        return {
+            "value": round(flops(1, 1, rows, self.Nk, self.d) / wall / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": n,
+            "kind": "oracle",
+            "sample": f"{rows} query rows of heads 0-{self.heads - 1} (batch 0) against all "
+                      f"{self.Nk} keys ({rows} of {Nq * heads_total} rows of the workload), fp64 "
+                      f"NumPy oracle, a pool of {n} worker processes (one per core in "
+                      f"os.sched_getaffinity) with one BLAS thread each over {chunk}-row chunks "
+                      f"taken in turn, {wall:.1f} s wall",
+        }
 
 
 def calib_copy(nbytes=1 << 30, reps=5):
@@ -263,6 +317,8 @@ def main():
                          "bwd: the backward pass, gradients through O (10 Nq Nk d algorithmic)")
     ap.add_argument("--out-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-clock budget of the CPU oracle baseline")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
 
@@ -271,6 +327,11 @@ def main():
               "(the path would shard by head, one all-to-all before and after the kernel)",
               file=sys.stderr)
         sys.exit(2)
+
+    cpu = None
+    if not (args.no_cpu_baseline or args.calib_copy or args.mode != "jvp"
+            or args.out_dtype != "f32"):
+        cpu = CpuBaseline(args.workload)  # forks its workers before the GPU is touched
 
     import torch
 
@@ -356,8 +417,6 @@ def main():
                    "d": d, "scale": scale, "outputs": "fp32 O, dO, lse"},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "hbm_gbs_algorithmic": round(alg_bytes / (ms / 1e3) / 1e9, 1),
-        "hbm_gbs_measured_kernel": (round(traffic / (kern_ms / 1e3) / 1e9, 1)
-                                    if traffic is not None else None),
         "roofline": {
             "kernel": jvp_kernel_name(Nk, d),
             "bound": "mfma",
@@ -375,8 +434,8 @@ def main():
     if loop is not None:
         loop["kernel_frac_of_loop"] = round(kern_tflops / loop["tflops"], 4)
     res["mfma_loop"] = loop
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(x, scale)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu.run(heads_total=B * H, budget_s=args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

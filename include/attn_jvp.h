@@ -58,6 +58,11 @@
  * (stream-ordered hipMallocFromPoolAsync / hipFreeAsync); attn_jvp_fwd_ws uses
  * a caller-provided workspace instead.
  *
+ * Tuning.  The environment variable ATTN_JVP_TILE, read on every call, can
+ * force the workgroup size of the bf16 kernels: 128 or 256 query rows for the
+ * JVP (the default takes 128 when a work item has at most 16 key tiles), 256
+ * or 512 for attn_fwd.  The results are the same bit for bit either way.
+ *
  * Errors.  Argument errors are detected before anything is launched and leave
  * every output untouched:
  *   ATTN_JVP_EINVAL       a required pointer is NULL; B, H, Nq or Nk < 1;
