@@ -6,6 +6,8 @@ Only the test suite, ``__graft_entry__.smoke()`` and ``bench.py``'s
 imports it and shares no code with it.
 """
 
-from .attention_jvp import attention, attention_jvp, attention_jvp_rows, attention_vjp, ROW_CHUNK
+from .attention_jvp import (attention, attention_jvp, attention_jvp_rows, attention_vjp,
+                            attention_vjp_keys, ROW_CHUNK)
 
-__all__ = ["attention", "attention_jvp", "attention_jvp_rows", "attention_vjp", "ROW_CHUNK"]
+__all__ = ["attention", "attention_jvp", "attention_jvp_rows", "attention_vjp",
+           "attention_vjp_keys", "ROW_CHUNK"]

@@ -49,7 +49,8 @@ here is "parity unpinned".
 
 import numpy as np
 
-__all__ = ["attention", "attention_jvp", "attention_jvp_rows", "attention_vjp"]
+__all__ = ["attention", "attention_jvp", "attention_jvp_rows", "attention_vjp",
+           "attention_vjp_keys"]
 
 # Rows per chunk: bounds the Nq_chunk x Nk float64 temporaries (512 x 32760 x 8 B
 # = 134 MB each) without changing any value.
@@ -131,6 +132,31 @@ def attention_vjp(q, k, v, go, scale):
                 gk[b, h] += c
                 gv[b, h] += e
     return gq, gk, gv
+
+
+def attention_vjp_keys(q, k, v, go, scale, b, h, keys):
+    """gK and gV of ``attention_vjp`` for selected key rows of one (b, h) head.
+
+    A key's gradients sum over every query: gK_j = s sum_i gS_ij q_i and
+    gV_j = sum_i P_ij gO_i, where P_ij and gS_ij need the whole row i (its
+    softmax normaliser and D_i = sum_j' P_ij' gP_ij').  So every query row is
+    still processed, in chunks, with all keys for P and D, and only the
+    selected key columns are kept for the sums.  Returns (gK, gV) for ``keys``
+    (an int array), float64.
+    """
+    keys = np.asarray(keys, dtype=np.int64)
+    qb, kb, vb, gob = (_f64(t[b, h]) for t in (q, k, v, go))
+    gk = np.zeros((len(keys), kb.shape[-1]))
+    gv = np.zeros((len(keys), vb.shape[-1]))
+    for r0 in range(0, qb.shape[0], ROW_CHUNK):
+        r1 = min(qb.shape[0], r0 + ROW_CHUNK)
+        _, _, P = _head_forward(qb[r0:r1], kb, vb, scale)
+        gP = gob[r0:r1] @ vb.T
+        D = (P * gP).sum(axis=1, keepdims=True)
+        gS = P[:, keys] * (gP[:, keys] - D)
+        gk += scale * (gS.T @ qb[r0:r1])
+        gv += P[:, keys].T @ gob[r0:r1]
+    return gk, gv
 
 
 def attention(q, k, v, scale):

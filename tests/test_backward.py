@@ -65,10 +65,10 @@ def test_backward_recipes_reduced(name):
 
 
 def test_backward_video_full_size():
-    """One head of the 1.3B-video shape (N = 32760): gQ on sampled rows against
-    the oracle; gK, gV (sums over all 32760 queries) through the adjoint
-    identity <gO, dO(t)> = <gQ, tq> + <gK, tk> + <gV, tv> with the JVP kernel's
-    dO for the workload's tangents."""
+    """One head of the 1.3B-video shape (N = 32760): gQ on sampled query rows
+    and gK, gV (sums over all 32760 queries) on sampled key rows against the
+    oracle, and all three through the adjoint identity <gO, dO(t)> = <gQ, tq> +
+    <gK, tk> + <gV, tv> with the JVP kernel's dO for independent tangents."""
     x, s = make_inputs("video_1p3b", heads=[0])
     g = to_device(x)
     go = g["dq"]
@@ -93,6 +93,14 @@ def test_backward_video_full_size():
     scale_ref = float((go.double().abs() * dO.double().abs()).sum())
     assert abs(lhs - rhs) <= 1e-2 * scale_ref
     assert torch.isfinite(gk).all() and torch.isfinite(gv).all()
+    # gK, gV rows element by element: sampled keys (each a sum over all 32760
+    # queries) against the oracle, which processes every query row for them
+    keys = np.unique(np.concatenate([rng.choice(32760, 40, replace=False), [0, 32759]]))
+    rk, rv = oracle.attention_vjp_keys(x["q"], x["k"], x["v"], x["dq"], s, 0, 0, keys)
+    for name, got, want in (("gK", gk, rk), ("gV", gv, rv)):
+        m = metrics(got[0, 0, keys].double().cpu().numpy(), want)
+        print(f"[bwd video_1p3b full] {name} rows: {m}", flush=True)
+        assert m["rel_frob"] <= 1e-2 and m["max_rel"] <= 2e-2, (name, m)
 
 
 def test_backward_text_cross_full_size():

@@ -8,7 +8,9 @@ things other than the function itself.
   gradient of the scalar <gO, O> one input element at a time);
 * closed forms: a single key (gQ = gK = 0, gV = sum of gO rows) and uniform
   attention (Q = 0);
-* torch.autograd of a plain torch fp64 attention (a library special case).
+* torch.autograd of a plain torch fp64 attention (a library special case);
+* the sampled-keys form (attention_vjp_keys) equals the key rows of the
+  whole-tensor gradients.
 
 Planted mistakes in a copy of the oracle (CPU only) must each fail a pin.
 """
@@ -117,8 +119,22 @@ def pin_vjp_torch_autograd(orc):
         _close(a, b.numpy(), 1e-12, name)
 
 
+def pin_vjp_keys(orc):
+    """The sampled-keys form equals the key rows of the whole-tensor gradients
+    (pinned above), with chunks of query rows that split the rows unevenly."""
+    rng = np.random.default_rng(16)
+    q, k, v, go = _inputs(rng, 2, 3, 1200, 37, 8, 1.5)
+    s = 0.3
+    _, gk, gv = orc.attention_vjp(q, k, v, go, s)
+    for b, h in ((0, 0), (1, 2)):
+        keys = np.array([0, 5, 17, 36])
+        a, c = orc.attention_vjp_keys(q, k, v, go, s, b, h, keys)
+        _close(a, gk[b, h, keys], 1e-12, "gK rows")
+        _close(c, gv[b, h, keys], 1e-12, "gV rows")
+
+
 PINS = [pin_vjp_adjoint, pin_vjp_complex_step, pin_vjp_single_key, pin_vjp_uniform,
-        pin_vjp_torch_autograd]
+        pin_vjp_torch_autograd, pin_vjp_keys]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -137,6 +153,10 @@ MUTATIONS = [
     ("gQ and gK swapped operands", "return scale * (gS @ k), scale * (gS.T @ q), gV", "return scale * (gS @ v), scale * (gS.T @ q), gV"),
     ("gK from the wrong side", "return scale * (gS @ k), scale * (gS.T @ q), gV", "return scale * (gS @ k), scale * (gS.T @ go), gV"),
     ("chunked gK not accumulated", "gk[b, h] += c", "gk[b, h] = c"),
+    ("sampled keys: D from the kept columns only", "gS = P[:, keys] * (gP[:, keys] - D)",
+     "gS = P[:, keys] * (gP[:, keys] - (P[:, keys] * gP[:, keys]).sum(axis=1, keepdims=True))"),
+    ("sampled keys: chunks not accumulated", "gv += P[:, keys].T @ gob[r0:r1]",
+     "gv = P[:, keys].T @ gob[r0:r1]"),
 ]
 
 
