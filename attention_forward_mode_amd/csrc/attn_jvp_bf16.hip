@@ -1,8 +1,9 @@
 // attn_jvp_bf16.hip -- fused attention forward + JVP for gfx950, bf16 inputs.
 //
 // The operation (rCM record LIT-783 in the Anthology of the SOTA, "Key
-// takeaways", "JVP at production scale", paper §3.2 / App. C: FlashAttention-2
-// and its Jacobian-vector product in one tiled pass):
+// takeaways", "JVP at production scale", paper §3.2 / App. C: the
+// FlashAttention-2 forward fused with its directional derivative in a single
+// sweep over key tiles):
 //   O = softmax(s Q K^T) V,  dO = (P * (dS - mu)) V + P dV,
 //   dS = s (dQ K^T + Q dK^T),  mu = rowsum(P * dS),  lse = ln rowsum exp(s Q K^T),
 //   and mu is also the tangent of lse.

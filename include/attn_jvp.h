@@ -4,9 +4,10 @@
  *
  * The operation.  The rCM record in the Anthology of the SOTA (LIT-783, "Key
  * takeaways", bullet "JVP at production scale", paper §3.2 and App. C)
- * describes one tiled pass that computes FlashAttention-2 together with its
- * Jacobian-vector product, for self- and cross-attention, with the tangents
- * of Q, K and V laid out exactly like Q, K and V.  Per (batch b, head h), for
+ * credits a kernel that fuses the FlashAttention-2 forward with its
+ * directional derivative in a single sweep over key tiles, whether the keys
+ * come from the queries' own sequence or from another one, and with the
+ * tangents of Q, K and V laid out like Q, K and V.  Per (batch b, head h), for
  * queries i < Nq, keys j < Nk, head dim d and the scalar `scale` s:
  *
  *   S   = s Q K^T,  P = row-softmax(S),  O = P V,
@@ -54,9 +55,12 @@
  * caller, on the current HIP device.  Outputs must not alias inputs or each
  * other.  Every call is asynchronous on `stream` (NULL = the null stream) and
  * never synchronises the host.  The calls hold no state across calls apart
- * from a per-device memory pool used by attn_jvp_fwd for its workspace
- * (stream-ordered hipMallocFromPoolAsync / hipFreeAsync); attn_jvp_fwd_ws uses
- * a caller-provided workspace instead.
+ * from a per-device memory pool used by attn_jvp_fwd (and the calls below
+ * given a NULL workspace) for its workspace: stream-ordered
+ * hipMallocFromPoolAsync / hipFreeAsync, up to 2 GiB kept cached between
+ * calls; concurrent calls from several threads or streams are safe.
+ * attn_jvp_fwd_ws takes a caller-provided workspace instead, and
+ * attn_jvp_fwd_noalloc a fixed buffer of the library's.
  *
  * Tuning.  The environment variable ATTN_JVP_TILE, read on every call, can
  * force the workgroup size of the bf16 kernels: 128 or 256 query rows for the

@@ -9,11 +9,12 @@ header, table or helper with it.
 What it computes
 ----------------
 The rCM record on the Anthology of the SOTA (LIT-783, "Key takeaways", the
-"JVP at production scale (paper §3.2, App. C)" bullet) describes one fused pass
-that produces FlashAttention-2's output together with its Jacobian-vector
-product, for self- and cross-attention, with the tangents of Q, K and V laid out
-like Q, K and V themselves.  The pages give no formula, so this oracle is the
-plain mathematical definition of that result, not the tiled algorithm:
+"JVP at production scale (paper §3.2, App. C)" bullet) credits a kernel that
+returns the FlashAttention-2 forward result and its directional derivative
+along tangents of Q, K and V (shaped like Q, K and V) from a single fused
+sweep, for keys from the queries' own sequence or from another one.  The pages
+give no formula, so this oracle is the plain mathematical definition of that
+result, not the tiled algorithm:
 
   per (batch, head), queries i < Nq, keys j < Nk, head dim d, scalar scale s
 

@@ -76,6 +76,49 @@ def test_pool_entry_point_matches_workspace_entry_point():
     assert torch.equal(o1, o2) and torch.equal(t1, t2) and torch.equal(l1, l2)
 
 
+def test_pool_entry_point_from_two_threads():
+    """attn_jvp_fwd called from two host threads at once, each on its own
+    stream (default priority), each taking its workspace from the library's
+    pool: every call equals attn_jvp_fwd_ws's result bit for bit."""
+    import threading
+
+    cases = []
+    for seed, (Nq, Nk) in enumerate([(333, 1500), (700, 271)]):
+        x, s = make_inputs("image_dit", Nq=Nq, Nk=Nk, heads=[seed, seed + 1])
+        g = to_device(x)
+        ref = ajvp.attn_jvp_fwd(*[g[n] for n in NAMES], scale=s)  # caller workspace (_ws)
+        outs = [tuple(torch.empty_like(t) for t in ref) for _ in range(4)]
+        cases.append((g, s, ref, outs))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    start = threading.Barrier(2)
+    rcs = [[], []]
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def work(i):
+        g, s, _, outs = cases[i]
+        B, H, Nq, d = g["q"].shape
+        st = ctypes.c_void_p(streams[i].cuda_stream)
+        start.wait()
+        for o, to, lse in outs:
+            rcs[i].append(ajvp.lib().attn_jvp_fwd(*[p(g[n]) for n in NAMES], p(o), p(to), p(lse),
+                                                  B, H, Nq, g["k"].shape[2], d, ctypes.c_float(s),
+                                                  st))
+
+    print("  launch attn_jvp_fwd from two threads on two streams", flush=True)
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert rcs == [[0] * 4, [0] * 4], rcs
+    for g, s, ref, outs in cases:
+        for out in outs:
+            for a, b in zip(out, ref):
+                assert torch.equal(a, b)
+
+
 def test_rejected_call_leaves_outputs_untouched():
     g, s = _inputs()
     B, H, Nq, d = g["q"].shape
