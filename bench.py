@@ -52,7 +52,8 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attn+JVP TFLOP/s and % bf16 MFMA peak at 1 GPU (N=32760, H=12, d=128)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_jvp_bf16_d128_video_1p3b.txt")
 KERNEL_SOURCES = ["attention_forward_mode_amd/csrc/attn_jvp_bf16.hip",
-                  "attention_forward_mode_amd/csrc/cdna4.hpp"]
+                  "attention_forward_mode_amd/csrc/cdna4.hpp",
+                  "attention_forward_mode_amd/csrc/range.hpp"]
 
 
 def kernel_source_hash():
