@@ -381,20 +381,31 @@ __device__ __attribute__((always_inline)) inline void sm_pv_phase(
   }
 }
 
-// One 32-key block (block `kb` of the 64-key tile image in `stage`): both
-// phases back to back.
+// One 32-key block whose K, dK, V^T and dV^T fragments start at the four
+// given LDS addresses (fragment f of a part at its base + f KiB): both phases
+// back to back.
+template <int D, int kMode, bool kMask, bool kScaleDV, typename Issue>
+__device__ __attribute__((always_inline)) inline void jvp_block_at(
+    RowState<D>& st, const char* kp, const char* dkp, const char* vp, const char* dvp,
+    const u32x4* qf, const u32x4* dqf, int l32, int g, int key0, int Nk, float c_log2,
+    float scale, uint32_t dv_mul, Issue issue) {
+  const int lane16 = 16 * l32 + 512 * g;  // this lane's 16 bytes of a fragment
+  f32x16 s, ds;
+  qk_phase<D, kMode>(s, ds, kp, dkp, qf, dqf, lane16, issue);
+  sm_pv_phase<D, kMode, kMask, kScaleDV>(st, s, ds, vp, dvp, lane16, g, key0, Nk, c_log2, scale,
+                                         dv_mul, issue);
+}
+
+// Block `kb` of the 64-key tile image in `stage`.
 template <int D, int kMode, bool kMask, bool kScaleDV, typename Issue>
 __device__ __attribute__((always_inline)) inline void jvp_block(
     RowState<D>& st, const char* stage, int kb, const u32x4* qf, const u32x4* dqf, int l32,
     int g, int key0, int Nk, float c_log2, float scale, uint32_t dv_mul, Issue issue) {
   using G = Geo<D, Mode<kMode>::kKV>;
-  const int lane16 = 16 * l32 + 512 * g;  // this lane's 16 bytes of a fragment
   const int kf0 = kb * G::kKS * kDmaBytes, vf0 = 2 * kb * G::kCB * kDmaBytes;
-  f32x16 s, ds;
-  qk_phase<D, kMode>(s, ds, stage + kf0, stage + G::kOffdK + kf0, qf, dqf, lane16, issue);
-  sm_pv_phase<D, kMode, kMask, kScaleDV>(st, s, ds, stage + G::kOffV + vf0,
-                                         stage + G::kOffdV + vf0, lane16, g, key0, Nk, c_log2,
-                                         scale, dv_mul, issue);
+  jvp_block_at<D, kMode, kMask, kScaleDV>(st, stage + kf0, stage + G::kOffdK + kf0,
+                                          stage + G::kOffV + vf0, stage + G::kOffdV + vf0, qf,
+                                          dqf, l32, g, key0, Nk, c_log2, scale, dv_mul, issue);
 }
 
 // One full tile: the copy of the next tile image into `next` is spread over
@@ -666,16 +677,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
                             sc.t);
 }
 
-// ---- short key ranges: 128-row workgroups, one LDS stage, two per CU ----
+// ---- short key ranges: 128-row workgroups, two per CU ----
 // With few key tiles per work item (cross-attention to a short text, or a
 // short split-KV range) the 256-row kernel spends a large share of its time
 // loading Q, dQ and storing O, dO, and with one workgroup per CU nothing runs
-// beside those memory phases.  Here a workgroup holds 4 waves (128 rows) and
-// one 64 KiB stage, so two fit on a CU (registers: 2 x 4 waves x 256 = two
-// waves per SIMD, as before; LDS: 2 x 64 KiB) and one computes while the other
-// loads, stores or waits for its next tile.  Per row the arithmetic is that of
-// the 256-row kernel (same blocks, same key order), so the results are the
-// same bit for bit.
+// beside those memory phases.  Here a workgroup holds 4 waves (128 rows), so
+// two fit on a CU (registers: 2 x 4 waves x 256 = two waves per SIMD, as
+// before) and one computes while the other loads, stores or waits.  The key
+// range is streamed in 32-key halves of the tile images: the half-stage holds
+// one block's K, dK, V^T and dV^T fragments (32 KiB at d = 128 with the
+// tangents), and two half-stages alternate, so the copy of the next block
+// runs under the products of the current one (LDS: 2 x 64 KiB per CU at
+// d = 128).  Per row the arithmetic is that of the 256-row kernel (same
+// blocks, same key order), so the results are the same bit for bit.
 constexpr int kShortWaves = 4;
 constexpr int kShortThreads = 64 * kShortWaves;
 constexpr int kShortBR = kShortWaves * kRowsPerWave;  // query rows per workgroup
@@ -686,6 +700,45 @@ constexpr int kShortBR = kShortWaves * kRowsPerWave;  // query rows per workgrou
 // row costs more than the overlap gains).
 constexpr int kShortMaxTiles = 16;
 
+// One 32-key block of a tile image as the short kernel stages it: its K, dK,
+// V^T, dV^T parts (kF fragments each; K and dK blocks are kKS fragments, V^T
+// and dV^T blocks 2 kCB, both D / 16) back to back.  Fragment i of block kb of
+// tile kt comes from image offset kt img + (i / kF) kPart + kb kF KiB + (i % kF)
+// KiB, since every part of the image spans the same kPart bytes.
+template <int D, bool kKV>
+struct HalfGeo {
+  using G = Geo<D, kKV>;
+  static constexpr int kF = D / 16;
+  static constexpr int kPart = G::kKTile;
+  static constexpr int kParts = 2 * G::kNT;
+  static constexpr int kBytes = kParts * kF * kDmaBytes;
+  static constexpr int kPerWave = kBytes / (kShortWaves * kDmaBytes);
+  static_assert(G::kKTile == G::kVTile && G::kOffV == G::kNT * kPart && 2 * G::kCB == kF &&
+                    G::kKS == kF && kPerWave * kShortWaves * kDmaBytes == kBytes,
+                "half-stage layout");
+};
+
+// One block of the short kernel: computed from half-stage `cur` while
+// copy(next, slot) fills the other half-stage over the block's first steps.
+// As in tile_step, the two restrict-qualified pointers name disjoint halves of
+// the LDS, so reads of `cur` need not wait for the copy into `next`.
+template <int D, int kMode, bool kMask, bool kScaleDV, typename Copy>
+__device__ __attribute__((always_inline)) inline void short_block(
+    char* __restrict__ next, const char* __restrict__ cur, Copy copy, RowState<D>& st,
+    const u32x4* qf, const u32x4* dqf, int l32, int g, int key0, int Nk, float c_log2,
+    float scale, uint32_t dv_mul) {
+  using M = Mode<kMode>;
+  using G = Geo<D, M::kKV>;
+  using HG = HalfGeo<D, M::kKV>;
+  const char* dkp = cur + (M::kKV ? HG::kF * kDmaBytes : 0);
+  const char* vp = cur + G::kNT * HG::kF * kDmaBytes;
+  const char* dvp = vp + (M::kKV ? HG::kF * kDmaBytes : 0);
+  jvp_block_at<D, kMode, kMask, kScaleDV>(st, cur, dkp, vp, dvp, qf, dqf, l32, g, key0, Nk,
+                                          c_log2, scale, dv_mul, [&](int slot) {
+                                            if (slot < HG::kPerWave) copy(next, slot);
+                                          });
+}
+
 template <int D, int kMode, bool kOutBf16>
 __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ tq,
@@ -694,7 +747,8 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
     int nbh, int tps, Extents ext, float scale, float c_log2) {
   using M = Mode<kMode>;
   using G = Geo<D, M::kKV>;
-  __shared__ __attribute__((aligned(1024))) char smem[G::kImgBytes];
+  using HG = HalfGeo<D, M::kKV>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * HG::kBytes];
 
   // work item: as in attn_jvp_bf16_kernel, with row tiles of kShortBR rows
   const uint32_t wg = blockIdx.x, nwg = gridDim.x;
@@ -718,17 +772,18 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
   const auto rimg = make_rsrc(img + (size_t)bh * sb, sb);
   const uint32_t hdr = (uint32_t)ntiles * G::kImgBytes;
 
-  // Copy of tile image kt into the stage: this wave's quarter, 1 KiB per
-  // instruction, lane l moving bytes 16 l .. 16 l + 15 of each KiB.
-  constexpr int kPer = G::kImgBytes / (kShortWaves * kDmaBytes);
-  const uint32_t wave_part = (uint32_t)wave * kPer * kDmaBytes;
-  auto copy_one = [&](int kt, char* stage, int j) {
-    const uint32_t src = (uint32_t)kt * G::kImgBytes + wave_part + j * kDmaBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rimg, (lds_ptr_t)(stage + wave_part + j * kDmaBytes),
-                                             16, lane * 16, src, 0, 0);
+  // Copy of block h of the range (tile t0 + h / 2, block h % 2) into a
+  // half-stage: this wave's kPerWave consecutive fragments of it, 1 KiB per
+  // instruction, lane l moving bytes 16 l .. 16 l + 15.
+  auto copy_half = [&](int h, char* stage, int j) {
+    const int i = wave * HG::kPerWave + j;
+    const uint32_t src = (uint32_t)(t0 + (h >> 1)) * G::kImgBytes + (i / HG::kF) * HG::kPart +
+                         ((h & 1) * HG::kF + i % HG::kF) * kDmaBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rimg, (lds_ptr_t)(stage + i * kDmaBytes), 16,
+                                             lane * 16, src, 0, 0);
   };
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) copy_one(t0, smem, j);
+  for (int j = 0; j < HG::kPerWave; ++j) copy_half(0, smem, j);
 
   u32x4 qf[G::kKS], dqf[G::kKS];
   const uint32_t qrow = row_ok ? (bh * (uint32_t)Nq + row) * D * 2 : 0x80000000u;
@@ -751,34 +806,36 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
   st.l = 0.f;
   st.u = 0.f;
 
-  // Tile kt: wait for its copy (every wave's share) and make it visible, compute
-  // both blocks, then a barrier retires every read of the stage before the
-  // copy of tile kt + 1 overwrites it.  Both forms of the loop (with and
-  // without the dV^T rescale) run the same barriers.
-  auto none = [](int) {};
-  auto tile_ready = [&]() {
+  // Block h: wait for its copy (every wave's share) and make it visible; the
+  // same barrier retires every read of block h - 1, whose half-stage the copy
+  // of block h + 1 (issued over the first steps of block h) overwrites.  The
+  // two blocks of the last tile are masked (keys >= Nk).  Both forms of the
+  // loop (with and without the dV^T rescale) run the same barriers.
+  const int nh = 2 * (t1 - t0);
+  auto block_ready = [&]() {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  const int kLast = t1 - 1;
+  auto block = [&](int h, auto mask, auto scale_dv, bool copy_next) {
+    constexpr bool kMk = decltype(mask)::value, kS = decltype(scale_dv)::value;
+    short_block<D, kMode, kMk, kS>(
+        smem + ((h + 1) & 1) * HG::kBytes, smem + (h & 1) * HG::kBytes,
+        [&](char* next, int j) {
+          if (copy_next) copy_half(h + 1, next, j);
+        },
+        st, qf, dqf, l32, g, (t0 + (h >> 1)) * kBC + 32 * (h & 1), Nk, c_log2, sc.s_t,
+        sc.dv_mul);
+  };
   auto key_loop = [&](auto scale_dv) {
-    constexpr bool kS = decltype(scale_dv)::value;
-    for (int kt = t0; kt < kLast; ++kt) {
-      tile_ready();
-      jvp_block<D, kMode, false, kS>(st, smem, 0, qf, dqf, l32, g, 0, Nk, c_log2, sc.s_t,
-                                     sc.dv_mul, none);
-      jvp_block<D, kMode, false, kS>(st, smem, 1, qf, dqf, l32, g, 0, Nk, c_log2, sc.s_t,
-                                     sc.dv_mul, none);
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) copy_one(kt + 1, smem, j);
+    int h = 0;
+    for (; h < nh - 2; ++h) {
+      block_ready();
+      block(h, Flag<false>{}, scale_dv, true);
     }
-    tile_ready();
-    const int kl = kLast * kBC;
-    jvp_block<D, kMode, true, kS>(st, smem, 0, qf, dqf, l32, g, kl, Nk, c_log2, sc.s_t,
-                                  sc.dv_mul, none);
-    jvp_block<D, kMode, true, kS>(st, smem, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, sc.s_t,
-                                  sc.dv_mul, none);
+    block_ready();
+    block(h, Flag<true>{}, scale_dv, true);
+    block_ready();
+    block(h + 1, Flag<true>{}, scale_dv, false);
   };
   if (M::kKV && sc.slow)
     key_loop(Flag<M::kKV>{});
