@@ -195,7 +195,7 @@ def calib_copy(nbytes=1 << 30, reps=5):
 
 # flops per (b, h) and Nq Nk d of each mode: the contractions it performs
 # (bwd: S, gP, gV, gQ, gK; the kernels form S and gP twice, 14 Nq Nk d in all)
-MODE_FLOPS = {"jvp": 12.0, "frozen": 8.0, "fwd": 4.0, "bwd": 10.0}
+MODE_FLOPS = {"jvp": 12.0, "splitkv": 12.0, "frozen": 8.0, "fwd": 4.0, "bwd": 10.0}
 
 
 def bench_variant(args, ajvp, w, g, x, scale):
@@ -210,6 +210,9 @@ def bench_variant(args, ajvp, w, g, x, scale):
         ws = torch.empty(ajvp.attn_bwd_workspace_bytes(B, H, Nq, Nk, d), dtype=torch.uint8,
                          device="cuda")
         o_f, lse_f = ajvp.attn_fwd(g["q"], g["k"], g["v"], scale=scale)
+    elif args.mode == "splitkv":
+        ws = torch.empty(ajvp.attn_jvp_splitkv_workspace_bytes(B, H, Nq, Nk, d, args.nsplit),
+                         dtype=torch.uint8, device="cuda")
     else:
         ws = torch.empty(ajvp.attn_jvp_workspace_bytes(B, H, Nk, d), dtype=torch.uint8,
                          device="cuda")
@@ -218,6 +221,9 @@ def bench_variant(args, ajvp, w, g, x, scale):
         if args.mode == "bwd":  # the cotangent gO is the dQ draw, N(0, 0.1^2)
             return ajvp.attn_bwd(g["q"], g["k"], g["v"], o_f, g["dq"], lse_f, scale=scale,
                                  workspace=ws)
+        if args.mode == "splitkv":
+            return ajvp.attn_jvp_fwd_splitkv(g["q"], g["k"], g["v"], g["dq"], g["dk"], g["dv"],
+                                             scale=scale, nsplit=args.nsplit, workspace=ws)
         if args.mode == "fwd":
             return ajvp.attn_fwd(g["q"], g["k"], g["v"], scale=scale, out_dtype=out_dtype,
                                  workspace=ws)
@@ -244,7 +250,8 @@ def bench_variant(args, ajvp, w, g, x, scale):
     assert all(torch.isfinite(t).all() for t in out if t is not None), "non-finite output"
     fl = MODE_FLOPS[args.mode] * B * H * Nq * Nk * d
     tflops = fl / (ms / 1e3) / 1e12
-    names = {"jvp": "attn+JVP", "frozen": "attn+JVP with frozen keys (dK = dV = 0)",
+    names = {"jvp": "attn+JVP", "splitkv": "attn+JVP, key tiles in ranges merged (split-KV)",
+             "frozen": "attn+JVP with frozen keys (dK = dV = 0)",
              "fwd": "forward attention", "bwd": "attention backward (gradients through O)"}
     res = {
         "metric": f"{names[args.mode]} TFLOP/s at 1 GPU ({args.workload})",
@@ -254,13 +261,15 @@ def bench_variant(args, ajvp, w, g, x, scale):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded Gaussians)",
         "config": {"workload": f"{w.name}: {w.description}", "B": B, "H": H, "Nq": Nq, "Nk": Nk,
                    "d": d, "scale": scale, "mode": args.mode,
+                   **({"nsplit": args.nsplit or "auto"} if args.mode == "splitkv" else {}),
                    "outputs": ("fp32 gQ, gK, gV" if args.mode == "bwd" else
                                f"{args.out_dtype} O" + ("" if args.mode == "fwd" else ", dO") +
                                ", fp32 lse")},
         "flops_per_step": fl,
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"kernel": {"bwd": "pack_q + pack_k + bwd_kv + bwd_q (one call)",
-                                "fwd": "pack_kv + attn_fwd_bf16_kernel (one call, pack included)"}
+                                "fwd": "pack_kv + attn_fwd_bf16_kernel (one call, pack included)",
+                                "splitkv": "pack_kv + key-range JVP kernel + merge (one call)"}
                                .get(args.mode, f"pack_kv + {jvp_kernel_name(Nk, d).split('<')[0]} "
                                                "(one call, pack included)"),
                      "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
@@ -312,10 +321,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video_1p3b")
-    ap.add_argument("--mode", choices=["jvp", "frozen", "fwd", "bwd"], default="jvp",
+    ap.add_argument("--mode", choices=["jvp", "splitkv", "frozen", "fwd", "bwd"], default="jvp",
                     help="jvp: the full attention+JVP (the headline); frozen: dK = dV = 0 passed "
                          "as NULL (8 Nq Nk d flops); fwd: forward attention alone (4 Nq Nk d); "
-                         "bwd: the backward pass, gradients through O (10 Nq Nk d algorithmic)")
+                         "bwd: the backward pass, gradients through O (10 Nq Nk d algorithmic); "
+                         "splitkv: the full attention+JVP through attn_jvp_fwd_splitkv")
+    ap.add_argument("--nsplit", type=int, default=0,
+                    help="key-tile ranges of --mode splitkv (0: chosen by the library)")
     ap.add_argument("--out-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,

@@ -88,6 +88,17 @@ def test_video_14b_full_size():
 
 
 @pytest.mark.slow
+def test_video_14b_head_shard_full_size():
+    """One GPU's share of the 14B shape under an 8-way head split (H = 5), in
+    the launch configuration bench.py times for it."""
+    w = WORKLOADS["video_14b_shard8"]
+    x, s = make_inputs("video_14b_shard8")
+    outs = run(to_device(x), s)
+    q_out = outlier_rows(0, 0, w.Nq, w.outlier_frac)[:4].tolist()
+    check_sampled("video_14b_shard8 H5 N32760", x, s, outs, rows_per_head=24, extra_rows=q_out)
+
+
+@pytest.mark.slow
 def test_video_14b_fp32_full_size():
     x, s = make_inputs("video_14b_fp32")
     outs = run(to_device(x), s)

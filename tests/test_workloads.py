@@ -79,6 +79,18 @@ def test_outliers():
         assert torch.equal(f[t].to(torch.bfloat16), g[t])
 
 
+def test_head_shard_is_heads_of_the_full_draw():
+    """One GPU's share of the 14B shape under an 8-way head split is heads 0-4
+    of the 40-head draw, value for value."""
+    w = WORKLOADS["video_14b_shard8"]
+    assert (w.B, w.H, w.Nq, w.Nk, w.d) == (1, 5, 32760, 32760, 128)
+    a, s1 = make_inputs("video_14b_shard8", Nq=300, Nk=400)
+    b, s2 = make_inputs("video_14b", Nq=300, Nk=400, heads=range(5))
+    assert s1 == s2
+    for t in TENSORS:
+        assert torch.equal(a[t], b[t])
+
+
 def test_unrounded_draws_round_to_the_bf16_draws():
     """dtype="fp32" gives the draws before their bf16 rounding: rounding them
     reproduces the bf16 workload exactly (no row-max step), or to within one

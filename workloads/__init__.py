@@ -77,6 +77,9 @@ WORKLOADS = {w.name: w for w in [
     Workload("video_14b_fp32", "fp32 run of the 14B video shape on its first 2 heads (unrounded "
              "draws, same outliers)", 1, 2, 32760, 32760, 128, "fp32",
              outlier_frac=0.01, seed_H=40),
+    Workload("video_14b_shard8", "one GPU's share of the 14B video shape sharded by head over 8 "
+             "GPUs: heads 0-4 of the 40-head draw, B=1 H=5 N=32760 d=128", 1, 5, 32760, 32760,
+             128, "bf16", outlier_frac=0.01, seed_H=40),
 ]}
 
 
