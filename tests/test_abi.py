@@ -376,6 +376,10 @@ def test_splitkv_workspace_bytes():
     assert auto_count(1, 12, 32760, 32760, 128) == 1      # 1536 row tiles
     assert auto_count(1, 12, 32760, 512, 128) == 1        # cross-attention shape
     assert auto_count(2, 16, 4096, 4096, 128) == 1        # 512 row tiles
+    # one GPU's share of the 14B shape (H = 5): the JVP kernel's 640 row tiles
+    # fill 2.5 rounds of the CUs (it picks 2 ranges), the forward kernel's 320
+    # tiles of 512 rows 1.25 (it picks 3); the workspace covers the larger
+    assert auto_count(1, 5, 32760, 32760, 128) == 3
     assert auto_count(1, 12, 256, 32760, 128) > 8         # 12 row tiles, 512 key tiles
     assert 1 < auto_count(1, 1, 10, 512, 64) <= 2         # 8 key tiles: ranges of >= 4
     assert ajvp.attn_jvp_splitkv_workspace_bytes(1, 1, 10, 512, 64, -1) == 0
