@@ -257,6 +257,7 @@ def bench_variant(args, ajvp, w, g, x, scale):
         "metric": f"{names[args.mode]} TFLOP/s at 1 GPU ({args.workload})",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "ms_per_step_min": round(min(per), 4),
+        "ms_per_step_median": round(sorted(per)[len(per) // 2], 4),
         "wall_ms_timed_region": round(wall_ms, 2), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded Gaussians)",
         "config": {"workload": f"{w.name}: {w.description}", "B": B, "H": H, "Nq": Nq, "Nk": Nk,
