@@ -512,6 +512,26 @@ struct WaveScale {
   bool slow;
 };
 
+// A negative scale s: s Q K^T = |s| (-Q) K^T and s (dQ K^T + Q dK^T) =
+// |s| ((-dQ) K^T + (-Q) dK^T), so flipping the sign bits of the Q and dQ
+// fragments (exact in bf16) and working with |s| from here on gives every
+// scaled logit and tangent term unchanged, while the running max of the
+// online softmax is taken over the logits as they are (max_j s S_ij, not
+// s max_j S_ij).
+template <int D>
+__device__ __attribute__((always_inline)) inline void flip_negative_scale(
+    u32x4* qf, u32x4* dqf, float& scale, float& c_log2) {
+  if (scale < 0.f) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] ^= 0x80008000u;
+      dqf[ks] ^= 0x80008000u;
+    }
+    scale = -scale;
+    c_log2 = -c_log2;
+  }
+}
+
 template <int D, bool kKV>
 __device__ __attribute__((always_inline)) inline WaveScale wave_scale(
     __amdgpu_buffer_rsrc_t rimg, uint32_t hdr, int ntiles, const u32x4* qf, const u32x4* dqf,
@@ -626,6 +646,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
     dqf[ks] = buf_load16(rtq, off);
   }
 
+  flip_negative_scale<D>(qf, dqf, scale, c_log2);
   const WaveScale sc = wave_scale<D, M::kKV>(rimg, hdr, ntiles, qf, dqf, scale, lane);
 
   RowState<D> st;
@@ -794,6 +815,7 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
     dqf[ks] = buf_load16(rtq, off);
   }
 
+  flip_negative_scale<D>(qf, dqf, scale, c_log2);
   const WaveScale sc = wave_scale<D, M::kKV>(rimg, hdr, ntiles, qf, dqf, scale, lane);
 
   RowState<D> st;
@@ -1016,6 +1038,14 @@ __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kerne
     const uint32_t qrow = row < Nq ? (bh * (uint32_t)Nq + row) * D * 2 : 0x80000000u;
 #pragma unroll
     for (int ks = 0; ks < G::kKS; ++ks) qf[rb][ks] = buf_load16(rq, qrow + (16 * ks + 8 * g) * 2);
+  }
+  // a negative scale: the logits from -Q with |s| (see flip_negative_scale)
+  if (c_log2 < 0.f) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < G::kKS; ++ks) qf[rb][ks] ^= 0x80008000u;
+    c_log2 = -c_log2;
   }
 
   FwdState<D, RB> st;

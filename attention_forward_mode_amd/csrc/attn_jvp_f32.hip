@@ -192,6 +192,19 @@ __device__ __attribute__((always_inline)) inline void attn_jvp_f32_body(
     qf[j] = __builtin_bit_cast(f32x4, buf_load16(rq, off));
     dqf[j] = __builtin_bit_cast(f32x4, buf_load16(rtq, off));
   }
+  // A negative scale s: s Q K^T = |s| (-Q) K^T and s dS = |s| dS of (-Q, -dQ),
+  // so negating the Q and dQ fragments (exact) and working with |s| keeps every
+  // scaled logit and tangent term, while the running max is taken over the
+  // logits as they are.
+  if (scale < 0.f) {
+#pragma unroll
+    for (int j = 0; j < G::kQ4; ++j) {
+      qf[j] = -qf[j];
+      dqf[j] = -dqf[j];
+    }
+    scale = -scale;
+    c_log2 = -c_log2;
+  }
 
   // Direct-to-LDS copies of the next 32-key tile (no staging registers): wave
   // w copies tensor w (K, dK, V, dV), kChunks 1 KiB loads, load n writing

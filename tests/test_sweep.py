@@ -1,0 +1,166 @@
+"""GPU parity over a seeded sweep of call configurations.
+
+Forty configurations drawn once from a fixed seed: batch and head counts,
+query and key lengths (biased to the places where the kernels change shape:
+multiples of 64 and 128 and one past them, the 16-tile switch between the
+128-row and 256-row kernels at 1024 keys), d = 64 or 128, a scale of either
+sign, NULL tangents, bf16 outputs, with and without lse and its tangent, and
+split-KV ranges.  Every output element is compared with the fp64 oracle
+(oracle.attention_jvp on the same bf16 inputs) under the gate of
+tests/test_parity.py: max-abs <= 2e-2 and relative Frobenius <= 1e-2.
+"""
+
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import attention_forward_mode_amd as ajvp
+import oracle
+
+from _gpu import metrics
+
+pytestmark = pytest.mark.gpu
+
+EDGES_Q = [1, 31, 32, 33, 127, 128, 129, 255, 256, 257, 383, 511, 512, 513]
+EDGES_K = [1, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1023, 1024, 1025, 1088, 1089]
+
+
+def _configs(n=40, seed=20261203):
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        d = rng.choice([64, 128])
+        Nq = rng.choice(EDGES_Q) if rng.random() < 0.6 else rng.randint(1, 600)
+        Nk = rng.choice(EDGES_K) if rng.random() < 0.6 else rng.randint(1, 1300)
+        scale = rng.choice([1.0, -1.0, rng.uniform(-2.5, 2.5)]) / math.sqrt(d)
+        out.append(dict(
+            i=i, B=rng.choice([1, 2]), H=rng.choice([1, 2, 3]), Nq=Nq, Nk=Nk, d=d, scale=scale,
+            null=rng.choice([(), ("dk", "dv"), ("dq",), ("dv",), ("dk",)]),
+            bf16_out=rng.random() < 0.25, lse=rng.random() < 0.8, tlse=rng.random() < 0.6,
+            nsplit=rng.choice([None, None, None, 0, 2, 3]), tsig=rng.choice([0.1, 1.0])))
+    return out
+
+
+CONFIGS = _configs()
+
+
+def _inputs(c):
+    g = torch.Generator().manual_seed(1000 + c["i"])
+    shape = lambda n: (c["B"], c["H"], n, c["d"])
+    x = {}
+    for name, n, sg in (("q", c["Nq"], 1.0), ("k", c["Nk"], 1.0), ("v", c["Nk"], 1.0),
+                        ("dq", c["Nq"], c["tsig"]), ("dk", c["Nk"], c["tsig"]),
+                        ("dv", c["Nk"], c["tsig"])):
+        x[name] = (torch.randn(*shape(n), generator=g) * sg).to(torch.bfloat16)
+    return x
+
+
+@pytest.mark.parametrize("c", CONFIGS, ids=lambda c: (
+    f"{c['i']}-B{c['B']}H{c['H']}q{c['Nq']}k{c['Nk']}d{c['d']}"))
+def test_sweep_vs_oracle(c):
+    x = _inputs(c)
+    dev = torch.device("cuda:0")
+    g = {n: t.to(dev) for n, t in x.items()}
+    tan = {n: (None if n in c["null"] else g[n]) for n in ("dq", "dk", "dv")}
+    print(f"  launch sweep {c}", flush=True)
+    if c["nsplit"] is None:
+        o, to, lse, tlse = ajvp.attn_jvp_fwd_ex(
+            g["q"], g["k"], g["v"], tan["dq"], tan["dk"], tan["dv"], scale=c["scale"],
+            lse=c["lse"], tlse=c["tlse"],
+            out_dtype=torch.bfloat16 if c["bf16_out"] else torch.float32)
+    else:
+        o, to, lse, tlse = ajvp.attn_jvp_fwd_splitkv(
+            g["q"], g["k"], g["v"], tan["dq"], tan["dk"], tan["dv"], scale=c["scale"],
+            nsplit=c["nsplit"], lse=c["lse"], tlse=c["tlse"])
+    torch.cuda.synchronize()
+    # the oracle takes the zero tensors the NULL tangents stand for
+    xz = {n: (torch.zeros_like(x[n]) if n in c["null"] else x[n]) for n in x}
+    O, dO, L, dL = oracle.attention_jvp(xz["q"], xz["k"], xz["v"], xz["dq"], xz["dk"], xz["dv"],
+                                        c["scale"], with_dlse=True)
+    got = [("O", o, O), ("dO", to, dO)]
+    if c["lse"]:
+        got.append(("lse", lse, L))
+    else:
+        assert lse is None
+    if c["tlse"]:
+        got.append(("tlse", tlse, dL))
+    else:
+        assert tlse is None
+    for name, a, want in got:
+        a = a.float().cpu().numpy().astype(np.float64)
+        assert np.isfinite(a).all(), (name, c)
+        m = metrics(a, want)
+        print(f"  [{c['i']}] {name}: {m}", flush=True)
+        # bf16 outputs add their own rounding (half an ulp: 2^-9 of the value)
+        tol = 2e-2 + (2.0 ** -8 * float(np.abs(want).max()) if c["bf16_out"] and
+                      name in ("O", "dO") else 0.0)
+        assert m["max_abs"] <= tol, (name, m, c)
+        if np.linalg.norm(want) > 0:
+            assert m["rel_frob"] <= 1e-2, (name, m, c)
+
+
+# Forward alone and the backward over a smaller seeded sweep of shapes, each
+# with a positive and a negative scale: O, lse against oracle.attention, and
+# gQ, gK, gV against oracle.attention_vjp (cotangent gO drawn like dQ), under
+# the gates of tests/test_variants.py and tests/test_backward.py.
+def _small_configs(n=8, seed=7):
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        d = rng.choice([64, 128])
+        out.append(dict(i=i, B=rng.choice([1, 2]), H=rng.choice([1, 2]),
+                        Nq=rng.choice(EDGES_Q + [rng.randint(1, 700)]),
+                        Nk=rng.choice(EDGES_K + [rng.randint(1, 1300)]), d=d))
+    return out
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0], ids=["pos", "neg"])
+@pytest.mark.parametrize("c", _small_configs(), ids=lambda c: (
+    f"{c['i']}-B{c['B']}H{c['H']}q{c['Nq']}k{c['Nk']}d{c['d']}"))
+def test_forward_and_backward_sweep(c, sign):
+    c = dict(c, i=100 + c["i"], tsig=0.1)
+    x = _inputs(c)
+    s = sign * (0.5 + 0.1 * c["i"] % 7) / math.sqrt(c["d"])
+    dev = torch.device("cuda:0")
+    g = {n: t.to(dev) for n, t in x.items()}
+    print(f"  launch fwd+bwd {c} scale={s:.4f}", flush=True)
+    o, lse = ajvp.attn_fwd(g["q"], g["k"], g["v"], scale=s)
+    gq, gk, gv = ajvp.attn_bwd(g["q"], g["k"], g["v"], o, g["dq"], lse, scale=s)
+    torch.cuda.synchronize()
+    O, L = oracle.attention(x["q"], x["k"], x["v"], s)
+    for name, a, want in (("O", o, O), ("lse", lse, L)):
+        m = metrics(a.double().cpu().numpy(), want)
+        print(f"  [{c['i']}] {name}: {m}", flush=True)
+        assert m["max_abs"] <= 2e-2 and m["rel_frob"] <= 1e-2, (name, m, c, s)
+    ref = oracle.attention_vjp(x["q"], x["k"], x["v"], x["dq"], s)
+    for name, a, want in zip(("gQ", "gK", "gV"), (gq, gk, gv), ref):
+        a = a.double().cpu().numpy()
+        assert np.isfinite(a).all(), (name, c, s)
+        m = metrics(a, want)
+        print(f"  [{c['i']}] {name}: {m}", flush=True)
+        if np.abs(want).max() < 1e-12:  # one key: gQ = gK = 0
+            assert m["max_abs"] <= 1e-5, (name, m, c, s)
+        else:
+            assert m["rel_frob"] <= 1e-2 and m["max_rel"] <= 2e-2, (name, m, c, s)
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0], ids=["pos", "neg"])
+@pytest.mark.parametrize("c", _small_configs(n=4, seed=11), ids=lambda c: (
+    f"{c['i']}-B{c['B']}H{c['H']}q{c['Nq']}k{c['Nk']}d{c['d']}"))
+def test_fp32_path_sweep(c, sign):
+    """The fp32 path under both signs of the scale: relative Frobenius <= 1e-5."""
+    c = dict(c, i=200 + c["i"], tsig=0.1)
+    x = {n: t.float() for n, t in _inputs(c).items()}
+    s = sign * 0.9 / math.sqrt(c["d"])
+    g = {n: t.to(torch.device("cuda:0")) for n, t in x.items()}
+    print(f"  launch fp32 {c} scale={s:.4f}", flush=True)
+    o, to, lse = ajvp.attn_jvp_fwd_f32(g["q"], g["k"], g["v"], g["dq"], g["dk"], g["dv"], scale=s)
+    torch.cuda.synchronize()
+    ref = oracle.attention_jvp(x["q"], x["k"], x["v"], x["dq"], x["dk"], x["dv"], s)
+    for name, a, want in zip(("O", "dO", "lse"), (o, to, lse), ref):
+        m = metrics(a.double().cpu().numpy(), want)
+        print(f"  [{c['i']}] {name}: {m}", flush=True)
+        assert m["rel_frob"] <= 1e-5, (name, m, c, s)
