@@ -113,6 +113,9 @@ static_assert(Geo<128, true>::kImgBytes == 65536 && Geo<64, true>::kImgBytes == 
 // of range.hpp (kHdrBytes): record = {int eV, int edV, uint flags}, the range
 // pass's partial maxima of |V| and |dV|, norm slots = {max |k_j|, max |dk_j|}.
 constexpr uint32_t kDvZero = 1u;  // flags: dV has no finite nonzero value (or no dV at all)
+
+// How a wave forms its tangent products (chosen per wave, see WaveScale).
+enum : int { kPathFast = 0, kPathScaleDV = 1, kPathSepU = 2 };
 template <int D, bool kKV>
 __host__ __device__ constexpr uint32_t slice_bytes(int ntiles) {
   return (uint32_t)ntiles * Geo<D, kKV>::kImgBytes + kHdrBytes;
@@ -258,11 +261,14 @@ __device__ __attribute__((always_inline)) inline int slot_key(int r, int g) {
 // them and adds the block's P V products with the V^T and dV^T fragments at
 // vbase, dvbase (fragment f of a part at base + f KiB, the tile image's
 // layout).  kMask: the block may hold keys >= Nk, which get p = 0 and
-// contribute nothing to u.  kScaleDV: the dV^T fragments are multiplied by
-// dv_mul (two equal fp16 powers of two) after their read, for a wave whose
-// tangent exponent is below the one dV was packed for.  `scale` is s 2^t, the
-// wave's scale of s P dS.  issue(slot) is called at the start of each step
-// (slots 0..kKS-1: the S/dS steps, then kKS.. the P V steps).
+// contribute nothing to u.  kPath (see WaveScale): kPathScaleDV multiplies
+// the dV^T fragments by dv_mul (two equal fp16 powers of two) after their
+// read, for a wave whose tangent exponent is below the one dV was packed for;
+// kPathSepU sums u from s P dS at its own power of two 2^tu (dv_mul then holds
+// the float s 2^tu), for a wave whose s P dS would sit far below fp16's range
+// at the exponent dV sets.  `scale` is s 2^t, the wave's scale of s P dS.
+// issue(slot) is called at the start of each step (slots 0..kKS-1: the S/dS
+// steps, then kKS.. the P V steps).
 // Online-softmax order: the accumulators hold sums normalised to the running
 // max m; a raised max rescales them by alpha = 2^(m_old - m_new) before this
 // block's P V is added.
@@ -290,7 +296,7 @@ __device__ __attribute__((always_inline)) inline void qk_phase(
   }
 }
 
-template <int D, int kMode, bool kMask, bool kScaleDV, typename Issue>
+template <int D, int kMode, bool kMask, int kPath, typename Issue>
 __device__ __attribute__((always_inline)) inline void sm_pv_phase(
     RowState<D>& st, f32x16 s, f32x16 ds, const char* vbase, const char* dvbase, int lane16,
     int g, int key0, int Nk, float c_log2, float scale, uint32_t dv_mul, Issue issue) {
@@ -318,9 +324,10 @@ __device__ __attribute__((always_inline)) inline void sm_pv_phase(
   // and sum_j (p_j s dS_j - mu p_j) cancels as it must.
   u32x4 p[2], pd[2];
   float lsum = 0.f, usum = 0.f;
+  const float su = __builtin_bit_cast(float, dv_mul);  // kPathSepU: s 2^tu
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    float pp[2], pdd[2];
+    float pp[2], pdd[2], pdu[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int r = 2 * q + e;
@@ -329,13 +336,17 @@ __device__ __attribute__((always_inline)) inline void sm_pv_phase(
       // unless the row's own Q or dQ is not finite)
       if (kMask && key0 + slot_key(r, g) >= Nk) pp[e] = 0.f;
       pdd[e] = pp[e] * ds[r] * scale;
+      if constexpr (kPath == kPathSepU) pdu[e] = pp[e] * ds[r] * su;
     }
     const uint32_t hp = pack_f16x2(pp[0], pp[1]);
     p[q >> 2][q & 3] = hp;
     lsum = add_f16x2(hp, lsum);
     const uint32_t hd = pack_f16x2(pdd[0], pdd[1]);
     pd[q >> 2][q & 3] = hd;
-    usum = add_f16x2(hd, usum);
+    if constexpr (kPath == kPathSepU)
+      usum = add_f16x2(pack_f16x2(pdu[0], pdu[1]), usum);
+    else
+      usum = add_f16x2(hd, usum);
   }
   st.l = st.l * alpha + lsum;
   st.u = st.u * alpha + usum;
@@ -374,7 +385,7 @@ __device__ __attribute__((always_inline)) inline void sm_pv_phase(
     st.accG[cb] = mma_f16(vf[step & 1], pd[t], st.accG[cb]);
     if constexpr (M::kKV) {
       u32x4 dvx = dvf[step & 1];
-      if constexpr (kScaleDV) dvx = mul_f16x8(dvx, dv_mul);
+      if constexpr (kPath == kPathScaleDV) dvx = mul_f16x8(dvx, dv_mul);
       st.accG[cb] = mma_f16(dvx, p[t], st.accG[cb]);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -384,7 +395,7 @@ __device__ __attribute__((always_inline)) inline void sm_pv_phase(
 // One 32-key block whose K, dK, V^T and dV^T fragments start at the four
 // given LDS addresses (fragment f of a part at its base + f KiB): both phases
 // back to back.
-template <int D, int kMode, bool kMask, bool kScaleDV, typename Issue>
+template <int D, int kMode, bool kMask, int kPath, typename Issue>
 __device__ __attribute__((always_inline)) inline void jvp_block_at(
     RowState<D>& st, const char* kp, const char* dkp, const char* vp, const char* dvp,
     const u32x4* qf, const u32x4* dqf, int l32, int g, int key0, int Nk, float c_log2,
@@ -392,18 +403,18 @@ __device__ __attribute__((always_inline)) inline void jvp_block_at(
   const int lane16 = 16 * l32 + 512 * g;  // this lane's 16 bytes of a fragment
   f32x16 s, ds;
   qk_phase<D, kMode>(s, ds, kp, dkp, qf, dqf, lane16, issue);
-  sm_pv_phase<D, kMode, kMask, kScaleDV>(st, s, ds, vp, dvp, lane16, g, key0, Nk, c_log2, scale,
+  sm_pv_phase<D, kMode, kMask, kPath>(st, s, ds, vp, dvp, lane16, g, key0, Nk, c_log2, scale,
                                          dv_mul, issue);
 }
 
 // Block `kb` of the 64-key tile image in `stage`.
-template <int D, int kMode, bool kMask, bool kScaleDV, typename Issue>
+template <int D, int kMode, bool kMask, int kPath, typename Issue>
 __device__ __attribute__((always_inline)) inline void jvp_block(
     RowState<D>& st, const char* stage, int kb, const u32x4* qf, const u32x4* dqf, int l32,
     int g, int key0, int Nk, float c_log2, float scale, uint32_t dv_mul, Issue issue) {
   using G = Geo<D, Mode<kMode>::kKV>;
   const int kf0 = kb * G::kKS * kDmaBytes, vf0 = 2 * kb * G::kCB * kDmaBytes;
-  jvp_block_at<D, kMode, kMask, kScaleDV>(st, stage + kf0, stage + G::kOffdK + kf0,
+  jvp_block_at<D, kMode, kMask, kPath>(st, stage + kf0, stage + G::kOffdK + kf0,
                                           stage + G::kOffV + vf0, stage + G::kOffdV + vf0, qf,
                                           dqf, l32, g, key0, Nk, c_log2, scale, dv_mul, issue);
 }
@@ -414,7 +425,7 @@ __device__ __attribute__((always_inline)) inline void jvp_block(
 // computed from `cur`.  The two stage pointers are restrict-qualified (they
 // name disjoint halves of the LDS), which tells the compiler that reads of
 // `cur` need not wait for the copy into `next`.
-template <int D, int kMode, bool kScaleDV, typename Copy>
+template <int D, int kMode, int kPath, typename Copy>
 __device__ __attribute__((always_inline)) inline void tile_step(
     char* __restrict__ next, const char* __restrict__ cur, Copy copy, RowState<D>& st,
     const u32x4* qf, const u32x4* dqf, int l32, int g, int Nk, float c_log2, float scale,
@@ -422,7 +433,7 @@ __device__ __attribute__((always_inline)) inline void tile_step(
   using G = Geo<D, Mode<kMode>::kKV>;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
-    jvp_block<D, kMode, false, kScaleDV>(st, cur, kb, qf, dqf, l32, g, 0, Nk, c_log2, scale,
+    jvp_block<D, kMode, false, kPath>(st, cur, kb, qf, dqf, l32, g, 0, Nk, c_log2, scale,
                                          dv_mul, [&](int slot) {
                                            if (kb == 0 && slot < G::kDmaPerWave) copy(next, slot);
                                          });
@@ -495,6 +506,10 @@ template <bool B>
 struct Flag {
   static constexpr bool value = B;
 };
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
 
 // A wave's fp16 exponents: eV of the slice (header record), and the tangent
 // exponent t of s P dS, from the bound |s dS_ij| <= |s| (|dq_i| Mk + |q_i| Mdk)
@@ -502,14 +517,20 @@ struct Flag {
 // fragments, fp64) and all keys of the slice (Mk, Mdk: the largest key norms,
 // from the header).
 // With dV present, t is the slice's edV - eV (dV was packed at 2^(eV + t))
-// unless the bound needs a smaller one; then `slow` is set and dv_mul = 2^(t -
-// edV + eV) rescales the dV^T fragments.  Without dV (frozen keys, or dV = 0)
-// any t is consistent and the bound alone sets it.
+// unless the bound needs a smaller one; then the path is kPathScaleDV and
+// dv_mul = 2^(t - edV + eV) rescales the dV^T fragments.  If instead the bound
+// is far below the range that t leaves to s P dS (bound 2^t < 1, so every
+// s P dS 2^t is under 16 and may sit among fp16's subnormals), the products
+// keep t (their part of dO is then below dV's by more than fp32 resolves) but
+// u, the sum behind mu and the tangent of lse, is taken from s P dS 2^tu with
+// tu from the bound (kPathSepU; dv_mul carries the float s 2^tu).  Without dV
+// (frozen keys, or dV = 0) any t is consistent and the bound alone sets it.
 struct WaveScale {
   int ev, t;
+  int eu;           // exponent of u: t, or tu on kPathSepU
   float s_t;        // scale 2^t
-  uint32_t dv_mul;  // two fp16 copies of 2^(t - edV + eV)
-  bool slow;
+  uint32_t dv_mul;  // kPathScaleDV: two fp16 copies of 2^(t - edV + eV); kPathSepU: s 2^tu
+  int path;         // kPathFast, kPathScaleDV or kPathSepU (wave-uniform)
 };
 
 // A negative scale s: s Q K^T = |s| (-Q) K^T and s (dQ K^T + Q dK^T) =
@@ -556,20 +577,28 @@ __device__ __attribute__((always_inline)) inline WaveScale wave_scale(
   const uint32_t flags = __builtin_amdgcn_readfirstlane(rec[2]);
   WaveScale w;
   w.ev = ev;
-  w.slow = false;
+  w.path = kPathFast;
   w.dv_mul = 0x3c003c00u;  // 1.0, 1.0
-  int t;
+  int t, tu;
   if (!kKV || (flags & kDvZero)) {
     t = product_exponent(b);
+    tu = t;
   } else {
     const int th = edv - ev;
-    const bool slow = __builtin_ldexp(b, th) > kProdSafe;  // false for NaN
+    const double bh = __builtin_ldexp(b, th);
+    const bool slow = bh > kProdSafe;  // false for NaN
     t = slow ? product_exponent(b) : th;
-    w.slow = __builtin_amdgcn_readfirstlane((int)slow) != 0;
-    const _Float16 m = (_Float16)__builtin_amdgcn_ldexpf(1.0f, t - th);
-    w.dv_mul = (uint32_t)__builtin_bit_cast(uint16_t, m) * 0x10001u;
+    tu = product_exponent(b);
+    w.path = __builtin_amdgcn_readfirstlane(slow ? kPathScaleDV : bh < 1.0 ? kPathSepU : kPathFast);
+    if (w.path == kPathSepU) {
+      w.dv_mul = __builtin_bit_cast(uint32_t, __builtin_amdgcn_ldexpf(scale, tu));
+    } else {
+      const _Float16 m = (_Float16)__builtin_amdgcn_ldexpf(1.0f, t - th);
+      w.dv_mul = (uint32_t)__builtin_bit_cast(uint16_t, m) * 0x10001u;
+    }
   }
   w.t = __builtin_amdgcn_readfirstlane(t);
+  w.eu = __builtin_amdgcn_readfirstlane(w.path == kPathSepU ? tu : t);
   w.dv_mul = __builtin_amdgcn_readfirstlane(w.dv_mul);
   w.s_t = __builtin_bit_cast(
       float, __builtin_amdgcn_readfirstlane(
@@ -669,8 +698,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  auto key_loop = [&](auto scale_dv) {
-    constexpr bool kS = decltype(scale_dv)::value;
+  auto key_loop = [&](auto path) {
+    constexpr int kS = decltype(path)::value;
     finish_tile();
     for (int kt = t0; kt < kLast; ++kt) {
       const int cs = (kt - t0) & 1;
@@ -689,13 +718,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
     jvp_block<D, kMode, true, kS>(st, cur, 1, qf, dqf, l32, g, kl + 32, Nk, c_log2, sc.s_t,
                                   sc.dv_mul, none);
   };
-  if (M::kKV && sc.slow)
-    key_loop(Flag<M::kKV>{});
+  if (M::kKV && sc.path == kPathScaleDV)
+    key_loop(IntC<M::kKV ? kPathScaleDV : kPathFast>{});
+  else if (M::kKV && sc.path == kPathSepU)
+    key_loop(IntC<M::kKV ? kPathSepU : kPathFast>{});
   else
-    key_loop(Flag<false>{});
+    key_loop(IntC<kPathFast>{});
 
   jvp_epilogue<D, kOutBf16>(st, obh, row, Nq, g, o, to, lse, tlse, ext, sc.ev, sc.ev + sc.t,
-                            sc.t);
+                            sc.eu);
 }
 
 // ---- short key ranges: 128-row workgroups, two per CU ----
@@ -743,7 +774,7 @@ struct HalfGeo {
 // copy(next, slot) fills the other half-stage over the block's first steps.
 // As in tile_step, the two restrict-qualified pointers name disjoint halves of
 // the LDS, so reads of `cur` need not wait for the copy into `next`.
-template <int D, int kMode, bool kMask, bool kScaleDV, typename Copy>
+template <int D, int kMode, bool kMask, int kPath, typename Copy>
 __device__ __attribute__((always_inline)) inline void short_block(
     char* __restrict__ next, const char* __restrict__ cur, Copy copy, RowState<D>& st,
     const u32x4* qf, const u32x4* dqf, int l32, int g, int key0, int Nk, float c_log2,
@@ -754,7 +785,7 @@ __device__ __attribute__((always_inline)) inline void short_block(
   const char* dkp = cur + (M::kKV ? HG::kF * kDmaBytes : 0);
   const char* vp = cur + G::kNT * HG::kF * kDmaBytes;
   const char* dvp = vp + (M::kKV ? HG::kF * kDmaBytes : 0);
-  jvp_block_at<D, kMode, kMask, kScaleDV>(st, cur, dkp, vp, dvp, qf, dqf, l32, g, key0, Nk,
+  jvp_block_at<D, kMode, kMask, kPath>(st, cur, dkp, vp, dvp, qf, dqf, l32, g, key0, Nk,
                                           c_log2, scale, dv_mul, [&](int slot) {
                                             if (slot < HG::kPerWave) copy(next, slot);
                                           });
@@ -838,8 +869,9 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  auto block = [&](int h, auto mask, auto scale_dv, bool copy_next) {
-    constexpr bool kMk = decltype(mask)::value, kS = decltype(scale_dv)::value;
+  auto block = [&](int h, auto mask, auto path, bool copy_next) {
+    constexpr bool kMk = decltype(mask)::value;
+    constexpr int kS = decltype(path)::value;
     short_block<D, kMode, kMk, kS>(
         smem + ((h + 1) & 1) * HG::kBytes, smem + (h & 1) * HG::kBytes,
         [&](char* next, int j) {
@@ -848,24 +880,26 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
         st, qf, dqf, l32, g, (t0 + (h >> 1)) * kBC + 32 * (h & 1), Nk, c_log2, sc.s_t,
         sc.dv_mul);
   };
-  auto key_loop = [&](auto scale_dv) {
+  auto key_loop = [&](auto path) {
     int h = 0;
     for (; h < nh - 2; ++h) {
       block_ready();
-      block(h, Flag<false>{}, scale_dv, true);
+      block(h, Flag<false>{}, path, true);
     }
     block_ready();
-    block(h, Flag<true>{}, scale_dv, true);
+    block(h, Flag<true>{}, path, true);
     block_ready();
-    block(h + 1, Flag<true>{}, scale_dv, false);
+    block(h + 1, Flag<true>{}, path, false);
   };
-  if (M::kKV && sc.slow)
-    key_loop(Flag<M::kKV>{});
+  if (M::kKV && sc.path == kPathScaleDV)
+    key_loop(IntC<M::kKV ? kPathScaleDV : kPathFast>{});
+  else if (M::kKV && sc.path == kPathSepU)
+    key_loop(IntC<M::kKV ? kPathSepU : kPathFast>{});
   else
-    key_loop(Flag<false>{});
+    key_loop(IntC<kPathFast>{});
 
   jvp_epilogue<D, kOutBf16>(st, obh, row, Nq, g, o, to, lse, tlse, ext, sc.ev, sc.ev + sc.t,
-                            sc.t);
+                            sc.eu);
 }
 
 // ---- forward attention alone (O, lse) ----

@@ -60,11 +60,12 @@ def _jvp_ex(x, scale=S128, frozen=False, out_dtype=torch.float32):
     return [None if t is None else t.cpu() for t in out]
 
 
-def _oracle(x, scale=S128, frozen=False):
+def _oracle(x, scale=S128, frozen=False, with_dlse=False):
     dk = torch.zeros_like(x["dk"]) if frozen else x["dk"]
     dv = torch.zeros_like(x["dv"]) if frozen else x["dv"]
     with np.errstate(all="ignore"):
-        return oracle.attention_jvp(x["q"], x["k"], x["v"], x["dq"], dk, dv, scale)
+        return oracle.attention_jvp(x["q"], x["k"], x["v"], x["dq"], dk, dv, scale,
+                                    with_dlse=with_dlse)
 
 
 def _gate(label, got, want):
@@ -121,6 +122,8 @@ CASES = {
     "tiny_all": (1.0, 1.0, 1e-6, 1e-8, 1e-8, 1e-7),
     "V_tiny_tangents_huge": (1.0, 1.0, 1e-5, 1e3, 1e3, 1e-3),
     "V_huge_dV_tiny": (1.0, 1.0, 1e5, 0.1, 0.1, 1e-6),
+    # s dS far below what dV's exponent leaves it (mu from its own exponent)
+    "dV_huge_dS_tiny": (1.0, 1.0, 1e-6, 1e-4, 1e-4, 1e5),
 }
 
 
@@ -128,7 +131,7 @@ CASES = {
 @pytest.mark.parametrize("case", list(CASES))
 def test_out_of_fp16_range_vs_oracle(case, Nk):
     x = _rand(2, 300, Nk, seed=list(CASES).index(case), sig=CASES[case])
-    ref = _oracle(x)
+    ref = _oracle(x, with_dlse=True)
     sds = S128 * (x["dq"].double() @ x["k"].double().transpose(-1, -2)
                   + x["q"].double() @ x["dk"].double().transpose(-1, -2))
     print(f"  {case}: max|V| {x['v'].float().abs().max():.3e} max|dV| "
@@ -139,6 +142,7 @@ def test_out_of_fp16_range_vs_oracle(case, Nk):
         _gate(tag + " O", o, ref[0])
         _gate(tag + " dO", to, ref[1])
         _gate(tag + " lse", lse, ref[2])
+        _gate(tag + " tlse", tlse, ref[3])
 
 
 @pytest.mark.parametrize("case", ["sdS_1e4", "tiny_all", "V_dV_1e6"])

@@ -164,3 +164,52 @@ def test_fp32_path_sweep(c, sign):
         m = metrics(a.double().cpu().numpy(), want)
         print(f"  [{c['i']}] {name}: {m}", flush=True)
         assert m["rel_frob"] <= 1e-5, (name, m, c, s)
+
+
+# Magnitudes far from 1: every tensor multiplied by its own power of ten
+# (V, dV, dQ, dK from 1e-6 to 1e5; Q and K so that the logits stay between
+# ~1e-3 and ~30 in size), either sign of the scale, NULL tangents and both
+# kernel forms, against the oracle under the scale-free gate of
+# tests/test_range.py (relative Frobenius <= 1e-2, max-abs <= 5e-3 of the
+# largest reference magnitude).
+def _magnitude_configs(n=24, seed=99):
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        d = rng.choice([64, 128])
+        mq = 10.0 ** rng.uniform(-2, 1)
+        mk = 10.0 ** rng.uniform(-1.5, 0.5)
+        out.append(dict(
+            i=300 + i, B=1, H=rng.choice([1, 2]), Nq=rng.choice(EDGES_Q + [rng.randint(1, 600)]),
+            Nk=rng.choice(EDGES_K + [rng.randint(1, 1300)]), d=d,
+            scale=rng.choice([1.0, -1.0]) / math.sqrt(d),
+            mag=dict(q=mq, k=mk, v=10.0 ** rng.randint(-6, 5), dq=10.0 ** rng.randint(-6, 5),
+                     dk=10.0 ** rng.randint(-6, 5), dv=10.0 ** rng.randint(-6, 5)),
+            null=rng.choice([(), ("dk", "dv"), ("dq",), ("dv",)]), tsig=1.0))
+    return out
+
+
+@pytest.mark.parametrize("c", _magnitude_configs(), ids=lambda c: (
+    f"{c['i']}-q{c['Nq']}k{c['Nk']}d{c['d']}"))
+def test_magnitude_sweep_vs_oracle(c):
+    x = {n: (t.float() * c["mag"][n]).to(torch.bfloat16) for n, t in _inputs(c).items()}
+    dev = torch.device("cuda:0")
+    g = {n: t.to(dev) for n, t in x.items()}
+    tan = {n: (None if n in c["null"] else g[n]) for n in ("dq", "dk", "dv")}
+    print(f"  launch magnitudes {c}", flush=True)
+    o, to, lse, tlse = ajvp.attn_jvp_fwd_ex(g["q"], g["k"], g["v"], tan["dq"], tan["dk"],
+                                            tan["dv"], scale=c["scale"])
+    torch.cuda.synchronize()
+    xz = {n: (torch.zeros_like(x[n]) if n in c["null"] else x[n]) for n in x}
+    with np.errstate(all="ignore"):
+        ref = oracle.attention_jvp(xz["q"], xz["k"], xz["v"], xz["dq"], xz["dk"], xz["dv"],
+                                   c["scale"], with_dlse=True)
+    for name, a, want in zip(("O", "dO", "lse", "tlse"), (o, to, lse, tlse), ref):
+        a = a.double().cpu().numpy()
+        assert np.isfinite(a).all(), (name, c)
+        m = metrics(a, want)
+        print(f"  [{c['i']}] {name}: {m} max|ref| {np.abs(want).max():.3e}", flush=True)
+        if np.abs(want).max() == 0:
+            assert m["max_abs"] == 0, (name, m, c)
+            continue
+        assert m["rel_frob"] <= 1e-2 and m["max_rel"] <= 5e-3, (name, m, c)
