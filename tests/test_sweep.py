@@ -213,3 +213,37 @@ def test_magnitude_sweep_vs_oracle(c):
             assert m["max_abs"] == 0, (name, m, c)
             continue
         assert m["rel_frob"] <= 1e-2 and m["max_rel"] <= 5e-3, (name, m, c)
+
+
+# The forward alone and the backward with magnitudes far from 1 (per-tensor
+# powers of ten; the cotangent gO drawn like dQ and scaled too), either sign
+# of the scale, against oracle.attention and oracle.attention_vjp under the
+# scale-free gate.
+@pytest.mark.parametrize("c", _magnitude_configs(n=16, seed=123), ids=lambda c: (
+    f"{c['i']}-q{c['Nq']}k{c['Nk']}d{c['d']}"))
+def test_magnitude_sweep_forward_and_backward(c):
+    c = dict(c, i=c["i"] + 100)
+    x = {n: (t.float() * c["mag"][n]).to(torch.bfloat16) for n, t in _inputs(c).items()}
+    dev = torch.device("cuda:0")
+    g = {n: t.to(dev) for n, t in x.items()}
+    s = c["scale"]
+    print(f"  launch fwd+bwd magnitudes {c}", flush=True)
+    o, lse = ajvp.attn_fwd(g["q"], g["k"], g["v"], scale=s)
+    gq, gk, gv = ajvp.attn_bwd(g["q"], g["k"], g["v"], o, g["dq"], lse, scale=s)
+    torch.cuda.synchronize()
+    with np.errstate(all="ignore"):
+        O, L = oracle.attention(x["q"], x["k"], x["v"], s)
+        ref = oracle.attention_vjp(x["q"], x["k"], x["v"], x["dq"], s)
+    for name, a, want in (("O", o, O), ("lse", lse, L)) + tuple(zip(("gQ", "gK", "gV"),
+                                                                    (gq, gk, gv), ref)):
+        a = a.double().cpu().numpy()
+        assert np.isfinite(a).all(), (name, c)
+        m = metrics(a, want)
+        print(f"  [{c['i']}] {name}: {m} max|ref| {np.abs(want).max():.3e}", flush=True)
+        if np.abs(want).max() < 1e-300:
+            continue
+        if np.abs(want).max() < 1e-12 * max(1.0, float(np.abs(ref[1]).max())):
+            # gQ = gK = 0 up to rounding (a single key): only the size of the result counts
+            assert m["max_abs"] <= 1e-5 * max(1.0, float(np.abs(ref[1]).max())), (name, m, c)
+            continue
+        assert m["rel_frob"] <= 1e-2 and m["max_rel"] <= 5e-3, (name, m, c)
