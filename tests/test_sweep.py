@@ -197,22 +197,27 @@ def test_magnitude_sweep_vs_oracle(c):
     g = {n: t.to(dev) for n, t in x.items()}
     tan = {n: (None if n in c["null"] else g[n]) for n in ("dq", "dk", "dv")}
     print(f"  launch magnitudes {c}", flush=True)
-    o, to, lse, tlse = ajvp.attn_jvp_fwd_ex(g["q"], g["k"], g["v"], tan["dq"], tan["dk"],
-                                            tan["dv"], scale=c["scale"])
+    runs = {"plain": ajvp.attn_jvp_fwd_ex(g["q"], g["k"], g["v"], tan["dq"], tan["dk"],
+                                          tan["dv"], scale=c["scale"]),
+            # key-tile ranges merged (3 ranges where the keys span 3 tiles or more)
+            "split": ajvp.attn_jvp_fwd_splitkv(g["q"], g["k"], g["v"], tan["dq"], tan["dk"],
+                                               tan["dv"], scale=c["scale"], nsplit=3)}
     torch.cuda.synchronize()
     xz = {n: (torch.zeros_like(x[n]) if n in c["null"] else x[n]) for n in x}
     with np.errstate(all="ignore"):
         ref = oracle.attention_jvp(xz["q"], xz["k"], xz["v"], xz["dq"], xz["dk"], xz["dv"],
                                    c["scale"], with_dlse=True)
-    for name, a, want in zip(("O", "dO", "lse", "tlse"), (o, to, lse, tlse), ref):
-        a = a.double().cpu().numpy()
-        assert np.isfinite(a).all(), (name, c)
-        m = metrics(a, want)
-        print(f"  [{c['i']}] {name}: {m} max|ref| {np.abs(want).max():.3e}", flush=True)
-        if np.abs(want).max() == 0:
-            assert m["max_abs"] == 0, (name, m, c)
-            continue
-        assert m["rel_frob"] <= 1e-2 and m["max_rel"] <= 5e-3, (name, m, c)
+    for form, outs in runs.items():
+        for name, a, want in zip(("O", "dO", "lse", "tlse"), outs, ref):
+            a = a.double().cpu().numpy()
+            assert np.isfinite(a).all(), (form, name, c)
+            m = metrics(a, want)
+            print(f"  [{c['i']} {form}] {name}: {m} max|ref| {np.abs(want).max():.3e}",
+                  flush=True)
+            if np.abs(want).max() == 0:
+                assert m["max_abs"] == 0, (form, name, m, c)
+                continue
+            assert m["rel_frob"] <= 1e-2 and m["max_rel"] <= 5e-3, (form, name, m, c)
 
 
 # The forward alone and the backward with magnitudes far from 1 (per-tensor
