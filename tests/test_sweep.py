@@ -252,3 +252,34 @@ def test_magnitude_sweep_forward_and_backward(c):
             assert m["max_abs"] <= 1e-5 * max(1.0, float(np.abs(ref[1]).max())), (name, m, c)
             continue
         assert m["rel_frob"] <= 1e-2 and m["max_rel"] <= 5e-3, (name, m, c)
+
+
+# Every entry point that computes the same thing returns the same bits: the
+# JVP through the torch workspace (attn_jvp_fwd), the library pool
+# (attn_jvp_fwd_ex without a workspace), the two phases (attn_jvp_pack_kv +
+# attn_jvp_fwd_packed) and the fixed buffer (attn_jvp_fwd_noalloc); split-KV
+# with one range; and the forward alone (its O and lse equal the JVP's).
+@pytest.mark.parametrize("c", _configs(n=12, seed=4242), ids=lambda c: (
+    f"{c['i']}-B{c['B']}H{c['H']}q{c['Nq']}k{c['Nk']}d{c['d']}"))
+def test_entry_points_agree_bit_for_bit(c):
+    c = dict(c, i=c["i"] + 500)
+    x = _inputs(c)
+    dev = torch.device("cuda:0")
+    g = {n: t.to(dev) for n, t in x.items()}
+    s = c["scale"]
+    args = (g["q"], g["k"], g["v"], g["dq"], g["dk"], g["dv"])
+    print(f"  launch entry points {c}", flush=True)
+    ref = ajvp.attn_jvp_fwd(*args, scale=s)
+    ex = ajvp.attn_jvp_fwd_ex(*args, scale=s, tlse=False)
+    ws = torch.empty(ajvp.attn_jvp_workspace_bytes(c["B"], c["H"], c["Nk"], c["d"]),
+                     dtype=torch.uint8, device=dev)
+    ajvp.attn_jvp_pack_kv(g["k"], g["v"], g["dk"], g["dv"], workspace=ws)
+    two = ajvp.attn_jvp_fwd_packed(g["q"], g["dq"], ws, c["Nk"], scale=s)
+    na = ajvp.attn_jvp_fwd_noalloc(*args, scale=s)
+    sp = ajvp.attn_jvp_fwd_splitkv(*args, scale=s, nsplit=1, tlse=False)
+    fo, flse = ajvp.attn_fwd(g["q"], g["k"], g["v"], scale=s)
+    torch.cuda.synchronize()
+    for name, outs in (("ex", ex[:3]), ("two-phase", two), ("noalloc", na), ("split 1", sp[:3])):
+        for a, b, what in zip(outs, ref, ("O", "dO", "lse")):
+            assert torch.equal(a, b), (name, what, c)
+    assert torch.equal(fo, ref[0]) and torch.equal(flse, ref[2]), c
