@@ -283,3 +283,53 @@ def test_entry_points_agree_bit_for_bit(c):
         for a, b, what in zip(outs, ref, ("O", "dO", "lse")):
             assert torch.equal(a, b), (name, what, c)
     assert torch.equal(fo, ref[0]) and torch.equal(flse, ref[2]), c
+
+
+# Non-finite inputs through every JVP form: one to three NaN or +-Inf values at
+# seeded positions of seeded tensors; each output (O, dO, lse, tlse) must be
+# non-finite exactly where the oracle's is, and match it elsewhere.
+def _nonfinite_configs(n=16, seed=31337):
+    rng = random.Random(seed)
+    out = []
+    for c in _configs(n=n, seed=seed):
+        k = rng.randint(1, 3)
+        c = dict(c, i=c["i"] + 700, tsig=0.1, bf16_out=False, lse=True, tlse=True,
+                 bad=[(rng.choice(["q", "k", "v", "dq", "dk", "dv"]), rng.random(), rng.random(),
+                       rng.choice([float("nan"), float("inf"), -float("inf")]))
+                      for _ in range(k)])
+        out.append(c)
+    return out
+
+
+@pytest.mark.parametrize("c", _nonfinite_configs(), ids=lambda c: (
+    f"{c['i']}-B{c['B']}H{c['H']}q{c['Nq']}k{c['Nk']}d{c['d']}"))
+def test_nonfinite_sweep_vs_oracle(c):
+    x = _inputs(c)
+    for name, fr, fc, val in c["bad"]:
+        t = x[name]
+        b, h = int(fr * 997) % t.shape[0], int(fc * 991) % t.shape[1]
+        r, col = int(fr * t.shape[2]) % t.shape[2], int(fc * t.shape[3]) % t.shape[3]
+        t[b, h, r, col] = val
+    dev = torch.device("cuda:0")
+    g = {n: t.to(dev) for n, t in x.items()}
+    tan = {n: (None if n in c["null"] else g[n]) for n in ("dq", "dk", "dv")}
+    print(f"  launch non-finite {c}", flush=True)
+    if c["nsplit"] is None:
+        got = ajvp.attn_jvp_fwd_ex(g["q"], g["k"], g["v"], tan["dq"], tan["dk"], tan["dv"],
+                                   scale=c["scale"])
+    else:
+        got = ajvp.attn_jvp_fwd_splitkv(g["q"], g["k"], g["v"], tan["dq"], tan["dk"], tan["dv"],
+                                        scale=c["scale"], nsplit=c["nsplit"])
+    torch.cuda.synchronize()
+    xz = {n: (torch.zeros_like(x[n]) if n in c["null"] else x[n]) for n in x}
+    with np.errstate(all="ignore"):
+        ref = oracle.attention_jvp(xz["q"], xz["k"], xz["v"], xz["dq"], xz["dk"], xz["dv"],
+                                   c["scale"], with_dlse=True)
+    for name, a, want in zip(("O", "dO", "lse", "tlse"), got, ref):
+        a = a.double().cpu().numpy()
+        bad_g, bad_r = ~np.isfinite(a), ~np.isfinite(want)
+        print(f"  [{c['i']}] {name}: {bad_g.sum()} non-finite (oracle {bad_r.sum()})", flush=True)
+        assert (bad_g == bad_r).all(), (name, int(bad_g.sum()), int(bad_r.sum()), c)
+        if (~bad_r).any():
+            m = metrics(a[~bad_r], want[~bad_r])
+            assert m["max_abs"] <= 2e-2 and m["rel_frob"] <= 1e-2, (name, m, c)
