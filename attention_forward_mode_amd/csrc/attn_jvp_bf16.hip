@@ -461,44 +461,74 @@ __device__ __attribute__((always_inline)) inline void store4(__amdgpu_buffer_rsr
   }
 }
 
+// Row-ordered output stores.  A wave's accumulators hold, for query row l32
+// of its 32 (lanes l32 and l32 + 32), the columns 32 cb + 8 qq + 4 g + e; a
+// store straight from them writes 32 bytes into each of 32 rows per
+// instruction.  Each 32-column block instead passes through the wave's own
+// stage of 32 rows x kRowPitch floats in LDS and is read back by rows, so one
+// store instruction writes 8 whole rows of the block (128 bytes each in fp32:
+// a whole cache line).  The 4 floats of padding per row put the rows' first
+// words in different banks.  The stage is the wave's alone and a wave's LDS
+// operations complete in the order it issues them, so the block's reads see
+// its writes and the next block's writes come after them without a barrier.
+constexpr int kRowPitch = 36;                    // floats per staged row
+constexpr int kStageBytes = 32 * kRowPitch * 4;  // one wave's stage
+template <int D, bool kOutBf16, typename Val>
+__device__ __attribute__((always_inline)) inline void store_rows(float* stage,
+                                                                 __amdgpu_buffer_rsrc_t r,
+                                                                 uint32_t elem0, int nrows,
+                                                                 int l32, int g, Val val) {
+  const int rr = (l32 >> 3) + 4 * g, cc = 4 * (l32 & 7);  // lane = l32 + 32 g reads row rr
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = val(cb, 4 * qq + e);
+      *reinterpret_cast<f32x4*>(stage + l32 * kRowPitch + 8 * qq + 4 * g) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rw = 8 * i + rr;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(stage + rw * kRowPitch + cc);
+      if (rw < nrows) store4<kOutBf16>(r, elem0 + (uint32_t)rw * D + 32 * cb + cc, x);
+    }
+    // one block's values in flight at a time (the scheduler would otherwise
+    // hoist every block's reads and run out of registers)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Epilogue of one wave: O = A 2^-ea / l, mu = u 2^-eu / l,
 // dO = G 2^-eg / l - mu O, lse and tlse = mu for this lane's query row of
 // output slice obh (rows past Nq are not stored).  The accumulators hold A,
 // G and u scaled by 2^ea, 2^eg and 2^eu (the fp16 exponents of V and of the
-// tangent terms); multiplying 1/l by a power of two is exact.
+// tangent terms); multiplying 1/l by a power of two is exact.  O and dO go
+// out through the wave's LDS stage (store_rows); every wave of the workgroup
+// must be done reading the tile stages the stage overlaps.
 template <int D, bool kOutBf16>
 __device__ __attribute__((always_inline)) inline void jvp_epilogue(
-    const RowState<D>& st, uint32_t obh, int row, int Nq, int g, void* o, void* to, float* lse,
-    float* tlse, const Extents& ext, int ea, int eg, int eu) {
+    const RowState<D>& st, float* stage, uint32_t obh, int row, int Nq, int l32, int g, void* o,
+    void* to, float* lse, float* tlse, const Extents& ext, int ea, int eg, int eu) {
   const float l = halves_sum(st.l);
   const float inv_l = 1.0f / l;
   const float fa = __builtin_amdgcn_ldexpf(inv_l, -ea), fg = __builtin_amdgcn_ldexpf(inv_l, -eg);
   const float mu = halves_sum(st.u) * __builtin_amdgcn_ldexpf(inv_l, -eu);
-  if (row < Nq) {
-    const uint32_t orow = (obh * (uint32_t)Nq + row) * D;  // first element of the row
-    const auto ro = make_rsrc(o, ext.o_bytes);
-    const auto rto = make_rsrc(to, ext.o_bytes);
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int c0 = 32 * cb + 8 * qq + 4 * g;
-        f32x4 ov, tv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a = st.accA[cb][4 * qq + e] * fa;
-          ov[e] = a;
-          tv[e] = st.accG[cb][4 * qq + e] * fg - mu * a;
-        }
-        store4<kOutBf16>(ro, orow + c0, ov);
-        store4<kOutBf16>(rto, orow + c0, tv);
-      }
-    if (g == 0) {
-      const uint32_t off = (obh * (uint32_t)Nq + row) * 4;
-      if (lse != nullptr)
-        buf_store4(make_rsrc(lse, ext.lse_bytes), off, (st.m + __log2f(l)) * kLn2);
-      if (tlse != nullptr) buf_store4(make_rsrc(tlse, ext.lse_bytes), off, mu);
-    }
+  const int row0 = row - l32;  // the wave's first row
+  const uint32_t elem0 = (obh * (uint32_t)Nq + row0) * D;
+  store_rows<D, kOutBf16>(stage, make_rsrc(o, ext.o_bytes), elem0, Nq - row0, l32, g,
+                          [&](int cb, int i) { return st.accA[cb][i] * fa; });
+  store_rows<D, kOutBf16>(stage, make_rsrc(to, ext.o_bytes), elem0, Nq - row0, l32, g,
+                          [&](int cb, int i) {
+                            const float a = st.accA[cb][i] * fa;
+                            return st.accG[cb][i] * fg - mu * a;
+                          });
+  if (row < Nq && g == 0) {
+    const uint32_t off = (obh * (uint32_t)Nq + row) * 4;
+    if (lse != nullptr)
+      buf_store4(make_rsrc(lse, ext.lse_bytes), off, (st.m + __log2f(l)) * kLn2);
+    if (tlse != nullptr) buf_store4(make_rsrc(tlse, ext.lse_bytes), off, mu);
   }
 }
 
@@ -620,7 +650,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
     int nbh, int tps, Extents ext, float scale, float c_log2) {
   using M = Mode<kMode>;
   using G = Geo<D, M::kKV>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * G::kImgBytes];
+  __shared__ __attribute__((aligned(1024)))
+  char smem[2 * G::kImgBytes > kWaves * kStageBytes ? 2 * G::kImgBytes : kWaves * kStageBytes];
 
   // Work item (query tile qt of kBR rows, (b, h) slice bh, key split) from
   // the linear workgroup id: the dispatcher deals workgroups to the 8 XCDs in
@@ -725,8 +756,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
   else
     key_loop(IntC<kPathFast>{});
 
-  jvp_epilogue<D, kOutBf16>(st, obh, row, Nq, g, o, to, lse, tlse, ext, sc.ev, sc.ev + sc.t,
-                            sc.eu);
+  __syncthreads();  // the output stages overlap the tile stages
+  jvp_epilogue<D, kOutBf16>(st, reinterpret_cast<float*>(smem + wave * kStageBytes), obh, row,
+                            Nq, l32, g, o, to, lse, tlse, ext, sc.ev, sc.ev + sc.t, sc.eu);
 }
 
 // ---- short key ranges: 128-row workgroups, two per CU ----
@@ -800,7 +832,9 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
   using M = Mode<kMode>;
   using G = Geo<D, M::kKV>;
   using HG = HalfGeo<D, M::kKV>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * HG::kBytes];
+  __shared__ __attribute__((aligned(1024)))
+  char smem[2 * HG::kBytes > kShortWaves * kStageBytes ? 2 * HG::kBytes
+                                                       : kShortWaves * kStageBytes];
 
   // work item: as in attn_jvp_bf16_kernel, with row tiles of kShortBR rows
   const uint32_t wg = blockIdx.x, nwg = gridDim.x;
@@ -898,8 +932,9 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
   else
     key_loop(IntC<kPathFast>{});
 
-  jvp_epilogue<D, kOutBf16>(st, obh, row, Nq, g, o, to, lse, tlse, ext, sc.ev, sc.ev + sc.t,
-                            sc.eu);
+  __syncthreads();  // the output stages overlap the tile stages
+  jvp_epilogue<D, kOutBf16>(st, reinterpret_cast<float*>(smem + wave * kStageBytes), obh, row,
+                            Nq, l32, g, o, to, lse, tlse, ext, sc.ev, sc.ev + sc.t, sc.eu);
 }
 
 // ---- forward attention alone (O, lse) ----
@@ -1034,7 +1069,8 @@ __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kerne
     float* __restrict__ lse, int Nq, int Nk, int ntiles, int nqt, int nbh, int tps, Extents ext,
     float c_log2) {
   using G = Geo<D, false>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * G::kImgBytes];
+  __shared__ __attribute__((aligned(1024)))
+  char smem[2 * G::kImgBytes > kWaves * kStageBytes ? 2 * G::kImgBytes : kWaves * kStageBytes];
   // XCD-aware work order and key-tile ranges, as in attn_jvp_bf16_kernel
   const uint32_t wg = blockIdx.x, nwg = gridDim.x;
   const uint32_t xcd = wg % kXcds, slot = wg / kXcds, per = nwg / kXcds, extra = nwg % kXcds;
@@ -1094,6 +1130,7 @@ __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kerne
   const int kLast = t1 - 1;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  const int ev = __builtin_amdgcn_readfirstlane((int)rec[0]);  // in a scalar register
   for (int kt = t0; kt < kLast; ++kt) {
     const int sc = (kt - t0) & 1;
     fwd_tile<D, RB>(smem + (sc ^ 1) * G::kImgBytes, smem + sc * G::kImgBytes,
@@ -1110,28 +1147,19 @@ __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kerne
     fwd_block<D, RB, true>(st, cur, 1, qf, l32, g, kl + 32, Nk, c_log2, none);
   }
 
+  __syncthreads();  // the output stages overlap the tile stages
   const auto ro = make_rsrc(o, ext.o_bytes);
-  const int ev = __builtin_amdgcn_readfirstlane((int)rec[0]);
+  float* stage = reinterpret_cast<float*>(smem + wave * kStageBytes);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int row = row0 + 32 * rb;
+    const int row = row0 + 32 * rb, first = row - l32;
     const float l = halves_sum(st.l[rb]);
     const float inv_l = __builtin_amdgcn_ldexpf(1.0f / l, -ev);
-    if (row < Nq) {
-      const uint32_t orow = (obh * (uint32_t)Nq + row) * D;
-#pragma unroll
-      for (int cb = 0; cb < G::kCB; ++cb)
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          f32x4 ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = st.acc[rb][cb][4 * qq + e] * inv_l;
-          store4<kOutBf16>(ro, orow + 32 * cb + 8 * qq + 4 * g, ov);
-        }
-      if (g == 0 && lse != nullptr)
-        buf_store4(make_rsrc(lse, ext.lse_bytes), (obh * (uint32_t)Nq + row) * 4,
-                   (st.m[rb] + __log2f(l)) * kLn2);
-    }
+    store_rows<D, kOutBf16>(stage, ro, (obh * (uint32_t)Nq + first) * D, Nq - first, l32, g,
+                            [&](int cb, int i) { return st.acc[rb][cb][i] * inv_l; });
+    if (row < Nq && g == 0 && lse != nullptr)
+      buf_store4(make_rsrc(lse, ext.lse_bytes), (obh * (uint32_t)Nq + row) * 4,
+                 (st.m[rb] + __log2f(l)) * kLn2);
   }
 }
 
