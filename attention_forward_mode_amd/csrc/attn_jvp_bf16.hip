@@ -583,18 +583,66 @@ __device__ __attribute__((always_inline)) inline void flip_negative_scale(
   }
 }
 
+// What wave_scale reads from the slice header: the record and this lane's
+// norm slot.  Loaded apart from the rest so that a kernel can issue the loads
+// before its Q and dQ loads and have them arrive together.
+struct ScaleLoads {
+  u32x4 rec;
+  float mk, mdk;  // this lane's norm slot (reduced over the wave in wave_scale)
+};
+__device__ __attribute__((always_inline)) inline ScaleLoads scale_loads(
+    __amdgpu_buffer_rsrc_t rimg, uint32_t hdr, int ntiles, int lane) {
+  ScaleLoads sl;
+  sl.rec = buf_load16(rimg, hdr + kHdrRecord);
+  slice_norm_slots(rimg, hdr, ntiles, lane, sl.mk, sl.mdk);
+  return sl;
+}
+
+// Squares of the 64 bf16 values of a lane's D / 16 fragments, summed in fp32
+// by v_dot2 (each product exact): the sum and the OR of the values' bits.
+template <int D>
+__device__ __attribute__((always_inline)) inline float sumsq_f32(const u32x4* f, uint32_t& bits) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  float s = 0.f;
+  bits = 0;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bf16x2 x = __builtin_bit_cast(bf16x2, f[ks][w]);
+      s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
+      bits |= f[ks][w];
+    }
+  return s;
+}
+
+// fp32 sum of squares that stands for the exact one: no term overflowed (sum
+// at most 2^100) and the terms lost to underflow (each below 2^-126, at most
+// 64) are under 2^-20 of it (sum at least 2^-100), or every value is zero.
+__device__ inline bool sumsq_f32_usable(float s, uint32_t bits) {
+  return (s >= 0x1p-100f && s <= 0x1p100f) || (bits & 0x7fff7fffu) == 0;
+}
+
 template <int D, bool kKV>
 __device__ __attribute__((always_inline)) inline WaveScale wave_scale(
-    __amdgpu_buffer_rsrc_t rimg, uint32_t hdr, int ntiles, const u32x4* qf, const u32x4* dqf,
-    float scale, int lane) {
-  const u32x4 rec = buf_load16(rimg, hdr + kHdrRecord);
-  float mk, mdk;
-  slice_norms(rimg, hdr, ntiles, lane, mk, mdk);
+    const ScaleLoads& sl, const u32x4* qf, const u32x4* dqf, float scale) {
+  const u32x4 rec = sl.rec;
+  const float mk = wave_max_f32(sl.mk), mdk = wave_max_f32(sl.mdk);
+  // Row norms: the fp32 sums of squares when every lane's are usable as they
+  // are (the bound needs far less than fp32's precision), else fp64 sums.
+  uint32_t bq = 0, bdq;
+  const float fdq = sumsq_f32<D>(dqf, bdq);
+  const float fq = kKV ? sumsq_f32<D>(qf, bq) : 0.f;
   double nq = 0.0, ndq = 0.0;
+  if (!wave_any(!(sumsq_f32_usable(fdq, bdq) && sumsq_f32_usable(fq, bq)))) {
+    ndq = fdq;
+    nq = fq;
+  } else {
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    if constexpr (kKV) nq += sumsq8(qf[ks]);
-    ndq += sumsq8(dqf[ks]);
+    for (int ks = 0; ks < D / 16; ++ks) {
+      if constexpr (kKV) nq += sumsq8(qf[ks]);
+      ndq += sumsq8(dqf[ks]);
+    }
   }
   double b = __builtin_sqrt(halves_sum_f64(ndq)) * (double)mk;
   if constexpr (kKV) b += __builtin_sqrt(halves_sum_f64(nq)) * (double)mdk;
@@ -697,6 +745,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
 
   // Q and dQ fragments: the B operand of S^T = K Q^T (lane: row l32, d-slice g).
   // Rows past Nq get an offset past the tensor, which the descriptor reads as 0.
+  const ScaleLoads sl = scale_loads(rimg, hdr, ntiles, lane);
   u32x4 qf[G::kKS], dqf[G::kKS];
   const uint32_t qrow = row_ok ? (bh * (uint32_t)Nq + row) * D * 2 : 0x80000000u;
 #pragma unroll
@@ -707,7 +756,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_jvp_bf16_kernel(
   }
 
   flip_negative_scale<D>(qf, dqf, scale, c_log2);
-  const WaveScale sc = wave_scale<D, M::kKV>(rimg, hdr, ntiles, qf, dqf, scale, lane);
+  const WaveScale sc = wave_scale<D, M::kKV>(sl, qf, dqf, scale);
 
   RowState<D> st;
 #pragma unroll
@@ -871,6 +920,7 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
 #pragma unroll
   for (int j = 0; j < HG::kPerWave; ++j) copy_half(0, smem, j);
 
+  const ScaleLoads sl = scale_loads(rimg, hdr, ntiles, lane);
   u32x4 qf[G::kKS], dqf[G::kKS];
   const uint32_t qrow = row_ok ? (bh * (uint32_t)Nq + row) * D * 2 : 0x80000000u;
 #pragma unroll
@@ -881,7 +931,7 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
   }
 
   flip_negative_scale<D>(qf, dqf, scale, c_log2);
-  const WaveScale sc = wave_scale<D, M::kKV>(rimg, hdr, ntiles, qf, dqf, scale, lane);
+  const WaveScale sc = wave_scale<D, M::kKV>(sl, qf, dqf, scale);
 
   RowState<D> st;
 #pragma unroll

@@ -87,28 +87,59 @@ __device__ inline double halves_sum_f64(double x) {
   return x0 + x1;
 }
 
+// Reductions over the 64 lanes of a wave, leaving the result in every lane,
+// without a trip through LDS: two quad permutations and two rotations of each
+// 16-lane row (DPP) combine a row, then the swaps of rows 0 <-> 1, 2 <-> 3
+// (v_permlane16_swap) and of the two halves (v_permlane32_swap) combine the
+// rows.  Each swap of x with itself hands every lane its own value and that of
+// its partner lane (l ^ 16, l ^ 32), in either order, so the operation must be
+// commutative.  Every lane of the wave must be active.
+template <int kCtrl>
+__device__ inline uint32_t dpp_word(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xf, 0xf, false);
+}
+template <typename T>
+struct LaneWords {  // T as 32-bit words (T of 4 or 8 bytes)
+  static constexpr int kN = sizeof(T) / 4;
+  uint32_t w[kN];
+};
+template <typename T, typename Op>
+__device__ inline T wave_allreduce(T x, Op op) {
+  using W = LaneWords<T>;
+  auto step = [&](auto move) {
+    W a = __builtin_bit_cast(W, x), b;
+#pragma unroll
+    for (int i = 0; i < W::kN; ++i) b.w[i] = move(a.w[i]);
+    x = op(x, __builtin_bit_cast(T, b));
+  };
+  step([](uint32_t v) { return dpp_word<0xB1>(v); });   // quad_perm [1,0,3,2]: lane ^ 1
+  step([](uint32_t v) { return dpp_word<0x4E>(v); });   // quad_perm [2,3,0,1]: lane ^ 2
+  step([](uint32_t v) { return dpp_word<0x124>(v); });  // row_ror:4
+  step([](uint32_t v) { return dpp_word<0x128>(v); });  // row_ror:8
+  auto swap = [&](auto perm) {
+    W a = __builtin_bit_cast(W, x), p, q;
+#pragma unroll
+    for (int i = 0; i < W::kN; ++i) {
+      const auto r = perm(a.w[i]);
+      p.w[i] = (uint32_t)r[0];
+      q.w[i] = (uint32_t)r[1];
+    }
+    x = op(__builtin_bit_cast(T, p), __builtin_bit_cast(T, q));
+  };
+  swap([](uint32_t v) { return __builtin_amdgcn_permlane16_swap(v, v, false, false); });
+  swap([](uint32_t v) { return __builtin_amdgcn_permlane32_swap(v, v, false, false); });
+  return x;
+}
+
 // Maximum over the 64 lanes of a wave (NaN lanes are ignored: fmax).
 __device__ inline double wave_max_f64(double x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, x);
-    const uint32_t lo = __shfl_xor((uint32_t)u, m), hi = __shfl_xor((uint32_t)(u >> 32), m);
-    x = __builtin_fmax(x, __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo));
-  }
-  return x;
+  return wave_allreduce(x, [](double a, double b) { return __builtin_fmax(a, b); });
 }
 __device__ inline uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const uint32_t y = __shfl_xor(x, m);
-    x = y > x ? y : x;
-  }
-  return x;
+  return wave_allreduce(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 __device__ inline float wave_max_f32(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = __builtin_fmaxf(x, __shfl_xor(x, m));
-  return x;
+  return wave_allreduce(x, [](float a, float b) { return __builtin_fmaxf(a, b); });
 }
 
 // Eight bf16 values times 2^t (exact while the results stay normal; rounded
@@ -249,9 +280,10 @@ __device__ inline void raise_norms(char* hdr_ptr, int tile, float a, float b) {
   atomicMax(slot + 1, __builtin_bit_cast(uint32_t, b));
 }
 
-// The two norm maxima of a slice (over its slots), in every lane of a wave.
-__device__ inline void slice_norms(__amdgpu_buffer_rsrc_t rws, uint32_t hdr, int ntiles,
-                                   int lane, float& a, float& b) {
+// This lane's norm slot of a slice (lane < the slot count; 0 elsewhere): the
+// loads of slice_norms, to be reduced over the wave later.
+__device__ inline void slice_norm_slots(__amdgpu_buffer_rsrc_t rws, uint32_t hdr, int ntiles,
+                                        int lane, float& a, float& b) {
   a = 0.f;
   b = 0.f;
   if (lane < (ntiles < kNormSlots ? ntiles : kNormSlots)) {
@@ -259,6 +291,12 @@ __device__ inline void slice_norms(__amdgpu_buffer_rsrc_t rws, uint32_t hdr, int
     a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rws, o, 0, 0));
     b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rws, o + 4, 0, 0));
   }
+}
+
+// The two norm maxima of a slice (over its slots), in every lane of a wave.
+__device__ inline void slice_norms(__amdgpu_buffer_rsrc_t rws, uint32_t hdr, int ntiles,
+                                   int lane, float& a, float& b) {
+  slice_norm_slots(rws, hdr, ntiles, lane, a, b);
   a = wave_max_f32(a);
   b = wave_max_f32(b);
 }

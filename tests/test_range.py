@@ -124,6 +124,10 @@ CASES = {
     "V_huge_dV_tiny": (1.0, 1.0, 1e5, 0.1, 0.1, 1e-6),
     # s dS far below what dV's exponent leaves it (mu from its own exponent)
     "dV_huge_dS_tiny": (1.0, 1.0, 1e-6, 1e-4, 1e-4, 1e5),
+    # row norms whose fp32 sums of squares underflow or overflow (the exact
+    # fp64 sums take over)
+    "dQ_tiny_dK_huge": (1.0, 1.0, 1.0, 1e-20, 1e12, 0.1),
+    "dQ_huge_dK_tiny": (1.0, 1.0, 1.0, 1e18, 1e-3, 0.1),
 }
 
 
