@@ -544,8 +544,8 @@ struct IntC {
 // A wave's fp16 exponents: eV of the slice (header record), and the tangent
 // exponent t of s P dS, from the bound |s dS_ij| <= |s| (|dq_i| Mk + |q_i| Mdk)
 // (Cauchy-Schwarz) over the wave's rows i (row norms from its Q and dQ
-// fragments, fp64) and all keys of the slice (Mk, Mdk: the largest key norms,
-// from the header).
+// fragments; see sumsq_f32) and all keys of the slice (Mk, Mdk: the largest
+// key norms, from the header).
 // With dV present, t is the slice's edV - eV (dV was packed at 2^(eV + t))
 // unless the bound needs a smaller one; then the path is kPathScaleDV and
 // dv_mul = 2^(t - edV + eV) rescales the dV^T fragments.  If instead the bound
