@@ -3,8 +3,8 @@
 // Same operation as the bf16 path (rCM record LIT-783 in the Anthology of the
 // SOTA, "Key takeaways", "JVP at production scale", paper §3.2 / App. C), kept
 // in fp32 end to end: it is the precision reference the pages motivate (the
-// record's second takeaway: BF16 JVP error is much larger than BF16 output
-// error, Fig. 11).  Structure: one workgroup = 4 waves x 32 query rows; 32-key
+// record's second takeaway, Fig. 11: a tangent computed in BF16 is far less
+// accurate than an output computed in BF16).  Structure: one workgroup = 4 waves x 32 query rows; 32-key
 // tiles of K, dK, V, dV copied straight into LDS (double buffered, one tile
 // ahead); fp32 MFMA 32x32x2 for S^T = K Q^T, dS^T = dK Q^T + K dQ^T,
 // A^T += V^T P^T and G^T += V^T (s P dS)^T + dV^T P^T; online softmax per lane.

@@ -1,7 +1,8 @@
 """Precision of the attention layer's tangent, measured (GPU).
 
-The rCM pages report that BF16 error in the JVP is much larger than BF16 error
-in the output (Anthology of the SOTA, LIT-783, "Key takeaways", Fig. 11), and
+The rCM pages report that a JVP computed in BF16 loses far more accuracy than
+an output computed in BF16 (Anthology of the SOTA, LIT-783, "Key takeaways",
+Fig. 11), and
 that a finite difference of the time derivative with dt = 1e-4 replaces the
 JVP only for the smallest model (§4.2).  This measures both at the level of
 one attention layer on each workload shape (first head, full length): the
