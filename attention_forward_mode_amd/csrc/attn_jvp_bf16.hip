@@ -998,6 +998,8 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
 // fit the chip one per CU.
 template <int RB>
 constexpr int fwd_rows() { return kWaves * 32 * RB; }  // query rows per workgroup
+// The 64-row form runs its two wave groups half a block apart (fwd_tile_lagged).
+constexpr bool kFwdLag = true;
 
 template <int D, int RB>
 struct FwdState {
@@ -1009,15 +1011,15 @@ struct FwdState {
 // One 32-key block for the wave's RB row blocks; same arithmetic as the
 // tangent-free part of jvp_block (online softmax with the lazy rescale, P
 // rounded to fp16 for the second product, l summed from those values).
-template <int D, int RB, bool kMask, typename Issue>
-__device__ __attribute__((always_inline)) inline void fwd_block(
-    FwdState<D, RB>& st, const char* stage, int kb, const u32x4 (*qf)[D / 16], int l32, int g,
-    int key0, int Nk, float c_log2, Issue issue) {
+// S^T of one 32-key block for the wave's RB row blocks (K fragments from the
+// stage, Q fragments from registers); issue(ks) runs at step ks.
+template <int D, int RB, typename Issue>
+__device__ __attribute__((always_inline)) inline void fwd_scores(f32x16 (&s)[RB], const char* stage,
+                                                                 int kb, const u32x4 (*qf)[D / 16],
+                                                                 int l32, int g, Issue issue) {
   using G = Geo<D, false>;
   const char* sK = stage;
-  const char* sV = stage + G::kOffV;
   const int lane16 = 16 * l32 + 512 * g;
-  f32x16 s[RB];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < G::kKS; ++ks) {
@@ -1028,7 +1030,18 @@ __device__ __attribute__((always_inline)) inline void fwd_block(
       s[rb] = mma_bf16(kf, qf[rb][ks], ks == 0 ? f32x16{} : s[rb]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  u32x4 p[RB][2];
+}
+
+// The online softmax of a block from its S^T, with the lazy rescale of the
+// accumulators: P rounded to fp16 pairs in the B-operand layout of the
+// second product, l summed from those values.
+template <int D, int RB, bool kMask>
+__device__ __attribute__((always_inline)) inline void fwd_softmax(FwdState<D, RB>& st,
+                                                                  f32x16 (&s)[RB],
+                                                                  u32x4 (&p)[RB][2], int g,
+                                                                  int key0, int Nk,
+                                                                  float c_log2) {
+  using G = Geo<D, false>;
   float alpha[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -1075,7 +1088,18 @@ __device__ __attribute__((always_inline)) inline void fwd_block(
       for (int cb = 0; cb < G::kCB; ++cb) st.acc[rb][cb] *= alpha[rb];
   }
   __builtin_amdgcn_sched_barrier(0);
-  // A^T += V^T P^T for every row block; step = (t, cb) reads fragment
+}
+
+// A^T += V^T P^T for a block; issue(kKS + step) runs at step `step`.
+template <int D, int RB, typename Issue>
+__device__ __attribute__((always_inline)) inline void fwd_pv(FwdState<D, RB>& st,
+                                                             const u32x4 (&p)[RB][2],
+                                                             const char* stage, int kb, int l32,
+                                                             int g, Issue issue) {
+  using G = Geo<D, false>;
+  const char* sV = stage + G::kOffV;
+  const int lane16 = 16 * l32 + 512 * g;
+  // step = (t, cb) reads fragment
   // (2 kb + t) kCB + cb, one step ahead with two row blocks (the one-block
   // instance, held to 128 registers, reads it at its step)
   constexpr int kSteps = 2 * G::kCB;
@@ -1099,6 +1123,26 @@ __device__ __attribute__((always_inline)) inline void fwd_block(
   }
 }
 
+template <int D, int RB, bool kMask, typename Issue>
+__device__ __attribute__((always_inline)) inline void fwd_finish(FwdState<D, RB>& st,
+                                                                 f32x16 (&s)[RB], const char* stage,
+                                                                 int kb, int l32, int g, int key0,
+                                                                 int Nk, float c_log2,
+                                                                 Issue issue) {
+  u32x4 p[RB][2];
+  fwd_softmax<D, RB, kMask>(st, s, p, g, key0, Nk, c_log2);
+  fwd_pv<D, RB>(st, p, stage, kb, l32, g, issue);
+}
+
+template <int D, int RB, bool kMask, typename Issue>
+__device__ __attribute__((always_inline)) inline void fwd_block(
+    FwdState<D, RB>& st, const char* stage, int kb, const u32x4 (*qf)[D / 16], int l32, int g,
+    int key0, int Nk, float c_log2, Issue issue) {
+  f32x16 s[RB];
+  fwd_scores<D, RB>(s, stage, kb, qf, l32, g, issue);
+  fwd_finish<D, RB, kMask>(st, s, stage, kb, l32, g, key0, Nk, c_log2, issue);
+}
+
 template <int D, int RB, typename Copy>
 __device__ __attribute__((always_inline)) inline void fwd_tile(
     char* __restrict__ next, const char* __restrict__ cur, Copy copy, FwdState<D, RB>& st,
@@ -1111,6 +1155,36 @@ __device__ __attribute__((always_inline)) inline void fwd_tile(
     });
 }
 
+// One tile of the lagged schedule of the 64-row form.  Waves 0-3 run blocks 0
+// and 1 of the tile (scores, softmax, products); waves 4-7, which share their
+// SIMDs, run a phase behind: they first run the products of block 1 of the
+// previous tile from its P (kept in pl), then block 0, then the scores and
+// softmax of block 1, whose products they carry into the next tile.  So while
+// one wave of a SIMD is in its softmax the other is mostly in matrix
+// products, which a shared per-tile barrier would otherwise keep in step.
+// Three stages rotate: the tile's own, the previous one (still read by waves
+// 4-7) and the next one (copied during block 0's scores); all three are
+// distinct, so the restrict-qualified pointers hold.
+template <int D, bool kLag, bool kMask, typename Copy>
+__device__ __attribute__((always_inline)) inline void fwd_tile_lagged(
+    const char* __restrict__ prev, const char* __restrict__ cur, char* __restrict__ next,
+    Copy copy, bool has_prev, FwdState<D, 2>& st, u32x4 (&pl)[2][2],
+    const u32x4 (*qf)[D / 16], int l32, int g, int key0, int Nk, float c_log2) {
+  using G = Geo<D, false>;
+  auto none = [](int) {};
+  if (kLag && has_prev) fwd_pv<D, 2>(st, pl, prev, 1, l32, g, none);
+  f32x16 s[2];
+  fwd_scores<D, 2>(s, cur, 0, qf, l32, g, [&](int slot) {
+    if (slot < G::kDmaPerWave) copy(next, slot);
+  });
+  fwd_finish<D, 2, kMask>(st, s, cur, 0, l32, g, key0, Nk, c_log2, none);
+  fwd_scores<D, 2>(s, cur, 1, qf, l32, g, none);
+  if constexpr (!kLag)
+    fwd_finish<D, 2, kMask>(st, s, cur, 1, l32, g, key0 + 32, Nk, c_log2, none);
+  else
+    fwd_softmax<D, 2, kMask>(st, s, pl, g, key0 + 32, Nk, c_log2);
+}
+
 // o: [B, H, Nq, D] fp32 or bf16; lse: [B, H, Nq] fp32 or NULL.  Tile images
 // hold K and V^T only (the layout of the frozen-key mode).
 template <int D, int RB, bool kOutBf16>
@@ -1119,8 +1193,10 @@ __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kerne
     float* __restrict__ lse, int Nq, int Nk, int ntiles, int nqt, int nbh, int tps, Extents ext,
     float c_log2) {
   using G = Geo<D, false>;
+  constexpr int kStages = RB == 2 && kFwdLag ? 3 : 2;
   __shared__ __attribute__((aligned(1024)))
-  char smem[2 * G::kImgBytes > kWaves * kStageBytes ? 2 * G::kImgBytes : kWaves * kStageBytes];
+  char smem[kStages * G::kImgBytes > kWaves * kStageBytes ? kStages * G::kImgBytes
+                                                          : kWaves * kStageBytes];
   // XCD-aware work order and key-tile ranges, as in attn_jvp_bf16_kernel
   const uint32_t wg = blockIdx.x, nwg = gridDim.x;
   const uint32_t xcd = wg % kXcds, slot = wg / kXcds, per = nwg / kXcds, extra = nwg % kXcds;
@@ -1181,15 +1257,43 @@ __global__ __launch_bounds__(kThreads, RB == 2 ? 2 : 4) void attn_fwd_bf16_kerne
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int ev = __builtin_amdgcn_readfirstlane((int)rec[0]);  // in a scalar register
-  for (int kt = t0; kt < kLast; ++kt) {
-    const int sc = (kt - t0) & 1;
-    fwd_tile<D, RB>(smem + (sc ^ 1) * G::kImgBytes, smem + sc * G::kImgBytes,
-                    [&](char* next, int j) { copy_one(kt + 1, next, j); }, st, qf, l32, g, Nk,
-                    c_log2);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  {
+  if constexpr (RB == 2 && kFwdLag) {
+    // waves 4-7 run a phase behind waves 0-3 (fwd_tile_lagged); both groups
+    // pass the same barriers
+    auto stg = [&](int i) { return smem + i * G::kImgBytes; };
+    auto lagged = [&](auto lagc) {
+      constexpr bool kL = decltype(lagc)::value;
+      u32x4 pl[2][2];
+      int cs = 0;  // stage of tile kt; the previous tile's is (cs + 2) % 3, the next one's (cs + 1) % 3
+      for (int kt = t0; kt < kLast; ++kt) {
+        const int ns = cs == 2 ? 0 : cs + 1, ps = cs == 0 ? 2 : cs - 1;
+        fwd_tile_lagged<D, kL, false>(stg(ps), stg(cs), stg(ns),
+                                      [&](char* next, int j) { copy_one(kt + 1, next, j); },
+                                      kt > t0, st, pl, qf, l32, g, kt * kBC, Nk, c_log2);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        cs = ns;
+      }
+      // last tile of the range (keys past Nk masked), nothing left to copy
+      const int ns = cs == 2 ? 0 : cs + 1, ps = cs == 0 ? 2 : cs - 1;
+      const int kl = kLast * kBC;
+      fwd_tile_lagged<D, kL, true>(stg(ps), stg(cs), stg(ns), [](char*, int) {}, kLast > t0, st,
+                                   pl, qf, l32, g, kl, Nk, c_log2);
+      if constexpr (kL) fwd_pv<D, 2>(st, pl, stg(cs), 1, l32, g, [](int) {});
+    };
+    if (wave >= kWaves / 2)
+      lagged(Flag<true>{});
+    else
+      lagged(Flag<false>{});
+  } else {
+    for (int kt = t0; kt < kLast; ++kt) {
+      const int sc = (kt - t0) & 1;
+      fwd_tile<D, RB>(smem + (sc ^ 1) * G::kImgBytes, smem + sc * G::kImgBytes,
+                      [&](char* next, int j) { copy_one(kt + 1, next, j); }, st, qf, l32, g, Nk,
+                      c_log2);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
     const char* cur = smem + ((kLast - t0) & 1) * G::kImgBytes;
     const int kl = kLast * kBC;
     auto none = [](int) {};
