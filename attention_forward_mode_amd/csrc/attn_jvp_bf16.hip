@@ -998,7 +998,7 @@ __global__ __launch_bounds__(kShortThreads, 2) void attn_jvp_bf16_short_kernel(
 // fit the chip one per CU.
 template <int RB>
 constexpr int fwd_rows() { return kWaves * 32 * RB; }  // query rows per workgroup
-// The 64-row form runs its two wave groups half a block apart (fwd_tile_lagged).
+// The 64-row form runs its two wave groups a phase apart (fwd_tile_lagged).
 constexpr bool kFwdLag = true;
 
 template <int D, int RB>

@@ -40,6 +40,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -56,11 +57,20 @@ KERNEL_SOURCES = ["attention_forward_mode_amd/csrc/attn_jvp_bf16.hip",
                   "attention_forward_mode_amd/csrc/range.hpp"]
 
 
+def _code_only(text):
+    """The source without its comments and with whitespace collapsed: the hash
+    then follows the code the compiler sees, not the comments around it (the
+    sources hold no string literal with a comment marker in it)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
