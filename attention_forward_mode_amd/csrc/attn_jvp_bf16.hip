@@ -448,16 +448,22 @@ struct Extents {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Four consecutive outputs of one row: 16 bytes of fp32, or 8 bytes of bf16.
+// The stores carry the non-temporal hint: outputs are written once and not
+// read again by this kernel, so they should not push the tile images out of
+// L2 (same-box A/B: text_cross 0.336 -> 0.298 ms, image_dit 0.670 -> 0.650).
 template <bool kBf16>
 __device__ __attribute__((always_inline)) inline void store4(__amdgpu_buffer_rsrc_t r,
                                                              uint32_t elem, f32x4 x) {
+  constexpr int kNonTemporal = 2;  // the nt cache-policy bit of a buffer store
   if constexpr (kBf16) {
     bf16x4 h;
 #pragma unroll
     for (int e = 0; e < 4; ++e) h[e] = (__bf16)x[e];
-    buf_store8(r, elem * 2, __builtin_bit_cast(u32x2, h));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, (int)(elem * 2), 0,
+                                          kNonTemporal);
   } else {
-    buf_store16(r, elem * 4, __builtin_bit_cast(u32x4, x));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)(elem * 4), 0,
+                                           kNonTemporal);
   }
 }
 
