@@ -33,6 +33,10 @@ __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) 
 }
 // Same, with the offset split into a per-lane part and a wave-uniform part
 // (kept in a scalar register); the range check applies to their sum.
+// The same with the non-temporal hint, for data read for the last time.
+__device__ inline u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2));
+}
 __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t uniform_off) {
   return __builtin_bit_cast(
       u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, (int)uniform_off, 0));
