@@ -464,10 +464,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_kernel(
 }
 
 // ---- bwd_q: gQ for 256 queries per workgroup --------------------------------
-template <int D, bool kMaskK>
+template <int D, bool kMaskK, typename Issue>
 __device__ __attribute__((always_inline)) inline void q_block(
     const char* stage, int kb, const u32x4* qf, const u32x4* gof, int l32, int g, f32x16* gq,
-    float c_log2, float lse2, float dq, int key0, int Nk) {
+    float c_log2, float lse2, float dq, int key0, int Nk, Issue issue) {
   using G = KImg<D>;
   const char* sK = stage;
   const char* sV = stage + G::kRTile;
@@ -477,6 +477,7 @@ __device__ __attribute__((always_inline)) inline void q_block(
   f32x16 s, gp;
 #pragma unroll
   for (int ks = 0; ks < G::kKS; ++ks) {
+    issue(ks);
     const u32x4 ka = lds_load16(sK + rowoff + 32 * ks);
     const u32x4 va = lds_load16(sV + rowoff + 32 * ks);
     s = mma_bf16(ka, qf[ks], ks == 0 ? f32x16{} : s);
@@ -499,14 +500,19 @@ __device__ __attribute__((always_inline)) inline void q_block(
     sb[q >> 2][q & 3] = pack_f16x2(gs[0], gs[1]);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // gQ^T += K^T gS^T
+  // gQ^T += K^T gS^T, each K^T fragment read one step ahead
   constexpr int kSteps = 2 * G::kCB;
+  auto koff = [&](int step) {
+    const int t = step / G::kCB, cb = step % G::kCB;
+    return (32 * cb + l32) * G::kTRow + 16 * g + 16 * (4 * kb + 2 * t);
+  };
+  u32x4 ktp[2];
+  ktp[0] = lds_load16(sKT + koff(0));
 #pragma unroll
   for (int step = 0; step < kSteps; ++step) {
     const int t = step / G::kCB, cb = step % G::kCB;
-    const u32x4 kt =
-        lds_load16(sKT + (32 * cb + l32) * G::kTRow + 16 * g + 16 * (4 * kb + 2 * t));
-    gq[cb] = mma_f16(kt, sb[t], gq[cb]);
+    if (step + 1 < kSteps) ktp[(step + 1) & 1] = lds_load16(sKT + koff(step + 1));
+    gq[cb] = mma_f16(ktp[step & 1], sb[t], gq[cb]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -517,9 +523,17 @@ __device__ __attribute__((always_inline)) inline void q_tile(
     uint32_t wave_part, int lane, int t_next, const u32x4* qf, const u32x4* gof, int l32, int g,
     f32x16* gq, float c_log2, float lse2, float dq, int Nk) {
   using G = KImg<D>;
-  copy_image<G::kDmaPerWave, G::kBytes>(rimg, next, wave_part, lane, t_next);
-  q_block<D, false>(cur, 0, qf, gof, l32, g, gq, c_log2, lse2, dq, 0, Nk);
-  q_block<D, false>(cur, 1, qf, gof, l32, g, gq, c_log2, lse2, dq, 0, Nk);
+  // the copy of the next tile, one instruction per step of block 0's S^T
+  // (not all at once: same-box A/B, backward of video_1p3b -0.8%)
+  auto one = [&](int j) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rimg, (lds_ptr_t)(next + wave_part + j * kDmaBytes), 16, lane * 16,
+        (uint32_t)t_next * G::kBytes + wave_part + j * kDmaBytes, 0, 0);
+  };
+  q_block<D, false>(cur, 0, qf, gof, l32, g, gq, c_log2, lse2, dq, 0, Nk, [&](int slot) {
+    if (slot < G::kDmaPerWave) one(slot);
+  });
+  q_block<D, false>(cur, 1, qf, gof, l32, g, gq, c_log2, lse2, dq, 0, Nk, [](int) {});
 }
 
 template <int D>
@@ -593,11 +607,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     const char* cur = smem + ((kLast - k0) & 1) * G::kBytes;
     const int kl = kLast * kTile;
     if (k1 == nktiles) {
-      q_block<D, true>(cur, 0, qf, gof, l32, g, acc, c_log2, lse2, dq, kl, Nk);
-      q_block<D, true>(cur, 1, qf, gof, l32, g, acc, c_log2, lse2, dq, kl + 32, Nk);
+      q_block<D, true>(cur, 0, qf, gof, l32, g, acc, c_log2, lse2, dq, kl, Nk, [](int) {});
+      q_block<D, true>(cur, 1, qf, gof, l32, g, acc, c_log2, lse2, dq, kl + 32, Nk, [](int) {});
     } else {
-      q_block<D, false>(cur, 0, qf, gof, l32, g, acc, c_log2, lse2, dq, kl, Nk);
-      q_block<D, false>(cur, 1, qf, gof, l32, g, acc, c_log2, lse2, dq, kl + 32, Nk);
+      q_block<D, false>(cur, 0, qf, gof, l32, g, acc, c_log2, lse2, dq, kl, Nk, [](int) {});
+      q_block<D, false>(cur, 1, qf, gof, l32, g, acc, c_log2, lse2, dq, kl + 32, Nk, [](int) {});
     }
   }
   if (row_ok)
