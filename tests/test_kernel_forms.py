@@ -106,3 +106,42 @@ def test_256_row_kernel_instances_vs_oracle(mode, d):
         print(f"[{mode} d={d}] {name}: max-abs {m['max_abs']:.3e} rel-Frobenius "
               f"{m['rel_frob']:.3e}", flush=True)
         assert m["max_abs"] <= 2e-2 and m["rel_frob"] <= 1e-2, (mode, d, name, m)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Nk", [30, 100, 130])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_forward_512_row_form_on_few_tiles(Nk, d, out_dtype):
+    """The 512-row forward form runs its two wave groups a phase apart over
+    three rotating tile stages; with 1, 2 and 3 key tiles (ragged last tile)
+    its first and last tiles meet (no previous tile, no next one).  Forced by
+    ATTN_JVP_TILE, it must equal the 256-row form bit for bit, and the oracle
+    within the gate; split ranges of 1-2 tiles likewise."""
+    x = _rand(2, 1100, Nk, d, seed=3 * Nk + d)
+    g = {n: t.cuda() for n, t in x.items()}
+    s = 1.0 / math.sqrt(d)
+
+    def fwd():
+        print(f"  launch attn_fwd Nk={Nk} d={d} {out_dtype} tile={os.environ['ATTN_JVP_TILE']}",
+              flush=True)
+        return ajvp.attn_fwd(g["q"], g["k"], g["v"], scale=s, out_dtype=out_dtype)
+    a = _with_tile(256, fwd)
+    b = _with_tile(512, fwd)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), (Nk, d)
+    z = torch.zeros_like(x["q"])
+    O, _, L = oracle.attention_jvp(x["q"], x["k"], x["v"], z, torch.zeros_like(x["k"]),
+                                   torch.zeros_like(x["v"]), s)[:3]
+    for name, got, want in (("O", b[0], O), ("lse", b[1], L)):
+        m = metrics(got.double().numpy(), want)
+        assert m["max_abs"] <= 2e-2 and m["rel_frob"] <= 1e-2, (Nk, d, name, m)
+    if out_dtype == torch.float32 and Nk > 64:
+        for ns in (2, (Nk + 63) // 64):
+            def split():
+                print(f"  launch attn_fwd_splitkv Nk={Nk} d={d} nsplit={ns} "
+                      f"tile={os.environ['ATTN_JVP_TILE']}", flush=True)
+                return ajvp.attn_fwd_splitkv(g["q"], g["k"], g["v"], scale=s, nsplit=ns)
+            c = _with_tile(256, split)
+            e = _with_tile(512, split)
+            assert torch.equal(c[0], e[0]) and torch.equal(c[1], e[1]), (Nk, d, ns)
+            m = metrics(e[0].double().numpy(), O)
+            assert m["max_abs"] <= 2e-2 and m["rel_frob"] <= 1e-2, (Nk, d, ns, m)
